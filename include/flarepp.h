@@ -1,0 +1,164 @@
+/*
+ * flarepp.h -- C ABI of libflarepp, the FLARE++ routing forward pass on one
+ * AMD Instinct MI355X (gfx950) GPU.
+ *
+ * The operation.  For every batch element b and head h, with token keys and
+ * values K, V (N x D), learned latent seeds S (M x D) and a scale s:
+ *
+ *     Qd = SDPA(S,  K, V,  s)   seed encode: M input-conditioned queries
+ *     Z  = SDPA(Qd, K, V,  s)   encode: the queries compress the tokens
+ *     Y  = SDPA(K,  Qd, Z, s)   decode: every token reads the latents back
+ *
+ * where SDPA(Q, K, V, s)_i = sum_j softmax_j(s <Q_i, K_j>) V_j.  The first
+ * line is the extra encode call driven by learned latent seeds that the
+ * FLARE++ abstract introduces ("FLARE++: Low-rank attention with dynamic
+ * attention routing", abstract; French technical summary, "Méthodologie",
+ * "Synthèse de Requêtes Dynamiques"); the second and third are FLARE's
+ * encode and decode with the synthesised queries in place of fixed ones
+ * ("FLARE: Fast Low-rank Attention Routing Engine", section
+ * "Основной механизм FLARE"; French summary, "Routage Encode-Décode").  The
+ * encode softmaxes run over the N tokens and the decode softmax over the M
+ * latents (FLARE summary, "Матрица коммуникации низкого ранга").  Nothing is
+ * applied between the stages.  The N x N mixing matrix is never formed.
+ *
+ * Layouts.  Every tensor is dense, row-major, with D innermost:
+ *     K, V         B x H x N x D   (dtype of the descriptor)
+ *     S            M x D           (seed_head_stride == 0: shared by all
+ *                                   (b, h)) or H x M x D (seed_head_stride
+ *                                   == M*D: per-head seeds), descriptor dtype
+ *     Qd, Z        B x H x M x D   float32
+ *     Y            B x H x N x D   float32
+ * Base pointers must be 16-byte aligned device pointers.
+ *
+ * Arithmetic.  FLAREPP_F32: float32 inputs, float32 arithmetic throughout.
+ * FLAREPP_BF16: bf16 inputs; the contractions run on bf16 matrix cores with
+ * float32 accumulation, softmax statistics are float32, and Qd is carried
+ * into the later stages as a bf16 hi/lo pair; outputs are float32.
+ *
+ * Ownership and threading.  The caller owns every buffer.  The library never
+ * allocates device memory, never synchronises, keeps no pointer after a call
+ * returns and has no mutable global state; calls on different streams may
+ * run concurrently if their output and workspace buffers are disjoint.  Work
+ * is enqueued on `stream` (a hipStream_t; NULL = the default stream).
+ * Workspace contents are undefined on return.
+ *
+ * Errors.  Every call validates its arguments on the host before any GPU
+ * call and returns a flarepp_status; no exception crosses the ABI.  A launch
+ * failure is reported as FLAREPP_HIP_ERROR.  Faults inside kernels surface at
+ * the caller's next synchronisation.  Results are bitwise repeatable for a
+ * given descriptor and device (fixed split counts, no atomics).
+ */
+#ifndef FLAREPP_H
+#define FLAREPP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FLAREPP_ABI_VERSION 1
+
+typedef enum flarepp_status {
+    FLAREPP_OK = 0,
+    FLAREPP_INVALID_ARG = 1,          /* null pointer, dims < 1, bad stride, non-finite scale, misaligned */
+    FLAREPP_UNSUPPORTED = 2,          /* D not 16 or 32, dtype unknown, M or N*D beyond the limits below */
+    FLAREPP_WORKSPACE_TOO_SMALL = 3,  /* ws_bytes below flarepp_workspace_size() */
+    FLAREPP_ALIASING = 4,             /* an output overlaps an input, another output or the workspace */
+    FLAREPP_HIP_ERROR = 5             /* a kernel launch failed */
+} flarepp_status;
+
+typedef enum flarepp_dtype {
+    FLAREPP_F32 = 0,
+    FLAREPP_BF16 = 1
+} flarepp_dtype;
+
+typedef enum flarepp_op {
+    FLAREPP_OP_SEED_ENCODE = 0,
+    FLAREPP_OP_ENCODE = 1,
+    FLAREPP_OP_DECODE = 2,
+    FLAREPP_OP_ROUTE = 3,
+    FLAREPP_OP_FLARE = 4
+} flarepp_op;
+
+/* Limits of this build. */
+#define FLAREPP_MAX_M 256
+#define FLAREPP_MAX_SLICE_ELEMS ((int64_t)1 << 31) /* N * D per (b, h) */
+
+typedef struct flarepp_desc {
+    int64_t B, H, N, M, D;    /* batch, heads, tokens, latents, head dim (16 or 32) */
+    int32_t dtype;            /* flarepp_dtype of S, K, V */
+    float scale;              /* s, used in all three stages */
+    int64_t seed_head_stride; /* elements between heads' seed blocks: 0 or M*D */
+} flarepp_desc;
+
+/* FLAREPP_ABI_VERSION of the loaded library. */
+int flarepp_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *flarepp_status_string(flarepp_status status);
+
+/*
+ * Bytes of device workspace that `op` needs for `desc` (the split-N partial
+ * softmax statistics and the bf16 operand copies of Qd and Z).  Pure host
+ * computation.  Returns INVALID_ARG / UNSUPPORTED for descriptors the
+ * compute calls would reject.
+ */
+flarepp_status flarepp_workspace_size(const flarepp_desc *desc, int32_t op, size_t *bytes);
+
+/*
+ * Seed encode, Qd = SDPA(S, K, V, s) for every (b, h): the extra encode
+ * call with learned latent seeds as queries (FLARE++ abstract; French
+ * summary, "Synthèse de Requêtes Dynamiques").  S: M x D or H x M x D
+ * (descriptor dtype); K, V: B x H x N x D; Qd (output): B x H x M x D fp32.
+ */
+flarepp_status flarepp_seed_encode(const flarepp_desc *desc, const void *S, const void *K,
+                                   const void *V, float *Qd, void *ws, size_t ws_bytes,
+                                   void *stream);
+
+/*
+ * Encode, Z = SDPA(Qd, K, V, s): FLARE's encode step with per-(b, h)
+ * queries (FLARE summary, "Основной механизм FLARE", encode step).
+ * Qd: B x H x M x D fp32; K, V: B x H x N x D; Z (output): B x H x M x D fp32.
+ * Calling the stages one by one lets a caller transform Qd in between.
+ */
+flarepp_status flarepp_encode(const flarepp_desc *desc, const float *Qd, const void *K,
+                              const void *V, float *Z, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Decode, Y = SDPA(K, Qd, Z, s): every token attends over the M latents
+ * (FLARE summary, "Основной механизм FLARE", decode step; softmax over the
+ * latents, "Матрица коммуникации низкого ранга").  Qd, Z: B x H x M x D
+ * fp32; K: B x H x N x D; Y (output): B x H x N x D fp32.
+ */
+flarepp_status flarepp_decode(const flarepp_desc *desc, const float *Qd, const float *Z,
+                              const void *K, float *Y, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The complete route, seed encode -> encode -> decode, enqueued on one
+ * stream with no host synchronisation ("FLARE++" abstract: the complete
+ * routing operation is scaled-dot-product attention calls alone).  Y is
+ * required; Qd_out and Z_out may be NULL.
+ */
+flarepp_status flarepp_route(const flarepp_desc *desc, const void *S, const void *K,
+                             const void *V, float *Y, float *Qd_out, float *Z_out, void *ws,
+                             size_t ws_bytes, void *stream);
+
+/*
+ * Fixed-query FLARE, the special case FLARE++ generalises: the latent
+ * queries Q are parameters rather than synthesised, Z = SDPA(Q, K, V, s) and
+ * Y = SDPA(K, Q, Z, s) ("FLARE: Fast Low-rank Attention Routing Engine",
+ * section "Основной механизм FLARE"; the FLARE++ abstract's fixed learned
+ * query templates).  Q: M x D or H x M x D (seed_head_stride), descriptor
+ * dtype.  Y is required; Z_out may be NULL.
+ */
+flarepp_status flarepp_flare(const flarepp_desc *desc, const void *Q, const void *K,
+                             const void *V, float *Y, float *Z_out, void *ws, size_t ws_bytes,
+                             void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLAREPP_H */

@@ -1,0 +1,78 @@
+// Device-side building blocks shared by the libflarepp kernels (gfx950 only).
+//
+// Matrix-core operand layouts (v_mfma_f32_16x16x32_bf16; lane l, g = l / 16):
+//   A (16 rows x 32 k): lane holds row l % 16, k = 8g .. 8g + 7
+//   B (32 k x 16 cols): lane holds col l % 16, k = 8g .. 8g + 7
+//   C (16 x 16 fp32)  : lane holds col l % 16, rows 4g .. 4g + 3
+// v_mfma_f32_16x16x16_bf16 is the same with k = 4g .. 4g + 3.
+// A C tile of S^T = K Q^T (rows = tokens, cols = latents) therefore leaves each
+// lane with one latent and four tokens; two such tiles give exactly the eight
+// k-slots of a B operand over 32 tokens, so softmax weights feed the next
+// contraction without leaving registers, provided the other operand orders its
+// 32 k-slots the same way: slot (g, j) <-> token 4g + j for j < 4 and
+// 16 + 4g + (j - 4) for j >= 4.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flarepp {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x4 mfma_k32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_k16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Round-to-nearest-even pair conversion (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16x2 pack_bf16(float lo, float hi) {
+  bf16x2 r = {(__bf16)lo, (__bf16)hi};
+  return r;
+}
+
+// Sum of a packed bf16 pair, accumulated in fp32: acc + p.x + p.y.
+__device__ __forceinline__ float add_pair(bf16x2 p, float acc) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(p, ones, acc, false);
+}
+
+// Reductions across the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48),
+// i.e. over g for a fixed l % 16: two permlane swaps, no LDS traffic.
+__device__ __forceinline__ float max_over_rows(float x) {
+  uint32_t u = __float_as_uint(x);
+  auto s = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  float y = fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  uint32_t v = __float_as_uint(y);
+  auto t = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float sum_over_rows(float x) {
+  uint32_t u = __float_as_uint(x);
+  auto s = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  float y = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+  uint32_t v = __float_as_uint(y);
+  auto t = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  return fmaxf(fmaxf(a, b), c);  // v_max3_f32
+}
+
+// Per-split softmax partial record: acc[0..D-1], sum at D, max (log2 units) at D+1.
+template <int D>
+struct Part {
+  static constexpr int kStride = D + 4;  // 16-byte aligned records
+};
+
+}  // namespace flarepp

@@ -1,0 +1,619 @@
+// libflarepp host side: argument validation, workspace planning and the
+// launch sequences of the C ABI declared in include/flarepp.h.
+//
+// Launch sequence of the route for the bf16 path, per group of G heads
+// (G is chosen so that one group's K and V stay resident in the MI355X's
+// 256 MB last-level cache between the three passes over them):
+//   prep    seeds -> c*S as a bf16 hi/lo operand (once per call)
+//   encode  split-N seed encode, also records each split's max key norm
+//   merge   -> Qd (caller's copy, bf16 hi/lo operand, row norms, the bound for
+//              the next encode)
+//   encode  split-N encode with Qd
+//   merge   -> Z (caller's copy, transposed bf16 operand)
+//   decode  -> Y
+// Everything is enqueued on the caller's stream; nothing synchronises.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+
+#include "flarepp.h"
+#include "common.h"
+#include "decode_bf16.h"
+#include "encode_bf16.h"
+#include "f32_path.h"
+#include "merge.h"
+
+using namespace flarepp;
+
+namespace {
+
+constexpr int kComputeUnits = 256;                  // MI355X
+constexpr int64_t kGroupKVBytes = int64_t(128) << 20;  // K + V of one launch group
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Plan {
+  int64_t BH;
+  int B, H, N, M, D, Mp;
+  bool bf16;
+  float c;          // scale * log2(e)
+  int G;            // heads per launch group
+  int J, chunk;     // splits of N and tokens per split (encode)
+  int mbw;          // 16-latent blocks per wave (bf16 encode)
+  int tpr;          // threads per latent row in the merge
+  int dchunk;       // tokens per decode workgroup (bf16)
+  int nS;           // seed / fixed-query operand blocks (1 or H)
+  size_t o_shi, o_slo, o_sqn, o_part, o_knorm, o_qhi, o_qlo, o_qnorm, o_bias, o_zt, o_qf, o_zf, total;
+};
+
+bool env_int(const char* name, int* out) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return false;
+  char* end = nullptr;
+  long x = std::strtol(v, &end, 10);
+  if (*end || x < 1 || x > 1 << 30) return false;
+  *out = (int)x;
+  return true;
+}
+
+flarepp_status check_desc(const flarepp_desc* d) {
+  if (!d) return FLAREPP_INVALID_ARG;
+  if (d->B < 1 || d->H < 1 || d->N < 1 || d->M < 1 || d->D < 1) return FLAREPP_INVALID_ARG;
+  if (!std::isfinite(d->scale)) return FLAREPP_INVALID_ARG;
+  if (d->dtype != FLAREPP_F32 && d->dtype != FLAREPP_BF16) return FLAREPP_UNSUPPORTED;
+  if (d->D != 16 && d->D != 32) return FLAREPP_UNSUPPORTED;
+  if (d->M > FLAREPP_MAX_M) return FLAREPP_UNSUPPORTED;
+  if (d->N >= FLAREPP_MAX_SLICE_ELEMS / d->D) return FLAREPP_UNSUPPORTED;
+  if (d->B > (int64_t(1) << 31) / d->H) return FLAREPP_UNSUPPORTED;
+  if (d->B * d->H > INT64_MAX / 8 / (d->N * d->D)) return FLAREPP_UNSUPPORTED;
+  if (d->seed_head_stride != 0 && d->seed_head_stride != d->M * d->D) return FLAREPP_INVALID_ARG;
+  return FLAREPP_OK;
+}
+
+Plan make_plan(const flarepp_desc* d, int op) {
+  Plan p{};
+  p.B = (int)d->B;
+  p.H = (int)d->H;
+  p.BH = d->B * d->H;
+  p.N = (int)d->N;
+  p.M = (int)d->M;
+  p.D = (int)d->D;
+  p.Mp = (int)cdiv(d->M, 16) * 16;
+  p.bf16 = d->dtype == FLAREPP_BF16;
+  p.c = d->scale * 1.4426950408889634f;
+  p.nS = d->seed_head_stride ? p.H : 1;
+  const int elem = p.bf16 ? 2 : 4;
+
+  const int64_t kv = 2 * d->N * d->D * elem;
+  int64_t G = std::max<int64_t>(1, kGroupKVBytes / kv);
+  int env_g;
+  if (env_int("FLAREPP_HEAD_GROUP", &env_g)) G = env_g;
+  G = std::min<int64_t>(G, std::min<int64_t>(p.BH, 65535));
+  p.G = (int)G;
+
+  const int nMB = p.Mp / 16;
+  p.mbw = nMB <= 4 ? 1 : nMB <= 8 ? 2 : nMB <= 12 ? 3 : 4;
+  const int tile = p.bf16 ? 4096 / p.D : 64;
+  const int64_t target = (p.bf16 ? 2 : 4) * int64_t(kComputeUnits);
+  int64_t J = std::max<int64_t>(1, cdiv(target, G));
+  int env_j;
+  if (env_int("FLAREPP_SPLITS", &env_j)) J = env_j;
+  J = std::min<int64_t>(J, cdiv(d->N, tile));
+  const int64_t chunk = cdiv(cdiv(d->N, J), tile) * tile;
+  p.chunk = (int)chunk;
+  p.J = (int)cdiv(d->N, chunk);
+  int tpr = 1;
+  while (tpr < p.J && tpr < 64) tpr *= 2;
+  p.tpr = tpr;
+  const int64_t dwg = std::max<int64_t>(1, cdiv(2 * int64_t(kComputeUnits), G));
+  p.dchunk = (int)(cdiv(cdiv(d->N, dwg), 64) * 64);
+
+  // workspace layout
+  const size_t G_ = (size_t)p.G, Mp = (size_t)p.Mp, D = (size_t)p.D;
+  const size_t opnd = Mp * D * 2;  // one bf16 Mp x D block
+  const bool route = op == FLAREPP_OP_ROUTE, seed = op == FLAREPP_OP_SEED_ENCODE;
+  const bool enc = op == FLAREPP_OP_ENCODE, dec = op == FLAREPP_OP_DECODE, flare = op == FLAREPP_OP_FLARE;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  const size_t none = SIZE_MAX;
+  p.o_shi = p.o_slo = p.o_sqn = p.o_part = p.o_knorm = p.o_qhi = p.o_qlo = p.o_qnorm = p.o_bias =
+      p.o_zt = p.o_qf = p.o_zf = none;
+  if (p.bf16) {
+    if (route || seed || flare) {
+      p.o_shi = take(p.nS * opnd);
+      p.o_slo = take(p.nS * opnd);
+      if (flare) p.o_sqn = take(p.nS * Mp * 4);
+    }
+    if (!dec) p.o_part = take(G_ * p.J * Mp * (D + 4) * 4);
+    if (route) p.o_knorm = take(G_ * p.J * 4);
+    if (route || enc || dec) {
+      p.o_qhi = take(G_ * opnd);
+      p.o_qlo = take(G_ * opnd);
+    }
+    if (route || dec) p.o_qnorm = take(G_ * Mp * 4);
+    if (route) p.o_bias = take(G_ * Mp * 4);
+    if (route || dec || flare) p.o_zt = take(G_ * opnd);
+  } else {
+    if (!dec) p.o_part = take(G_ * p.J * Mp * (D + 4) * 4);
+    if (route) {
+      p.o_qf = take(G_ * p.M * D * 4);
+      p.o_zf = take(G_ * p.M * D * 4);
+    }
+    if (flare) p.o_zf = take(G_ * p.M * D * 4);
+  }
+  p.total = off;
+  return p;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return off == SIZE_MAX ? nullptr : reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
+
+struct Range {
+  uintptr_t lo, hi;
+};
+Range range(const void* p, size_t bytes) {
+  return Range{reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + bytes};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Outputs must be disjoint from every input, from each other and from the
+// workspace.  Null entries are skipped.
+flarepp_status check_aliasing(const Range* outs, const void* const* outp, int nout, const Range* ins,
+                              const void* const* inp, int nin) {
+  for (int i = 0; i < nout; ++i) {
+    if (!outp[i]) continue;
+    for (int k = 0; k < nin; ++k)
+      if (inp[k] && overlap(outs[i], ins[k])) return FLAREPP_ALIASING;
+    for (int k = i + 1; k < nout; ++k)
+      if (outp[k] && overlap(outs[i], outs[k])) return FLAREPP_ALIASING;
+  }
+  return FLAREPP_OK;
+}
+
+flarepp_status launched() {
+  return hipGetLastError() == hipSuccess ? FLAREPP_OK : FLAREPP_HIP_ERROR;
+}
+
+#define FLAREPP_TRY(x)                          \
+  do {                                          \
+    const flarepp_status st_ = (x);             \
+    if (st_ != FLAREPP_OK) return st_;          \
+  } while (0)
+
+// ------------------------------------------------------------- launchers --
+
+template <int D>
+flarepp_status run_prep(const Plan& p, const void* src, bool src_bf16, int64_t src_off, int64_t src_blk,
+                        int nblk, __bf16* hi, __bf16* lo, __bf16* zt, float* qn, float c, hipStream_t st) {
+  PrepArgs a{src, src_bf16 ? 1 : 0, src_off, src_blk, nblk, p.M, p.Mp, hi, lo, zt, qn, c};
+  const int64_t n = (int64_t)nblk * p.Mp;
+  prep_rows<D><<<dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st>>>(a);
+  return launched();
+}
+
+template <int D, bool KNORM>
+flarepp_status run_encode_bf16(const Plan& p, const EncodeArgs& a, int Gc, hipStream_t st) {
+  const dim3 grid((unsigned)p.J, (unsigned)Gc, (unsigned)cdiv(p.Mp / 16, 4 * p.mbw));
+  switch (p.mbw) {
+    case 1: encode_split_bf16<D, 1, KNORM><<<grid, dim3(256), 0, st>>>(a); break;
+    case 2: encode_split_bf16<D, 2, KNORM><<<grid, dim3(256), 0, st>>>(a); break;
+    case 3: encode_split_bf16<D, 3, KNORM><<<grid, dim3(256), 0, st>>>(a); break;
+    default: encode_split_bf16<D, 4, KNORM><<<grid, dim3(256), 0, st>>>(a); break;
+  }
+  return launched();
+}
+
+template <int D>
+flarepp_status run_encode_f32(const Plan& p, const EncodeF32Args& a, int Gc, hipStream_t st) {
+  const dim3 grid((unsigned)p.J, (unsigned)Gc, (unsigned)cdiv(p.M, 256));
+  encode_split_f32<D><<<grid, dim3(256), 0, st>>>(a);
+  return launched();
+}
+
+template <int D>
+flarepp_status run_merge(const Plan& p, const MergeArgs& a, int Gc, hipStream_t st) {
+  const int rpb = 256 / p.tpr;
+  const dim3 grid((unsigned)cdiv(p.Mp, rpb), (unsigned)Gc);
+  switch (p.tpr) {
+    case 1: merge_partials<D, 1><<<grid, dim3(256), 0, st>>>(a); break;
+    case 2: merge_partials<D, 2><<<grid, dim3(256), 0, st>>>(a); break;
+    case 4: merge_partials<D, 4><<<grid, dim3(256), 0, st>>>(a); break;
+    case 8: merge_partials<D, 8><<<grid, dim3(256), 0, st>>>(a); break;
+    case 16: merge_partials<D, 16><<<grid, dim3(256), 0, st>>>(a); break;
+    case 32: merge_partials<D, 32><<<grid, dim3(256), 0, st>>>(a); break;
+    default: merge_partials<D, 64><<<grid, dim3(256), 0, st>>>(a); break;
+  }
+  return launched();
+}
+
+template <int D, int MB>
+void launch_decode_mb(const DecodeArgs& a, dim3 grid, hipStream_t st) {
+  decode_bf16<D, MB><<<grid, dim3(256), 0, st>>>(a);
+}
+
+template <int D>
+flarepp_status run_decode_bf16(const Plan& p, const DecodeArgs& a, int Gc, hipStream_t st) {
+  const dim3 grid((unsigned)cdiv(p.N, p.dchunk), (unsigned)Gc);
+  switch (p.Mp / 16) {
+    case 1: launch_decode_mb<D, 1>(a, grid, st); break;
+    case 2: launch_decode_mb<D, 2>(a, grid, st); break;
+    case 3: launch_decode_mb<D, 3>(a, grid, st); break;
+    case 4: launch_decode_mb<D, 4>(a, grid, st); break;
+    case 5: launch_decode_mb<D, 5>(a, grid, st); break;
+    case 6: launch_decode_mb<D, 6>(a, grid, st); break;
+    case 7: launch_decode_mb<D, 7>(a, grid, st); break;
+    case 8: launch_decode_mb<D, 8>(a, grid, st); break;
+    case 9: launch_decode_mb<D, 9>(a, grid, st); break;
+    case 10: launch_decode_mb<D, 10>(a, grid, st); break;
+    case 11: launch_decode_mb<D, 11>(a, grid, st); break;
+    case 12: launch_decode_mb<D, 12>(a, grid, st); break;
+    case 13: launch_decode_mb<D, 13>(a, grid, st); break;
+    case 14: launch_decode_mb<D, 14>(a, grid, st); break;
+    case 15: launch_decode_mb<D, 15>(a, grid, st); break;
+    default: launch_decode_mb<D, 16>(a, grid, st); break;
+  }
+  return launched();
+}
+
+template <int D>
+flarepp_status run_decode_f32(const Plan& p, const DecodeF32Args& a, int Gc, hipStream_t st) {
+  const dim3 grid((unsigned)cdiv(p.N, 256), (unsigned)Gc);
+  decode_f32<D><<<grid, dim3(256), (size_t)2 * p.M * D * sizeof(float), st>>>(a);
+  return launched();
+}
+
+MergeArgs merge_args(const Plan& p, void* ws, int64_t g0) {
+  MergeArgs m{};
+  m.part = at<float>(ws, p.o_part);
+  m.J = p.J;
+  m.Mp = p.Mp;
+  m.M = p.M;
+  m.bh0 = g0;
+  m.c = p.c;
+  return m;
+}
+
+EncodeArgs encode_args(const Plan& p, void* ws, const void* K, const void* V, int64_t g0) {
+  EncodeArgs e{};
+  e.K = static_cast<const __bf16*>(K);
+  e.V = static_cast<const __bf16*>(V);
+  e.part = at<float>(ws, p.o_part);
+  e.H = p.H;
+  e.N = p.N;
+  e.Mp = p.Mp;
+  e.J = p.J;
+  e.chunk = p.chunk;
+  e.bh0 = g0;
+  return e;
+}
+
+// ---------------------------------------------------------------- stages --
+
+enum Stage { kSeed, kEncode, kDecode, kRoute, kFlare };
+
+template <int D>
+flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in, const float* Z_in,
+                   const void* K, const void* V, float* Y, float* Qd_out, float* Z_out, void* ws,
+                   hipStream_t st) {
+  const int64_t MD = (int64_t)p.M * D, MpD = (int64_t)p.Mp * D;
+  const int64_t seed_h = p.nS > 1 ? MD : 0;
+  if (p.bf16) {
+    __bf16* shi = at<__bf16>(ws, p.o_shi);
+    __bf16* slo = at<__bf16>(ws, p.o_slo);
+    if (stage == kSeed || stage == kRoute || stage == kFlare)
+      FLAREPP_TRY(run_prep<D>(p, S, true, 0, seed_h, p.nS, shi, slo, nullptr, at<float>(ws, p.o_sqn), p.c, st));
+    for (int64_t g0 = 0; g0 < p.BH; g0 += p.G) {
+      const int Gc = (int)std::min<int64_t>(p.G, p.BH - g0);
+      __bf16* qhi = at<__bf16>(ws, p.o_qhi);
+      __bf16* qlo = at<__bf16>(ws, p.o_qlo);
+      __bf16* zt = at<__bf16>(ws, p.o_zt);
+      float* qnorm = at<float>(ws, p.o_qnorm);
+      if (stage == kSeed || stage == kRoute || stage == kFlare) {
+        EncodeArgs e = encode_args(p, ws, K, V, g0);
+        e.q_hi = shi;
+        e.q_lo = slo;
+        e.q_sb = 0;
+        e.q_sh = p.nS > 1 ? MpD : 0;
+        e.q_off = 0;
+        e.knorm = at<float>(ws, p.o_knorm);
+        if (stage == kRoute)
+          FLAREPP_TRY((run_encode_bf16<D, true>(p, e, Gc, st)));
+        else
+          FLAREPP_TRY((run_encode_bf16<D, false>(p, e, Gc, st)));
+        MergeArgs m = merge_args(p, ws, g0);
+        if (stage == kFlare) {
+          m.out = Z_out;
+          m.op_zt = zt;
+        } else {
+          m.out = Qd_out;
+          if (stage == kRoute) {
+            m.op_hi = qhi;
+            m.op_lo = qlo;
+            m.qnorm = qnorm;
+            m.knorm = e.knorm;
+            m.Jk = p.J;
+            m.bias = at<float>(ws, p.o_bias);
+          }
+        }
+        FLAREPP_TRY(run_merge<D>(p, m, Gc, st));
+      }
+      if (stage == kEncode)
+        FLAREPP_TRY(run_prep<D>(p, Qd_in, false, g0 * MD, MD, Gc, qhi, qlo, nullptr, nullptr, p.c, st));
+      if (stage == kEncode || stage == kRoute) {
+        EncodeArgs e = encode_args(p, ws, K, V, g0);
+        e.q_hi = qhi;
+        e.q_lo = qlo;
+        e.q_sb = (int64_t)p.H * MpD;
+        e.q_sh = MpD;
+        e.q_off = g0 * MpD;
+        e.bias = stage == kRoute ? at<float>(ws, p.o_bias) : nullptr;
+        FLAREPP_TRY((run_encode_bf16<D, false>(p, e, Gc, st)));
+        MergeArgs m = merge_args(p, ws, g0);
+        m.out = Z_out;
+        if (stage == kRoute) m.op_zt = zt;
+        FLAREPP_TRY(run_merge<D>(p, m, Gc, st));
+      }
+      if (stage == kDecode) {
+        FLAREPP_TRY(run_prep<D>(p, Qd_in, false, g0 * MD, MD, Gc, qhi, qlo, nullptr, qnorm, p.c, st));
+        FLAREPP_TRY(run_prep<D>(p, Z_in, false, g0 * MD, MD, Gc, nullptr, nullptr, zt, nullptr, p.c, st));
+      }
+      if (stage == kDecode || stage == kRoute || stage == kFlare) {
+        DecodeArgs dargs{};
+        if (stage == kFlare) {
+          dargs.q_hi = shi;
+          dargs.q_lo = slo;
+          dargs.q_sb = 0;
+          dargs.q_sh = p.nS > 1 ? MpD : 0;
+          dargs.q_off = 0;
+          dargs.qnorm = at<float>(ws, p.o_sqn);
+        } else {
+          dargs.q_hi = qhi;
+          dargs.q_lo = qlo;
+          dargs.q_sb = (int64_t)p.H * MpD;
+          dargs.q_sh = MpD;
+          dargs.q_off = g0 * MpD;
+          dargs.qnorm = qnorm;
+        }
+        dargs.zt = zt;
+        dargs.K = static_cast<const __bf16*>(K);
+        dargs.Y = Y;
+        dargs.H = p.H;
+        dargs.N = p.N;
+        dargs.M = p.M;
+        dargs.Mp = p.Mp;
+        dargs.chunk = p.dchunk;
+        dargs.bh0 = g0;
+        dargs.c = p.c;
+        FLAREPP_TRY(run_decode_bf16<D>(p, dargs, Gc, st));
+      }
+    }
+    return FLAREPP_OK;
+  }
+
+  // float32 path
+  float* qf = at<float>(ws, p.o_qf);
+  float* zf = at<float>(ws, p.o_zf);
+  for (int64_t g0 = 0; g0 < p.BH; g0 += p.G) {
+    const int Gc = (int)std::min<int64_t>(p.G, p.BH - g0);
+    auto encode = [&](const float* q, int64_t sb, int64_t sh, int64_t off, float* out, float* outl) {
+      EncodeF32Args e{};
+      e.q = q;
+      e.q_sb = sb;
+      e.q_sh = sh;
+      e.q_off = off;
+      e.K = static_cast<const float*>(K);
+      e.V = static_cast<const float*>(V);
+      e.part = at<float>(ws, p.o_part);
+      e.H = p.H;
+      e.N = p.N;
+      e.M = p.M;
+      e.Mp = p.Mp;
+      e.J = p.J;
+      e.chunk = p.chunk;
+      e.bh0 = g0;
+      e.c = p.c;
+      FLAREPP_TRY(run_encode_f32<D>(p, e, Gc, st));
+      MergeArgs m = merge_args(p, ws, g0);
+      m.out = out;
+      m.outl = outl;
+      return run_merge<D>(p, m, Gc, st);
+    };
+    auto decode = [&](const float* q, int64_t qsb, int64_t qsh, int64_t qoff, const float* z, int64_t zsb,
+                      int64_t zsh, int64_t zoff) {
+      DecodeF32Args d{q, qsb, qsh, qoff, z, zsb, zsh, zoff, static_cast<const float*>(K), Y,
+                      p.H, p.N, p.M, g0, p.c};
+      return run_decode_f32<D>(p, d, Gc, st);
+    };
+    const float* Sf = static_cast<const float*>(S);
+    const int64_t HMD = (int64_t)p.H * MD;
+    switch (stage) {
+      case kSeed:
+        FLAREPP_TRY(encode(Sf, 0, seed_h, 0, Qd_out, nullptr));
+        break;
+      case kEncode:
+        FLAREPP_TRY(encode(Qd_in, HMD, MD, 0, Z_out, nullptr));
+        break;
+      case kDecode:
+        FLAREPP_TRY(decode(Qd_in, HMD, MD, 0, Z_in, HMD, MD, 0));
+        break;
+      case kRoute:
+        FLAREPP_TRY(encode(Sf, 0, seed_h, 0, Qd_out, qf));
+        FLAREPP_TRY(encode(qf, HMD, MD, g0 * MD, Z_out, zf));
+        FLAREPP_TRY(decode(qf, HMD, MD, g0 * MD, zf, HMD, MD, g0 * MD));
+        break;
+      case kFlare:
+        FLAREPP_TRY(encode(Sf, 0, seed_h, 0, Z_out, zf));
+        FLAREPP_TRY(decode(Sf, 0, seed_h, 0, zf, HMD, MD, g0 * MD));
+        break;
+    }
+  }
+  return FLAREPP_OK;
+}
+
+flarepp_status dispatch(const Plan& p, Stage stage, const void* S, const float* Qd_in, const float* Z_in,
+                        const void* K, const void* V, float* Y, float* Qd_out, float* Z_out, void* ws,
+                        void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (p.D == 16) return run<16>(p, stage, S, Qd_in, Z_in, K, V, Y, Qd_out, Z_out, ws, st);
+  return run<32>(p, stage, S, Qd_in, Z_in, K, V, Y, Qd_out, Z_out, ws, st);
+}
+
+// Shared argument checks of the compute calls: descriptor, pointers,
+// alignment, workspace size and aliasing; all before any HIP call.
+flarepp_status prologue(const flarepp_desc* d, int op, const void* const* in, const size_t* in_bytes, int nin,
+                        const void* const* out, const size_t* out_bytes, const bool* out_required, int nout,
+                        void* ws, size_t ws_bytes, Plan* plan) {
+  FLAREPP_TRY(check_desc(d));
+  for (int i = 0; i < nin; ++i)
+    if (!in[i] || misaligned(in[i])) return FLAREPP_INVALID_ARG;
+  for (int i = 0; i < nout; ++i) {
+    if (out_required[i] && !out[i]) return FLAREPP_INVALID_ARG;
+    if (out[i] && misaligned(out[i])) return FLAREPP_INVALID_ARG;
+  }
+  *plan = make_plan(d, op);
+  if (plan->total > 0) {
+    if (!ws || misaligned(ws)) return FLAREPP_INVALID_ARG;
+    if (ws_bytes < plan->total) return FLAREPP_WORKSPACE_TOO_SMALL;
+  }
+  Range ins[6], outs[4];
+  const void* inp[6];
+  const void* outp[4];
+  int ni = 0;
+  for (int i = 0; i < nin; ++i) {
+    ins[ni] = range(in[i], in_bytes[i]);
+    inp[ni++] = in[i];
+  }
+  if (plan->total > 0) {
+    ins[ni] = range(ws, plan->total);
+    inp[ni++] = ws;
+  }
+  for (int i = 0; i < nout; ++i) {
+    outs[i] = range(out[i], out_bytes[i]);
+    outp[i] = out[i];
+  }
+  return check_aliasing(outs, outp, nout, ins, inp, ni);
+}
+
+struct Sizes {
+  size_t s, kv, md, y;
+};
+Sizes sizes(const flarepp_desc* d) {
+  const size_t elem = d->dtype == FLAREPP_BF16 ? 2 : 4;
+  Sizes z;
+  z.s = (size_t)(d->seed_head_stride ? d->H : 1) * d->M * d->D * elem;
+  z.kv = (size_t)d->B * d->H * d->N * d->D * elem;
+  z.md = (size_t)d->B * d->H * d->M * d->D * 4;
+  z.y = (size_t)d->B * d->H * d->N * d->D * 4;
+  return z;
+}
+
+}  // namespace
+
+extern "C" {
+
+int flarepp_abi_version(void) { return FLAREPP_ABI_VERSION; }
+
+const char* flarepp_status_string(flarepp_status s) {
+  switch (s) {
+    case FLAREPP_OK: return "ok";
+    case FLAREPP_INVALID_ARG: return "invalid argument";
+    case FLAREPP_UNSUPPORTED: return "unsupported shape or dtype";
+    case FLAREPP_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case FLAREPP_ALIASING: return "an output overlaps another buffer";
+    case FLAREPP_HIP_ERROR: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+flarepp_status flarepp_workspace_size(const flarepp_desc* desc, int32_t op, size_t* bytes) {
+  if (!bytes) return FLAREPP_INVALID_ARG;
+  FLAREPP_TRY(check_desc(desc));
+  if (op < FLAREPP_OP_SEED_ENCODE || op > FLAREPP_OP_FLARE) return FLAREPP_INVALID_ARG;
+  *bytes = make_plan(desc, op).total;
+  return FLAREPP_OK;
+}
+
+flarepp_status flarepp_seed_encode(const flarepp_desc* desc, const void* S, const void* K, const void* V,
+                                   float* Qd, void* ws, size_t ws_bytes, void* stream) {
+  FLAREPP_TRY(check_desc(desc));
+  const Sizes z = sizes(desc);
+  const void* in[3] = {S, K, V};
+  const size_t inb[3] = {z.s, z.kv, z.kv};
+  const void* out[1] = {Qd};
+  const size_t outb[1] = {z.md};
+  const bool req[1] = {true};
+  Plan p;
+  FLAREPP_TRY(prologue(desc, FLAREPP_OP_SEED_ENCODE, in, inb, 3, out, outb, req, 1, ws, ws_bytes, &p));
+  return dispatch(p, kSeed, S, nullptr, nullptr, K, V, nullptr, Qd, nullptr, ws, stream);
+}
+
+flarepp_status flarepp_encode(const flarepp_desc* desc, const float* Qd, const void* K, const void* V, float* Z,
+                              void* ws, size_t ws_bytes, void* stream) {
+  FLAREPP_TRY(check_desc(desc));
+  const Sizes z = sizes(desc);
+  const void* in[3] = {Qd, K, V};
+  const size_t inb[3] = {z.md, z.kv, z.kv};
+  const void* out[1] = {Z};
+  const size_t outb[1] = {z.md};
+  const bool req[1] = {true};
+  Plan p;
+  FLAREPP_TRY(prologue(desc, FLAREPP_OP_ENCODE, in, inb, 3, out, outb, req, 1, ws, ws_bytes, &p));
+  return dispatch(p, kEncode, nullptr, Qd, nullptr, K, V, nullptr, nullptr, Z, ws, stream);
+}
+
+flarepp_status flarepp_decode(const flarepp_desc* desc, const float* Qd, const float* Zin, const void* K, float* Y,
+                              void* ws, size_t ws_bytes, void* stream) {
+  FLAREPP_TRY(check_desc(desc));
+  const Sizes z = sizes(desc);
+  const void* in[3] = {Qd, Zin, K};
+  const size_t inb[3] = {z.md, z.md, z.kv};
+  const void* out[1] = {Y};
+  const size_t outb[1] = {z.y};
+  const bool req[1] = {true};
+  Plan p;
+  FLAREPP_TRY(prologue(desc, FLAREPP_OP_DECODE, in, inb, 3, out, outb, req, 1, ws, ws_bytes, &p));
+  return dispatch(p, kDecode, nullptr, Qd, Zin, K, nullptr, Y, nullptr, nullptr, ws, stream);
+}
+
+flarepp_status flarepp_route(const flarepp_desc* desc, const void* S, const void* K, const void* V, float* Y,
+                             float* Qd_out, float* Z_out, void* ws, size_t ws_bytes, void* stream) {
+  FLAREPP_TRY(check_desc(desc));
+  const Sizes z = sizes(desc);
+  const void* in[3] = {S, K, V};
+  const size_t inb[3] = {z.s, z.kv, z.kv};
+  const void* out[3] = {Y, Qd_out, Z_out};
+  const size_t outb[3] = {z.y, z.md, z.md};
+  const bool req[3] = {true, false, false};
+  Plan p;
+  FLAREPP_TRY(prologue(desc, FLAREPP_OP_ROUTE, in, inb, 3, out, outb, req, 3, ws, ws_bytes, &p));
+  return dispatch(p, kRoute, S, nullptr, nullptr, K, V, Y, Qd_out, Z_out, ws, stream);
+}
+
+flarepp_status flarepp_flare(const flarepp_desc* desc, const void* Q, const void* K, const void* V, float* Y,
+                             float* Z_out, void* ws, size_t ws_bytes, void* stream) {
+  FLAREPP_TRY(check_desc(desc));
+  const Sizes z = sizes(desc);
+  const void* in[3] = {Q, K, V};
+  const size_t inb[3] = {z.s, z.kv, z.kv};
+  const void* out[2] = {Y, Z_out};
+  const size_t outb[2] = {z.y, z.md};
+  const bool req[2] = {true, false};
+  Plan p;
+  FLAREPP_TRY(prologue(desc, FLAREPP_OP_FLARE, in, inb, 3, out, outb, req, 2, ws, ws_bytes, &p));
+  return dispatch(p, kFlare, Q, nullptr, nullptr, K, V, Y, nullptr, Z_out, ws, stream);
+}
+
+}  // extern "C"

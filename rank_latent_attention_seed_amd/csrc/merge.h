@@ -1,0 +1,179 @@
+// Cross-workgroup merge of split-N softmax partials, and the query-operand
+// preparation used by the next stage.
+//
+// A split j of the tokens leaves, per latent m, its running max mu_j (log2
+// units), the sum lambda_j of its weights exp2(t - mu_j) and the matching
+// unnormalised accumulator acc_j.  The exact softmax over all tokens is
+//     O_m = sum_j 2^(mu_j - mu) acc_j / sum_j 2^(mu_j - mu) lambda_j,
+//     mu  = max_j mu_j,
+// the same combination of "latent outputs and softmax statistics" the pages
+// use to join token shards across devices (French technical summary,
+// "Contributions Clés", context parallelism).  The merged rows are written as
+// float32 (the caller's Qd or Z) and, for the next stage, as bf16 operands:
+// c * row as a hi/lo pair (hi = bf16(x), lo = bf16(x - hi)), the unscaled row
+// as bf16, and the row's Euclidean norm.
+#pragma once
+
+#include "common.h"
+
+namespace flarepp {
+
+// Buffers marked [G] are indexed by the launch-local head lbh = blockIdx.y;
+// the caller's output by the global (b, h) = bh0 + lbh.
+struct MergeArgs {
+  const float* part;   // [G][J][Mp][D + 4]
+  int J, Mp, M;
+  int64_t bh0;
+  float* out;          // [BH][M][D] float32 (the caller's Qd or Z), or null
+  float* outl;         // [G][M][D] float32 staging copy, or null
+  __bf16* op_hi;       // [G][Mp][D] bf16(c * row), or null
+  __bf16* op_lo;       // [G][Mp][D] bf16(c * row - hi), or null
+  __bf16* op_zt;       // [G][D][Mp] bf16(row), transposed, or null
+  float* qnorm;        // [G][Mp] ||row||, or null
+  const float* knorm;  // [G][Jk] squared key norms per split of a seed encode, or null
+  int Jk;
+  float* bias;         // [G][Mp] bound c ||row|| max||K|| for the next encode (+inf if unsafe), or null
+  float c;
+};
+
+// Largest exponent span (log2 units) a bound-shifted softmax may cover: with
+// every exponent in [-100, 0] the largest weight is >= 2^-100, far above the
+// float32 / bf16 normal range floor 2^-126.
+constexpr float kBoundSpan = 100.0f;
+
+template <int D, int TPR>
+__global__ __launch_bounds__(256) void merge_partials(MergeArgs a) {
+  constexpr int PS = Part<D>::kStride;
+  constexpr int RPB = 256 / TPR;
+  const int tid = threadIdx.x;
+  const int r = tid / TPR, q = tid % TPR;
+  const int m = blockIdx.x * RPB + r;
+  const int64_t lbh = blockIdx.y, bh = a.bh0 + lbh;
+  const bool row_ok = m < a.Mp;
+  const int mm = row_ok ? m : a.Mp - 1;
+  const float* base = a.part + (lbh * a.J * (int64_t)a.Mp + mm) * PS;
+  const int64_t jstride = (int64_t)a.Mp * PS;
+
+  float mx = -INFINITY;
+  for (int jj = q; jj < a.J; jj += TPR) mx = fmaxf(mx, base[jj * jstride + D + 1]);
+#pragma unroll
+  for (int off = TPR / 2; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+
+  float den = 0.0f;
+  float num[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) num[d] = 0.0f;
+  for (int jj = q; jj < a.J; jj += TPR) {
+    const float* rec = base + jj * jstride;
+    const float w = fast_exp2(rec[D + 1] - mx);
+    den += w * rec[D];
+#pragma unroll
+    for (int d4 = 0; d4 < D / 4; ++d4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(rec + 4 * d4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) num[4 * d4 + e] += w * v[e];
+    }
+  }
+#pragma unroll
+  for (int off = TPR / 2; off >= 1; off >>= 1) {
+    den += __shfl_xor(den, off);
+#pragma unroll
+    for (int d = 0; d < D; ++d) num[d] += __shfl_xor(num[d], off);
+  }
+  const bool real = m < a.M;
+  const float inv = 1.0f / den;
+  float x[D];
+  float n2 = 0.0f;
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    x[d] = real ? num[d] * inv : 0.0f;
+    n2 += x[d] * x[d];
+  }
+  const float nrm = sqrtf(n2);
+
+  float kmax2 = 0.0f;
+  if (a.bias && a.knorm) {
+    const float* kn = a.knorm + lbh * a.Jk;
+    for (int jj = q; jj < a.Jk; jj += TPR) kmax2 = fmaxf(kmax2, kn[jj]);
+#pragma unroll
+    for (int off = TPR / 2; off >= 1; off >>= 1) kmax2 = fmaxf(kmax2, __shfl_xor(kmax2, off));
+  }
+  if (!row_ok) return;
+
+  const int64_t orow = (lbh * a.Mp + m) * D;
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    if (d % TPR != q) continue;
+    if (a.out && real) a.out[(bh * a.M + m) * D + d] = x[d];
+    if (a.outl && real) a.outl[(lbh * a.M + m) * D + d] = x[d];
+    if (a.op_hi) {
+      const float xs = x[d] * a.c;
+      const __bf16 hi = (__bf16)xs;
+      a.op_hi[orow + d] = hi;
+      if (a.op_lo) a.op_lo[orow + d] = (__bf16)(xs - (float)hi);
+    }
+    if (a.op_zt) a.op_zt[(lbh * D + d) * (int64_t)a.Mp + m] = (__bf16)x[d];
+  }
+  if (q == 0) {
+    if (a.qnorm) a.qnorm[lbh * a.Mp + m] = nrm;
+    if (a.bias) {
+      float bnd = INFINITY;
+      if (a.knorm) {
+        bnd = a.c * nrm * sqrtf(kmax2) * (1.0f + 1.0f / 4096.0f);
+        if (!(2.0f * bnd <= kBoundSpan)) bnd = INFINITY;
+      }
+      a.bias[lbh * a.Mp + m] = bnd;
+    }
+  }
+}
+
+// Operands from a caller's rows (float32 or bf16): nblk blocks of M x D rows,
+// block k starting at element src_off + k * src_blk -> [nblk][Mp][D] bf16 hi/lo
+// of c * row, [nblk][D][Mp] bf16 of the row (transposed) and row norms; rows
+// M..Mp-1 are zero.
+struct PrepArgs {
+  const void* src;
+  int src_bf16;
+  int64_t src_off, src_blk;
+  int nblk, M, Mp;
+  __bf16* op_hi;
+  __bf16* op_lo;
+  __bf16* op_zt;
+  float* qnorm;
+  float c;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void prep_rows(PrepArgs a) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)a.nblk * a.Mp) return;
+  const int64_t blk = idx / a.Mp;
+  const int m = (int)(idx - blk * a.Mp);
+  float x[D];
+  float n2 = 0.0f;
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    float v = 0.0f;
+    if (m < a.M) {
+      const int64_t s = a.src_off + blk * a.src_blk + (int64_t)m * D + d;
+      v = a.src_bf16 ? (float)reinterpret_cast<const __bf16*>(a.src)[s]
+                     : reinterpret_cast<const float*>(a.src)[s];
+    }
+    x[d] = v;
+    n2 += v * v;
+  }
+  const int64_t orow = idx * D;
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    if (a.op_hi) {
+      const float xs = x[d] * a.c;
+      const __bf16 hi = (__bf16)xs;
+      a.op_hi[orow + d] = hi;
+      if (a.op_lo) a.op_lo[orow + d] = (__bf16)(xs - (float)hi);
+    }
+    if (a.op_zt) a.op_zt[(blk * D + d) * (int64_t)a.Mp + m] = (__bf16)x[d];
+  }
+  if (a.qnorm) a.qnorm[idx] = sqrtf(n2);
+}
+
+}  // namespace flarepp

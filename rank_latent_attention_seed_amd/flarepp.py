@@ -1,0 +1,273 @@
+"""Thin Python binding of libflarepp (ctypes).
+
+The functions named ``flarepp_*`` mirror the C ABI in ``include/flarepp.h``
+one to one: they take a :class:`FlareppDesc`, raw device addresses (ints) and
+a stream handle, and only marshal arguments.  ``route``, ``seed_encode``,
+``encode``, ``decode`` and ``flare`` are conveniences over them that take
+torch tensors already on the GPU and allocate outputs and workspace with
+torch (device memory and streams are all torch is used for).  Every step of
+the computation runs in the library's HIP kernels; there is no fallback: if
+``libflarepp.so`` is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_PKG, "libflarepp.so")
+
+F32, BF16 = 0, 1
+OP_SEED_ENCODE, OP_ENCODE, OP_DECODE, OP_ROUTE, OP_FLARE = range(5)
+STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE_TOO_SMALL", 4: "ALIASING",
+          5: "HIP_ERROR"}
+ABI_VERSION = 1
+SYMBOLS = ("flarepp_abi_version", "flarepp_status_string", "flarepp_workspace_size",
+           "flarepp_seed_encode", "flarepp_encode", "flarepp_decode", "flarepp_route",
+           "flarepp_flare")
+
+
+class FlareppDesc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int64),
+        ("H", ctypes.c_int64),
+        ("N", ctypes.c_int64),
+        ("M", ctypes.c_int64),
+        ("D", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("seed_head_stride", ctypes.c_int64),
+    ]
+
+
+class FlareppError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({_lib().flarepp_status_string(status).decode()})")
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIBRARY):
+            raise RuntimeError(
+                f"{LIBRARY} is not built; run `python -m rank_latent_attention_seed_amd.build` "
+                "(or __graft_entry__.build()) first")
+        lib = ctypes.CDLL(LIBRARY)
+        vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+        dp = ctypes.POINTER(FlareppDesc)
+        lib.flarepp_abi_version.restype = ctypes.c_int
+        lib.flarepp_abi_version.argtypes = []
+        lib.flarepp_status_string.restype = ctypes.c_char_p
+        lib.flarepp_status_string.argtypes = [ctypes.c_int]
+        lib.flarepp_workspace_size.restype = ctypes.c_int
+        lib.flarepp_workspace_size.argtypes = [dp, i32, ctypes.POINTER(sz)]
+        lib.flarepp_seed_encode.restype = ctypes.c_int
+        lib.flarepp_seed_encode.argtypes = [dp, vp, vp, vp, vp, vp, sz, vp]
+        lib.flarepp_encode.restype = ctypes.c_int
+        lib.flarepp_encode.argtypes = [dp, vp, vp, vp, vp, vp, sz, vp]
+        lib.flarepp_decode.restype = ctypes.c_int
+        lib.flarepp_decode.argtypes = [dp, vp, vp, vp, vp, vp, sz, vp]
+        lib.flarepp_route.restype = ctypes.c_int
+        lib.flarepp_route.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.flarepp_flare.restype = ctypes.c_int
+        lib.flarepp_flare.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
+        if lib.flarepp_abi_version() != ABI_VERSION:
+            raise RuntimeError("libflarepp ABI version mismatch")
+        _LIB = lib
+    return _LIB
+
+
+def library():
+    """The loaded ctypes library (raises if it is not built)."""
+    return _lib()
+
+
+def make_desc(B, H, N, M, D, dtype, scale, seed_head_stride=0) -> FlareppDesc:
+    return FlareppDesc(int(B), int(H), int(N), int(M), int(D), int(dtype), float(scale),
+                       int(seed_head_stride))
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise FlareppError(status, where)
+
+
+# ---------------------------------------------------------------- C ABI ----
+
+def flarepp_abi_version() -> int:
+    return _lib().flarepp_abi_version()
+
+
+def flarepp_status_string(status: int) -> str:
+    return _lib().flarepp_status_string(status).decode()
+
+
+def flarepp_workspace_size(desc: FlareppDesc, op: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib().flarepp_workspace_size(ctypes.byref(desc), op, ctypes.byref(n)),
+           "flarepp_workspace_size")
+    return n.value
+
+
+def flarepp_seed_encode(desc, S, K, V, Qd, ws, ws_bytes, stream) -> int:
+    return _lib().flarepp_seed_encode(ctypes.byref(desc), S, K, V, Qd, ws, ws_bytes, stream)
+
+
+def flarepp_encode(desc, Qd, K, V, Z, ws, ws_bytes, stream) -> int:
+    return _lib().flarepp_encode(ctypes.byref(desc), Qd, K, V, Z, ws, ws_bytes, stream)
+
+
+def flarepp_decode(desc, Qd, Z, K, Y, ws, ws_bytes, stream) -> int:
+    return _lib().flarepp_decode(ctypes.byref(desc), Qd, Z, K, Y, ws, ws_bytes, stream)
+
+
+def flarepp_route(desc, S, K, V, Y, Qd_out, Z_out, ws, ws_bytes, stream) -> int:
+    return _lib().flarepp_route(ctypes.byref(desc), S, K, V, Y, Qd_out, Z_out, ws, ws_bytes, stream)
+
+
+def flarepp_flare(desc, Q, K, V, Y, Z_out, ws, ws_bytes, stream) -> int:
+    return _lib().flarepp_flare(ctypes.byref(desc), Q, K, V, Y, Z_out, ws, ws_bytes, stream)
+
+
+# ------------------------------------------------------ torch plumbing -----
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _require(t, name):
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous GPU tensor")
+
+
+def desc_for(S, K, scale) -> FlareppDesc:
+    """Descriptor from K (B x H x N x D) and S (M x D or H x M x D)."""
+    B, H, N, D = K.shape
+    if S.dim() == 2:
+        M, shs = S.shape[0], 0
+    elif S.dim() == 3 and S.shape[0] == H:
+        M = S.shape[1]
+        shs = M * D
+    else:
+        raise ValueError("S must be M x D or H x M x D")
+    return make_desc(B, H, N, M, D, _dtype_code(K), scale, shs)
+
+
+class Workspace:
+    """A reusable device workspace (grown on demand, never shrunk)."""
+
+    def __init__(self, device=None):
+        self.buf = None
+        self.device = device
+
+    def get(self, nbytes: int):
+        torch = _torch()
+        if nbytes == 0:
+            return None, 0
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device or "cuda")
+        return self.buf, self.buf.numel()
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def route(S, K, V, scale, *, with_intermediates=False, workspace: Workspace | None = None, stream=None,
+          out=None):
+    """Y (and optionally Qd, Z) of the full route for GPU tensors S, K, V."""
+    torch = _torch()
+    for t, n in ((S, "S"), (K, "K"), (V, "V")):
+        _require(t, n)
+    desc = desc_for(S, K, scale)
+    B, H, N, D = K.shape
+    M = desc.M
+    Y = out if out is not None else torch.empty((B, H, N, D), dtype=torch.float32, device=K.device)
+    Qd = Z = None
+    if with_intermediates:
+        Qd = torch.empty((B, H, M, D), dtype=torch.float32, device=K.device)
+        Z = torch.empty((B, H, M, D), dtype=torch.float32, device=K.device)
+    ws = workspace or Workspace(K.device)
+    buf, nbytes = ws.get(flarepp_workspace_size(desc, OP_ROUTE))
+    _check(flarepp_route(desc, _ptr(S), _ptr(K), _ptr(V), _ptr(Y), _ptr(Qd), _ptr(Z), _ptr(buf),
+                         nbytes, _stream(stream)), "flarepp_route")
+    return (Y, Qd, Z) if with_intermediates else Y
+
+
+def seed_encode(S, K, V, scale, *, workspace: Workspace | None = None, stream=None):
+    torch = _torch()
+    for t, n in ((S, "S"), (K, "K"), (V, "V")):
+        _require(t, n)
+    desc = desc_for(S, K, scale)
+    B, H, N, D = K.shape
+    Qd = torch.empty((B, H, desc.M, D), dtype=torch.float32, device=K.device)
+    ws = workspace or Workspace(K.device)
+    buf, nbytes = ws.get(flarepp_workspace_size(desc, OP_SEED_ENCODE))
+    _check(flarepp_seed_encode(desc, _ptr(S), _ptr(K), _ptr(V), _ptr(Qd), _ptr(buf), nbytes,
+                               _stream(stream)), "flarepp_seed_encode")
+    return Qd
+
+
+def encode(Qd, K, V, scale, *, workspace: Workspace | None = None, stream=None):
+    torch = _torch()
+    for t, n in ((Qd, "Qd"), (K, "K"), (V, "V")):
+        _require(t, n)
+    B, H, N, D = K.shape
+    desc = make_desc(B, H, N, Qd.shape[2], D, _dtype_code(K), scale, 0)
+    Z = torch.empty_like(Qd)
+    ws = workspace or Workspace(K.device)
+    buf, nbytes = ws.get(flarepp_workspace_size(desc, OP_ENCODE))
+    _check(flarepp_encode(desc, _ptr(Qd), _ptr(K), _ptr(V), _ptr(Z), _ptr(buf), nbytes,
+                          _stream(stream)), "flarepp_encode")
+    return Z
+
+
+def decode(Qd, Z, K, scale, *, workspace: Workspace | None = None, stream=None):
+    torch = _torch()
+    for t, n in ((Qd, "Qd"), (Z, "Z"), (K, "K")):
+        _require(t, n)
+    B, H, N, D = K.shape
+    desc = make_desc(B, H, N, Qd.shape[2], D, _dtype_code(K), scale, 0)
+    Y = torch.empty((B, H, N, D), dtype=torch.float32, device=K.device)
+    ws = workspace or Workspace(K.device)
+    buf, nbytes = ws.get(flarepp_workspace_size(desc, OP_DECODE))
+    _check(flarepp_decode(desc, _ptr(Qd), _ptr(Z), _ptr(K), _ptr(Y), _ptr(buf), nbytes,
+                          _stream(stream)), "flarepp_decode")
+    return Y
+
+
+def flare(Q, K, V, scale, *, with_latents=False, workspace: Workspace | None = None, stream=None):
+    """Fixed-query FLARE: Y (and optionally Z) with parameter queries Q."""
+    torch = _torch()
+    for t, n in ((Q, "Q"), (K, "K"), (V, "V")):
+        _require(t, n)
+    desc = desc_for(Q, K, scale)
+    B, H, N, D = K.shape
+    Y = torch.empty((B, H, N, D), dtype=torch.float32, device=K.device)
+    Z = torch.empty((B, H, desc.M, D), dtype=torch.float32, device=K.device) if with_latents else None
+    ws = workspace or Workspace(K.device)
+    buf, nbytes = ws.get(flarepp_workspace_size(desc, OP_FLARE))
+    _check(flarepp_flare(desc, _ptr(Q), _ptr(K), _ptr(V), _ptr(Y), _ptr(Z), _ptr(buf), nbytes,
+                         _stream(stream)), "flarepp_flare")
+    return (Y, Z) if with_latents else Y

@@ -313,11 +313,12 @@ def make_problem(name: str) -> Problem:
 
 def random_problem(B: int, H: int, N: int, M: int, D: int, dtype: str = "bf16",
                    scale: float | None = None, seed: int = 0, per_head_seeds: bool = False,
-                   sigma: float = 1.0) -> Problem:
-    """iid N(0, sigma^2) K and V, N(0, 1) seeds: for edge shapes (ragged N, small M, ...)."""
+                   sigma: float = 1.0, sigma_v: float | None = None) -> Problem:
+    """iid N(0, sigma^2) K, N(0, sigma_v^2) V (sigma_v defaults to sigma), N(0, 1) seeds:
+    for edge shapes (ragged N, small M, ...) and sharpness sweeps."""
     rng = np.random.default_rng(seed)
     K = _noise(rng, (B, H, N, D), sigma)
-    V = _noise(rng, (B, H, N, D), sigma)
+    V = _noise(rng, (B, H, N, D), sigma if sigma_v is None else sigma_v)
     S = rng.standard_normal((H, M, D) if per_head_seeds else (M, D)).astype(np.float32)
     if scale is None:
         scale = 1 / math.sqrt(D)

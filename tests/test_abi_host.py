@@ -1,0 +1,119 @@
+"""libflarepp's C ABI on the host: the library loads, exports every symbol the
+header declares, sizes workspaces, and rejects bad arguments with the
+documented status codes before touching the GPU (no compute call here
+reaches a kernel launch, so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from rank_latent_attention_seed_amd import flarepp as fp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flarepp.h")
+
+OK, INVALID_ARG, UNSUPPORTED, WS_SMALL, ALIASING = 0, 1, 2, 3, 4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flarepp_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = fp.library()
+    names = declared_functions()
+    assert set(names) == set(fp.SYMBOLS), names
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_strings():
+    assert fp.flarepp_abi_version() == fp.ABI_VERSION
+    for code in range(6):
+        assert isinstance(fp.flarepp_status_string(code), str)
+    assert fp.flarepp_status_string(99) == "unknown status"
+
+
+def desc(**kw):
+    d = dict(B=2, H=3, N=1000, M=64, D=32, dtype=fp.BF16, scale=0.25, seed_head_stride=0)
+    d.update(kw)
+    return fp.make_desc(**d)
+
+
+def ws_status(d, op):
+    n = ctypes.c_size_t(0)
+    return fp.library().flarepp_workspace_size(ctypes.byref(d), op, ctypes.byref(n)), n.value
+
+
+@pytest.mark.parametrize("op", range(5))
+def test_workspace_sizes(op):
+    st, n_bf16 = ws_status(desc(), op)
+    assert st == OK
+    st, n_f32 = ws_status(desc(dtype=fp.F32), op)
+    assert st == OK
+    if op == fp.OP_DECODE:
+        assert n_f32 == 0 and n_bf16 > 0
+    else:
+        assert n_f32 > 0 and n_bf16 > 0
+    # partial records grow with the latent count
+    assert ws_status(desc(M=256), op)[1] >= n_bf16
+
+
+def test_workspace_size_rejects():
+    assert ws_status(desc(D=24), fp.OP_ROUTE)[0] == UNSUPPORTED
+    assert ws_status(desc(M=257), fp.OP_ROUTE)[0] == UNSUPPORTED
+    assert ws_status(desc(dtype=7), fp.OP_ROUTE)[0] == UNSUPPORTED
+    assert ws_status(desc(N=0), fp.OP_ROUTE)[0] == INVALID_ARG
+    assert ws_status(desc(scale=float("nan")), fp.OP_ROUTE)[0] == INVALID_ARG
+    assert ws_status(desc(seed_head_stride=5), fp.OP_ROUTE)[0] == INVALID_ARG
+    assert ws_status(desc(), 9)[0] == INVALID_ARG
+    assert ws_status(desc(seed_head_stride=64 * 32), fp.OP_ROUTE)[0] == OK
+    n = ctypes.c_size_t(0)
+    assert fp.library().flarepp_workspace_size(None, 0, ctypes.byref(n)) == INVALID_ARG
+
+
+# Fake, never-dereferenced device addresses: every call below fails
+# validation on the host and returns before any HIP call.
+A = 1 << 40
+
+
+def addr(i):
+    return A + i * (1 << 34)
+
+
+def route(d, S=addr(0), K=addr(1), V=addr(2), Y=addr(3), Qd=addr(4), Z=addr(5), ws=addr(6), nbytes=None):
+    if nbytes is None:
+        nbytes = ws_status(d, fp.OP_ROUTE)[1]
+    return fp.flarepp_route(d, S, K, V, Y, Qd, Z, ws, nbytes, None)
+
+
+def test_route_validation():
+    d = desc()
+    assert route(d, S=None) == INVALID_ARG
+    assert route(d, K=None) == INVALID_ARG
+    assert route(d, Y=None) == INVALID_ARG
+    assert route(d, K=addr(1) + 2) == INVALID_ARG        # misaligned
+    assert route(d, ws=None) == INVALID_ARG
+    assert route(d, nbytes=16) == WS_SMALL
+    assert route(d, Y=addr(1) + 64) == ALIASING           # output inside K
+    assert route(d, Qd=addr(3) + 16) == ALIASING          # two outputs overlap
+    assert route(d, Z=addr(6)) == ALIASING                # output inside the workspace
+    assert route(desc(D=64)) == UNSUPPORTED
+    assert route(desc(M=0)) == INVALID_ARG
+
+
+def test_stage_validation():
+    d = desc()
+    n = ws_status(d, fp.OP_SEED_ENCODE)[1]
+    assert fp.flarepp_seed_encode(d, addr(0), addr(1), addr(2), None, addr(6), n, None) == INVALID_ARG
+    n = ws_status(d, fp.OP_ENCODE)[1]
+    assert fp.flarepp_encode(d, addr(0), addr(1), addr(2), addr(0), addr(6), n, None) == ALIASING
+    n = ws_status(d, fp.OP_DECODE)[1]
+    assert fp.flarepp_decode(d, addr(0), addr(1), addr(2), addr(3), addr(6), n - 1, None) == WS_SMALL
+    n = ws_status(d, fp.OP_FLARE)[1]
+    assert fp.flarepp_flare(d, addr(0), None, addr(2), addr(3), None, addr(6), n, None) == INVALID_ARG
+    assert fp.library().flarepp_route(None, addr(0), addr(1), addr(2), addr(3), None, None, addr(6),
+                                      1 << 30, None) == INVALID_ARG

@@ -1,0 +1,197 @@
+"""GPU parity of libflarepp against the CPU oracle, through the C ABI.
+
+Every case draws seeded inputs, runs the HIP path, and compares Qd, Z and Y
+element by element with the fp64 oracle on the same input bytes (bf16 inputs
+are compared against the oracle fed the same bf16 values)."""
+import math
+
+import numpy as np
+import pytest
+
+from rank_latent_attention_seed_amd import inputs
+from gpu_util import all_heads, assert_close, oracle_heads, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fp():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from rank_latent_attention_seed_amd import flarepp
+
+    flarepp.library()
+    return flarepp
+
+
+def run_and_compare(fp, p, heads=None, label=""):
+    import torch
+
+    print(f"\n  case {label or p.name}: B{p.B} H{p.H} N{p.N} M{p.M} D{p.D} {p.dtype} s={p.scale:g}",
+          flush=True)
+    S, K, V = to_device(p.S), to_device(p.K), to_device(p.V)
+    Y, Qd, Z = fp.route(S, K, V, p.scale, with_intermediates=True)
+    torch.cuda.synchronize()
+    Y, Qd, Z = Y.cpu().numpy(), Qd.cpu().numpy(), Z.cpu().numpy()
+    heads = heads or all_heads(p.B, p.H)
+    ref = oracle_heads(p.S, p.K, p.V, p.scale, heads)
+    got_q = np.stack([Qd[b, h] for b, h in heads])
+    got_z = np.stack([Z[b, h] for b, h in heads])
+    got_y = np.stack([Y[b, h] for b, h in heads])
+    out = {}
+    out["Qd"] = assert_close("Qd", got_q, np.stack([r[0] for r in ref]), p.dtype)
+    out["Z"] = assert_close("Z", got_z, np.stack([r[1] for r in ref]), p.dtype)
+    out["Y"] = assert_close("Y", got_y, np.stack([r[2] for r in ref]), p.dtype)
+    assert np.isfinite(Y).all()
+    return out
+
+
+@pytest.mark.parametrize("name", ["tiny", "mesh", "cloud", "stress"])
+def test_named_problem(fp, name):
+    run_and_compare(fp, inputs.make_problem(name))
+
+
+def test_longseq_sampled_heads(fp):
+    p = inputs.make_problem("longseq")
+    rng = np.random.default_rng(7)
+    heads = [tuple(x) for x in rng.choice(all_heads(p.B, p.H), size=24, replace=False)]
+    run_and_compare(fp, p, heads=heads)
+
+
+EDGE = [
+    # B, H, N, M, D, dtype
+    (1, 1, 1, 1, 16, "bf16"),
+    (1, 2, 2, 5, 32, "bf16"),
+    (2, 1, 63, 17, 32, "bf16"),
+    (1, 2, 129, 100, 16, "bf16"),
+    (1, 1, 1000, 256, 32, "bf16"),
+    (2, 2, 4097, 33, 32, "bf16"),
+    (1, 3, 300, 48, 16, "bf16"),
+    (1, 1, 1, 1, 32, "f32"),
+    (1, 2, 77, 19, 16, "f32"),
+    (2, 1, 1000, 256, 32, "f32"),
+    (1, 1, 5000, 64, 32, "f32"),
+]
+
+
+@pytest.mark.parametrize("B,H,N,M,D,dtype", EDGE)
+def test_edge_shapes(fp, B, H, N, M, D, dtype):
+    p = inputs.random_problem(B, H, N, M, D, dtype=dtype, seed=N * 31 + M)
+    run_and_compare(fp, p, label=f"edge {dtype} N{N} M{M} D{D}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_per_head_seeds(fp, dtype):
+    p = inputs.random_problem(2, 3, 700, 40, 32, dtype=dtype, seed=5, per_head_seeds=True)
+    run_and_compare(fp, p, label=f"per-head seeds {dtype}")
+
+
+@pytest.mark.parametrize("scale", [0.0, 1.0, 0.05])
+def test_scales(fp, scale):
+    p = inputs.random_problem(1, 2, 2000, 64, 32, dtype="bf16", scale=scale, seed=9)
+    run_and_compare(fp, p, label=f"scale {scale}")
+
+
+def test_large_logits_take_the_online_path(fp):
+    # sigma 4 keys with s = 1: the norm bounds exceed the safe exponent span,
+    # so the encode and decode fall back to exact running maxima.  Values keep
+    # unit scale: the bf16 path's error is ~2^-9 times the spread of V.
+    p = inputs.random_problem(1, 1, 3000, 32, 16, dtype="bf16", scale=1.0, seed=3, sigma=4.0,
+                              sigma_v=1.0)
+    run_and_compare(fp, p, label="large logits")
+
+
+def test_stages_match_oracle(fp):
+    import torch
+    import oracle
+
+    p = inputs.random_problem(2, 2, 1500, 48, 32, dtype="bf16", seed=21)
+    print(f"\n  case stages: B{p.B} H{p.H} N{p.N} M{p.M}", flush=True)
+    S, K, V = to_device(p.S), to_device(p.K), to_device(p.V)
+    ref = oracle_heads(p.S, p.K, p.V, p.scale, all_heads(p.B, p.H))
+    Qd_ref = np.stack([r[0] for r in ref]).reshape(p.B, p.H, p.M, p.D)
+    Z_ref = np.stack([r[1] for r in ref]).reshape(p.B, p.H, p.M, p.D)
+    Y_ref = np.stack([r[2] for r in ref]).reshape(p.B, p.H, p.N, p.D)
+    Qd = fp.seed_encode(S, K, V, p.scale)
+    # the later stages take the oracle's Qd / Z as inputs, so each stage is checked alone
+    Qd_o = torch.from_numpy(Qd_ref.astype(np.float32)).cuda()
+    Z_o = torch.from_numpy(Z_ref.astype(np.float32)).cuda()
+    Z = fp.encode(Qd_o, K, V, p.scale)
+    Y = fp.decode(Qd_o, Z_o, K, p.scale)
+    torch.cuda.synchronize()
+    assert_close("seed_encode", Qd.cpu().numpy(), Qd_ref, "bf16")
+    assert_close("encode", Z.cpu().numpy(), Z_ref, "bf16")
+    assert_close("decode", Y.cpu().numpy(), Y_ref, "bf16")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_fixed_query_flare(fp, dtype):
+    import torch
+    import oracle
+
+    p = inputs.random_problem(1, 2, 900, 24, 16, dtype=dtype, seed=12)
+    print(f"\n  case flare {dtype}", flush=True)
+    Q, K, V = to_device(p.S), to_device(p.K), to_device(p.V)
+    Y, Z = fp.flare(Q, K, V, p.scale, with_latents=True)
+    torch.cuda.synchronize()
+    Z_ref, Y_ref = oracle.flare(p.S, p.K, p.V, p.scale)
+    assert_close("Z", Z.cpu().numpy(), Z_ref, dtype)
+    assert_close("Y", Y.cpu().numpy(), Y_ref, dtype)
+
+
+def test_deterministic_and_split_invariant(fp, monkeypatch):
+    import torch
+
+    p = inputs.random_problem(1, 2, 20000, 128, 32, dtype="bf16", seed=4)
+    print("\n  case determinism / split invariance", flush=True)
+    S, K, V = to_device(p.S), to_device(p.K), to_device(p.V)
+    a = fp.route(S, K, V, p.scale, with_intermediates=True)
+    b = fp.route(S, K, V, p.scale, with_intermediates=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y), "two identical calls differ"
+    monkeypatch.setenv("FLAREPP_SPLITS", "1")
+    c = fp.route(S, K, V, p.scale, with_intermediates=True)
+    monkeypatch.setenv("FLAREPP_SPLITS", "7")
+    d = fp.route(S, K, V, p.scale, with_intermediates=True)
+    torch.cuda.synchronize()
+    for x, y, z in zip(a, c, d):
+        assert float((x - y).abs().max()) <= 1e-2
+        assert float((x - z).abs().max()) <= 1e-2
+    # grouping heads into launches does not change any head's arithmetic
+    monkeypatch.setenv("FLAREPP_HEAD_GROUP", "1")
+    e = fp.route(S, K, V, p.scale, with_intermediates=True)
+    monkeypatch.setenv("FLAREPP_HEAD_GROUP", "2")
+    f = fp.route(S, K, V, p.scale, with_intermediates=True)
+    torch.cuda.synchronize()
+    for x, y in zip(e, f):
+        assert torch.equal(x, y), "head grouping changed results"
+
+
+def test_outputs_only_y(fp):
+    import torch
+
+    p = inputs.random_problem(1, 1, 500, 16, 32, dtype="bf16", seed=2)
+    S, K, V = to_device(p.S), to_device(p.K), to_device(p.V)
+    Y1 = fp.route(S, K, V, p.scale)
+    Y2, _, _ = fp.route(S, K, V, p.scale, with_intermediates=True)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2)
+
+
+def test_error_status_on_device_buffers(fp):
+    import torch
+
+    p = inputs.random_problem(1, 1, 256, 16, 32, dtype="bf16", seed=1)
+    S, K, V = to_device(p.S), to_device(p.K), to_device(p.V)
+    d = fp.desc_for(S, K, p.scale)
+    Y = torch.empty((1, 1, 256, 32), dtype=torch.float32, device="cuda")
+    n = fp.flarepp_workspace_size(d, fp.OP_ROUTE)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    st = fp.flarepp_route(d, S.data_ptr(), K.data_ptr(), V.data_ptr(), Y.data_ptr(), None, None,
+                          ws.data_ptr(), n - 1, None)
+    assert st == 3
+    st = fp.flarepp_route(d, S.data_ptr(), K.data_ptr(), V.data_ptr(), K.data_ptr(), None, None,
+                          ws.data_ptr(), n, None)
+    assert st == 4
