@@ -157,6 +157,29 @@ flarepp_status flarepp_flare(const flarepp_desc *desc, const void *Q, const void
                              const void *V, float *Y, float *Z_out, void *ws, size_t ws_bytes,
                              void *stream);
 
+/* Kernel kinds reported by flarepp_route_profiled. */
+typedef enum flarepp_kernel_kind {
+    FLAREPP_KERNEL_PREP = 0,        /* query / value operand preparation */
+    FLAREPP_KERNEL_SEED_ENCODE = 1, /* split-N seed encode */
+    FLAREPP_KERNEL_ENCODE = 2,      /* split-N encode */
+    FLAREPP_KERNEL_MERGE = 3,       /* merge of split partials */
+    FLAREPP_KERNEL_DECODE = 4       /* decode */
+} flarepp_kernel_kind;
+
+/*
+ * Instrumented flarepp_route for measurement: identical work, plus events
+ * recorded on `stream` around every kernel launch.  events: 2*max_launches
+ * hipEvent_t handles created by the caller; launch i records events[2i]
+ * before and events[2i+1] after it and stores its flarepp_kernel_kind in
+ * kinds[i].  *n_launches receives the number of launches (which may exceed
+ * max_launches; launches beyond it are not recorded).  A failed event
+ * record is reported as FLAREPP_HIP_ERROR.
+ */
+flarepp_status flarepp_route_profiled(const flarepp_desc *desc, const void *S, const void *K,
+                                      const void *V, float *Y, float *Qd_out, float *Z_out,
+                                      void *ws, size_t ws_bytes, void *stream, void **events,
+                                      int32_t *kinds, int32_t max_launches, int32_t *n_launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -65,11 +65,35 @@ __device__ __forceinline__ float sum_over_rows(float x) {
   return __uint_as_float(t[0]) + __uint_as_float(t[1]);
 }
 
+// All-lane reductions over a whole wave using DPP row operations and the
+// two permlane swaps (VALU only): quad butterflies, rotations by 4 and 8
+// within each 16-lane row, then across rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp<0x124>(x);  // row_ror:4
+  x += dpp<0x128>(x);  // row_ror:8
+  return sum_over_rows(x);
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0x124>(x));
+  x = fmaxf(x, dpp<0x128>(x));
+  return max_over_rows(x);
+}
+
 __device__ __forceinline__ float max3(float a, float b, float c) {
   return fmaxf(fmaxf(a, b), c);  // v_max3_f32
 }
 
-// Per-split softmax partial record: acc[0..D-1], sum at D, max (log2 units) at D+1.
+// Per-split softmax partial record: acc[0..D-1], sum at D, max (log2 units) at
+// D+1.  Records are stored [head][latent][split] so that one latent's records
+// are contiguous for the merge.
 template <int D>
 struct Part {
   static constexpr int kStride = D + 4;  // 16-byte aligned records

@@ -11,13 +11,19 @@
 // technical summary, "Contributions Clés", multi-GPU context parallelism).
 //
 // Work decomposition.  A 256-thread workgroup owns one (b, h, split, latent
-// group); its four waves own MBW 16-latent blocks each and share K/V tiles of
-// TN tokens staged through LDS (double buffered: global loads for tile t+1 are
-// in flight while tile t is consumed).  Per 32-token step a wave computes
-// S^T = K Q^T tiles (rows = tokens, cols = latents), turns them into softmax
-// weights in registers, and accumulates O^T += V^T P^T on the matrix cores.
-// V is written to LDS transposed ([d][token]) so that its A-operand slices
-// are two 8-byte reads.
+// group); its four waves own MBW 16-latent blocks each and share tiles of TN
+// tokens of K and V.  Tiles travel HBM -> LDS by direct-to-LDS loads (no
+// staging registers) through a ring of four slots: while tile t is consumed,
+// the loads of tiles t+1 and t+2 are in flight and tile t+3's are issued.
+// The slots are distinct LDS variables and the tile loop is unrolled by four,
+// so each access names its slot statically and waiting for tile t's loads
+// (s_waitcnt vmcnt) leaves the younger tiles' loads running.  16-byte chunks
+// of each token row are XOR-swizzled in LDS (the fetching lane picks the
+// chunk that belongs to its slot) so the matrix-core operand reads are free
+// of bank conflicts.  Per 32-token step a wave computes S^T = K Q^T tiles
+// (rows = tokens, cols = latents), turns them into softmax weights in
+// registers, and accumulates O^T += V^T P^T; V's operand comes from the
+// token-major tile through transposing LDS reads (ds_read_b64_tr_b16).
 //
 // Softmax arithmetic.  The query operand arrives pre-multiplied by
 // c = s * log2(e) as a bf16 hi/lo pair (two MFMAs per tile, ~16 mantissa
@@ -45,7 +51,7 @@ struct EncodeArgs {
   int64_t q_off;       // the operand rows of (b, h) start at b*q_sb + h*q_sh - q_off
   const __bf16* K;     // B x H x N x D
   const __bf16* V;     // B x H x N x D
-  float* part;         // [G][J][Mp][D + 4] partial records (G = heads of this launch)
+  float* part;         // [G][Mp][J][D + 4] partial records (G = heads of this launch)
   float* knorm;        // [G][J] max squared key norm of each split, or null
   const float* bias;   // [G][Mp] mu_m bound (log2 units; +inf = use online), or null
   int H, N, Mp, J, chunk;
@@ -67,18 +73,237 @@ struct KOperand<16> {
   __device__ __forceinline__ static f32x4 mma(T a, T b, f32x4 c) { return mfma_k16(a, b, c); }
 };
 
-template <int D, int MBW, bool KNORM>
-__global__ __launch_bounds__(256, 2) void encode_split_bf16(EncodeArgs a) {
-  constexpr int TN = 4096 / D;   // tokens per LDS tile: 8 KB of K
-  constexpr int VROW = TN + 8;   // transposed-V row stride (elements); 4-dword skew per row
-  constexpr int DB = D / 16;     // 16-row blocks of O^T
+// ---- the LDS ring: four K slots and four V slots of one tile each
+// (TN * D = 4096 bf16 = 8 KB for D = 16 and D = 32).
+constexpr int kTileElems = 4096;
+__shared__ __attribute__((aligned(16))) __bf16 enc_k0[kTileElems];
+__shared__ __attribute__((aligned(16))) __bf16 enc_k1[kTileElems];
+__shared__ __attribute__((aligned(16))) __bf16 enc_k2[kTileElems];
+__shared__ __attribute__((aligned(16))) __bf16 enc_k3[kTileElems];
+__shared__ __attribute__((aligned(16))) __bf16 enc_v0[kTileElems];
+__shared__ __attribute__((aligned(16))) __bf16 enc_v1[kTileElems];
+__shared__ __attribute__((aligned(16))) __bf16 enc_v2[kTileElems];
+__shared__ __attribute__((aligned(16))) __bf16 enc_v3[kTileElems];
+template <int I>
+__device__ __forceinline__ __bf16* ring_k() {
+  return I == 0 ? enc_k0 : I == 1 ? enc_k1 : I == 2 ? enc_k2 : enc_k3;
+}
+template <int I>
+__device__ __forceinline__ __bf16* ring_v() {
+  return I == 0 ? enc_v0 : I == 1 ? enc_v1 : I == 2 ? enc_v2 : enc_v3;
+}
+
+// Swizzle of the 16-byte chunks of token row t (D/8 chunks per row): the
+// chunk holding elements 8u..8u+7 sits at position u ^ swz(t).
+template <int D>
+__device__ __forceinline__ int chunk_swz(int t) {
+  return D == 32 ? ((t >> 2) & 3) : ((t >> 3) & 1);
+}
+// Element offset of (token t, element e) inside a tile slot.
+template <int D>
+__device__ __forceinline__ int slot_off(int t, int e) {
+  return t * D + ((((e >> 3) ^ chunk_swz<D>(t)) << 3) | (e & 7));
+}
+
+#define FLAREPP_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#define FLAREPP_GLB(p) ((__attribute__((address_space(1))) void*)(p))
+// s_waitcnt with vmcnt <= n (n < 64); lgkmcnt and expcnt are not waited on.
+#define FLAREPP_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | (((n) >> 4) << 14))
+
+// Issue the direct-to-LDS loads of one tile into slot I: each wave fetches
+// 2 KB of K and 2 KB of V (two 1 KB instructions each); lane l of an
+// instruction fills LDS chunk base + 16 l and therefore fetches the (token,
+// chunk) that the swizzle places there.  Tokens past the split re-read the
+// split's last row (they receive zero weight), so every tile issues the same
+// number of loads and the wait counts stay uniform.
+template <int D, int I>
+__device__ __forceinline__ void tile_dma(const __bf16* Kp, const __bf16* Vp, int tb, int n1, int wave, int lane) {
+  constexpr int U = D / 8;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int blk = wave * 2 + i;
+    const int s = blk * 64 + lane;
+    const int t = s / U;
+    const int u = (s % U) ^ chunk_swz<D>(t);
+    const int64_t src = (int64_t)min(tb + t, n1 - 1) * D + 8 * u;
+    __builtin_amdgcn_global_load_lds(FLAREPP_GLB(Kp + src), FLAREPP_LDS(ring_k<I>() + blk * 512), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(FLAREPP_GLB(Vp + src), FLAREPP_LDS(ring_v<I>() + blk * 512), 16, 0, 0);
+  }
+}
+constexpr int kDmaPerTile = 4;  // load instructions per wave per tile
+
+// Per-wave register state of the encode: query operands, the shift entering
+// each S^T tile as its accumulator input, the softmax statistics, and O^T.
+template <int D, int MBW>
+struct EncodeState {
+  typedef typename KOperand<D>::T kop_t;
+  kop_t qh[MBW], ql[MBW];
+  f32x4 cb[MBW];
+  float mu[MBW], lam[MBW];
+  f32x4 acc[D / 16][MBW];
+  bool first;
+};
+
+// One 32-token step of one wave: S^T tiles, softmax weights, O^T += V^T P^T.
+// ONLINE: keep a running max (raised lazily); otherwise the shift is a bound.
+// MASK (ragged last step only): tokens at or past n1 get weight zero.
+template <int D, int MBW, bool ONLINE, bool MASK>
+__device__ __forceinline__ void encode_step(EncodeState<D, MBW>& st, const __bf16* sK, const __bf16* sV,
+                                            int ks, int sb, int n1, int g, int c16) {
   constexpr int KL = KOperand<D>::kLen;
-  constexpr int OCT = D / 8;     // 16-byte units per token row
+  constexpr int DB = D / 16;
   constexpr float TAU = 8.0f;
   typedef typename KOperand<D>::T kop_t;
+  const kop_t k0 = *reinterpret_cast<const kop_t*>(sK + slot_off<D>(ks * 32 + c16, KL * g));
+  const kop_t k1 = *reinterpret_cast<const kop_t*>(sK + slot_off<D>(ks * 32 + 16 + c16, KL * g));
+  f32x4 s0[MBW], s1[MBW];
+#pragma unroll
+  for (int i = 0; i < MBW; ++i) {
+    s0[i] = KOperand<D>::mma(k0, st.qh[i], st.cb[i]);
+    s1[i] = KOperand<D>::mma(k1, st.qh[i], st.cb[i]);
+    s0[i] = KOperand<D>::mma(k0, st.ql[i], s0[i]);
+    s1[i] = KOperand<D>::mma(k1, st.ql[i], s1[i]);
+  }
+  if (MASK) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool o0 = sb + 4 * g + r >= n1, o1 = sb + 16 + 4 * g + r >= n1;
+#pragma unroll
+      for (int i = 0; i < MBW; ++i) {
+        if (o0) s0[i][r] = -INFINITY;
+        if (o1) s1[i][r] = -INFINITY;
+      }
+    }
+  }
+  if (ONLINE) {
+    float lm[MBW];
+    bool hit = st.first;
+#pragma unroll
+    for (int i = 0; i < MBW; ++i) {
+      lm[i] = fmaxf(max3(s0[i][0], s0[i][1], s0[i][2]),
+                    max3(s0[i][3], s1[i][0], max3(s1[i][1], s1[i][2], s1[i][3])));
+      hit |= lm[i] > TAU;
+    }
+    if (__builtin_expect(__any(hit), 0)) {
+#pragma unroll
+      for (int i = 0; i < MBW; ++i) {
+        const float cm = max_over_rows(lm[i]);
+        const float d = st.first ? cm : fmaxf(cm, 0.0f);
+        st.mu[i] += d;
+        const float al = fast_exp2(-d);
+        st.lam[i] *= al;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) st.acc[db][i] *= al;
+        s0[i] -= d;
+        s1[i] -= d;
+        st.cb[i] = f32x4{-st.mu[i], -st.mu[i], -st.mu[i], -st.mu[i]};
+      }
+      st.first = false;
+    }
+  }
+  bf16x8 p[MBW];
+#pragma unroll
+  for (int i = 0; i < MBW; ++i) {
+    const bf16x2 p0 = pack_bf16(fast_exp2(s0[i][0]), fast_exp2(s0[i][1]));
+    const bf16x2 p1 = pack_bf16(fast_exp2(s0[i][2]), fast_exp2(s0[i][3]));
+    const bf16x2 p2 = pack_bf16(fast_exp2(s1[i][0]), fast_exp2(s1[i][1]));
+    const bf16x2 p3 = pack_bf16(fast_exp2(s1[i][2]), fast_exp2(s1[i][3]));
+    st.lam[i] = add_pair(p3, add_pair(p2, add_pair(p1, add_pair(p0, st.lam[i]))));
+    p[i] = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  }
+  // V^T operand: lane (row d = 16 db + c16, k-row g) needs V[tok][d] for the
+  // eight tokens of its k-slots; one transposing read gives a lane four
+  // tokens of its column when the 16 lanes of row g supply the 4-token x
+  // 16-column block (lane r: token base + r/4, columns 16 db + 4 (r%4) ..+3).
+  const int vt = ks * 32 + 4 * g + (c16 >> 2);
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const int ve = 16 * db + 4 * (c16 & 3);
+    const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(sV + slot_off<D>(vt, ve)));
+    const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(sV + slot_off<D>(vt + 16, ve)));
+    const bf16x8 vop = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+#pragma unroll
+    for (int i = 0; i < MBW; ++i) st.acc[db][i] = mfma_k32(vop, p[i], st.acc[db][i]);
+  }
+}
 
-  __shared__ __attribute__((aligned(16))) __bf16 sK[2][TN * D];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[2][D * VROW];
+// Largest squared key norm among the tile's tokens seen by this thread
+// (every thread reads two 16-byte chunks; the chunks of one row sit in
+// adjacent lanes).
+template <int D>
+__device__ __forceinline__ float tile_knorm(const __bf16* sK, int tid) {
+  constexpr int U = D / 8;
+  float best = 0.0f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(sK + (tid + 256 * h) * 8);
+    float ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bf16x2 pr = {x[2 * e], x[2 * e + 1]};
+      ss = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss, false);
+    }
+    ss += __shfl_xor(ss, 1);
+    if (U == 4) ss += __shfl_xor(ss, 2);
+    best = fmaxf(best, ss);
+  }
+  return best;
+}
+
+// One tile of the ring (slot I holds tile t): wait for this wave's loads of
+// tile t, barrier (every wave's part has landed, and every wave has finished
+// tile t-1, whose slot is refilled next), issue tile t+3 into that slot, then
+// consume tile t: whole 32-token steps, and a masked step if the split ends
+// inside the tile.
+template <int D, int MBW, bool KNORM, bool ONLINE, int I>
+__device__ __forceinline__ void encode_tile(EncodeState<D, MBW>& st, const __bf16* Kp, const __bf16* Vp, int t,
+                                            int n0, int n1, int tid, int wave, int lane, bool wave_active,
+                                            int g, int c16, float& kn2) {
+  constexpr int TN = kTileElems / D;
+  FLAREPP_WAIT_VM(2 * kDmaPerTile);
+  __builtin_amdgcn_s_barrier();
+  tile_dma<D, (I + 3) & 3>(Kp, Vp, n0 + (t + 3) * TN, n1, wave, lane);
+  if (KNORM) kn2 = fmaxf(kn2, tile_knorm<D>(ring_k<I>(), tid));
+  if (!wave_active) return;
+  const int tb = n0 + t * TN;
+  const int full = min(TN / 32, (n1 - tb) / 32);
+#pragma unroll 1
+  for (int ks = 0; ks < full; ++ks)
+    encode_step<D, MBW, ONLINE, false>(st, ring_k<I>(), ring_v<I>(), ks, tb + ks * 32, n1, g, c16);
+  if (full < TN / 32 && tb + full * 32 < n1)
+    encode_step<D, MBW, ONLINE, true>(st, ring_k<I>(), ring_v<I>(), full, tb + full * 32, n1, g, c16);
+}
+
+template <int D, int MBW, bool KNORM, bool ONLINE>
+__device__ __forceinline__ void encode_tiles(EncodeState<D, MBW>& st, const __bf16* Kp, const __bf16* Vp, int n0,
+                                             int n1, int tid, int wave, int lane, bool wave_active, int g, int c16,
+                                             float& kn2) {
+  constexpr int TN = kTileElems / D;
+  const int ntiles = (n1 - n0 + TN - 1) / TN;
+  tile_dma<D, 0>(Kp, Vp, n0, n1, wave, lane);
+  tile_dma<D, 1>(Kp, Vp, n0 + TN, n1, wave, lane);
+  tile_dma<D, 2>(Kp, Vp, n0 + 2 * TN, n1, wave, lane);
+  for (int t = 0; t < ntiles; t += 4) {
+    encode_tile<D, MBW, KNORM, ONLINE, 0>(st, Kp, Vp, t, n0, n1, tid, wave, lane, wave_active, g, c16, kn2);
+    if (t + 1 >= ntiles) break;
+    encode_tile<D, MBW, KNORM, ONLINE, 1>(st, Kp, Vp, t + 1, n0, n1, tid, wave, lane, wave_active, g, c16, kn2);
+    if (t + 2 >= ntiles) break;
+    encode_tile<D, MBW, KNORM, ONLINE, 2>(st, Kp, Vp, t + 2, n0, n1, tid, wave, lane, wave_active, g, c16, kn2);
+    if (t + 3 >= ntiles) break;
+    encode_tile<D, MBW, KNORM, ONLINE, 3>(st, Kp, Vp, t + 3, n0, n1, tid, wave, lane, wave_active, g, c16, kn2);
+  }
+  // the ring's trailing loads must land before the workgroup's LDS is released
+  FLAREPP_WAIT_VM(0);
+}
+
+// BOUNDED: the shift may come from a.bias (the bound path, with the online
+// path as fallback when a bound is unsafe); otherwise always online.
+template <int D, int MBW, bool KNORM, bool BOUNDED>
+__global__ __launch_bounds__(256, 2) void encode_split_bf16(EncodeArgs a) {
+  constexpr int DB = D / 16;     // 16-row blocks of O^T
+  constexpr int KL = KOperand<D>::kLen;
+  typedef typename KOperand<D>::T kop_t;
   __shared__ float sRed[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -95,185 +320,45 @@ __global__ __launch_bounds__(256, 2) void encode_split_bf16(EncodeArgs a) {
   const __bf16* Kp = a.K + bh * (int64_t)a.N * D;
   const __bf16* Vp = a.V + bh * (int64_t)a.N * D;
 
-  // ---- query operands (B of S^T = K Q^T: lane holds column m, k = d) and bias
-  kop_t qh[MBW], ql[MBW];
-  f32x4 cb[MBW];
-  float mu[MBW];
-  bool online = true;
+  // ---- query operands (B of S^T = K Q^T: lane holds column m, k = d) and shift
+  EncodeState<D, MBW> st;
+  bool need_online = !BOUNDED || a.bias == nullptr;
   {
     const int64_t qo = (int64_t)b * a.q_sb + (int64_t)h * a.q_sh - a.q_off;
-    const __bf16* qhp = a.q_hi + qo;
-    const __bf16* qlp = a.q_lo + qo;
-    bool need_online = a.bias == nullptr;
 #pragma unroll
     for (int i = 0; i < MBW; ++i) {
       const int mblk = mb0 + i;
       if (mblk < nMB) {
         const int m = mblk * 16 + c16;
-        qh[i] = *reinterpret_cast<const kop_t*>(qhp + (int64_t)m * D + KL * g);
-        ql[i] = *reinterpret_cast<const kop_t*>(qlp + (int64_t)m * D + KL * g);
-        mu[i] = a.bias ? a.bias[lbh * a.Mp + m] : 0.0f;
+        st.qh[i] = *reinterpret_cast<const kop_t*>(a.q_hi + qo + (int64_t)m * D + KL * g);
+        st.ql[i] = *reinterpret_cast<const kop_t*>(a.q_lo + qo + (int64_t)m * D + KL * g);
+        st.mu[i] = (BOUNDED && a.bias) ? a.bias[lbh * a.Mp + m] : 0.0f;
       } else {
-        qh[i] = kop_t{};
-        ql[i] = kop_t{};
-        mu[i] = 0.0f;
+        st.qh[i] = kop_t{};
+        st.ql[i] = kop_t{};
+        st.mu[i] = 0.0f;
       }
-      need_online |= !(mu[i] <= 1e30f);
-    }
-    online = __any(need_online);
+      need_online |= !(st.mu[i] <= 1e30f);
+      st.lam[i] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < MBW; ++i) {
-      if (online) mu[i] = 0.0f;
-      cb[i] = f32x4{-mu[i], -mu[i], -mu[i], -mu[i]};
+      for (int db = 0; db < DB; ++db) st.acc[db][i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
-  bool first = online;
-
-  f32x4 acc[DB][MBW];
-  float lam[MBW];
+  const bool online = __any(need_online);
 #pragma unroll
   for (int i = 0; i < MBW; ++i) {
-    lam[i] = 0.0f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) acc[db][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (online) st.mu[i] = 0.0f;
+    st.cb[i] = f32x4{-st.mu[i], -st.mu[i], -st.mu[i], -st.mu[i]};
   }
+  st.first = online;
   float kn2 = 0.0f;
+  // the operand loads above must not be counted with the ring's loads
+  FLAREPP_WAIT_VM(0);
 
-  // ---- staging of K/V tiles: K linear ([TN][D]), V transposed ([D][VROW])
-  const int ntiles = (n1 - n0 + TN - 1) / TN;
-  uint4 rk[2], rv[2];
-  auto gload = [&](int t) {
-    const int tb = n0 + t * TN;
-#pragma unroll
-    for (int u2 = 0; u2 < 2; ++u2) {
-      const int u = tid + u2 * 256;
-      const int tok = u / OCT, oc = u % OCT;
-      rk[u2] = (tb + tok < n1)
-                   ? *reinterpret_cast<const uint4*>(Kp + (int64_t)(tb + tok) * D + 8 * oc)
-                   : make_uint4(0, 0, 0, 0);
-    }
-    const int p = tid / OCT, q = tid % OCT;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int tok = 2 * p + e;
-      rv[e] = (tb + tok < n1)
-                  ? *reinterpret_cast<const uint4*>(Vp + (int64_t)(tb + tok) * D + 8 * q)
-                  : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto swrite = [&](int buf) {
-#pragma unroll
-    for (int u2 = 0; u2 < 2; ++u2) {
-      const int u = tid + u2 * 256;
-      *reinterpret_cast<uint4*>(&sK[buf][u * 8]) = rk[u2];
-      if (KNORM) {
-        const bf16x8 x = __builtin_bit_cast(bf16x8, rk[u2]);
-        float ss = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bf16x2 pr = {x[2 * e], x[2 * e + 1]};
-          ss = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss, false);
-        }
-        ss += __shfl_xor(ss, 1);
-        if (OCT == 4) ss += __shfl_xor(ss, 2);
-        kn2 = fmaxf(kn2, ss);
-      }
-    }
-    const int p = tid / OCT, q = tid % OCT;
-    const uint32_t w0[4] = {rv[0].x, rv[0].y, rv[0].z, rv[0].w};
-    const uint32_t w1[4] = {rv[1].x, rv[1].y, rv[1].z, rv[1].w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t lo = w0[e >> 1], hi = w1[e >> 1];
-      const uint32_t pair = (e & 1) ? ((hi & 0xFFFF0000u) | (lo >> 16)) : ((hi << 16) | (lo & 0xFFFFu));
-      *reinterpret_cast<uint32_t*>(&sV[buf][(8 * q + e) * VROW + 2 * p]) = pair;
-    }
-  };
-
-  gload(0);
-  swrite(0);
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) gload(t + 1);
-    const int tb = n0 + t * TN;
-    if (wave_active) {
-#pragma unroll 1
-      for (int ks = 0; ks < TN / 32; ++ks) {
-        const int sb = tb + ks * 32;
-        if (sb >= n1) break;
-        const kop_t k0 = *reinterpret_cast<const kop_t*>(&sK[buf][(ks * 32 + c16) * D + KL * g]);
-        const kop_t k1 = *reinterpret_cast<const kop_t*>(&sK[buf][(ks * 32 + 16 + c16) * D + KL * g]);
-        f32x4 s0[MBW], s1[MBW];
-#pragma unroll
-        for (int i = 0; i < MBW; ++i) {
-          s0[i] = KOperand<D>::mma(k0, qh[i], cb[i]);
-          s1[i] = KOperand<D>::mma(k1, qh[i], cb[i]);
-          s0[i] = KOperand<D>::mma(k0, ql[i], s0[i]);
-          s1[i] = KOperand<D>::mma(k1, ql[i], s1[i]);
-        }
-        if (sb + 32 > n1) {  // ragged tail: tokens past the split get no weight
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const bool o0 = sb + 4 * g + r >= n1, o1 = sb + 16 + 4 * g + r >= n1;
-#pragma unroll
-            for (int i = 0; i < MBW; ++i) {
-              if (o0) s0[i][r] = -INFINITY;
-              if (o1) s1[i][r] = -INFINITY;
-            }
-          }
-        }
-        if (online) {
-          float lm[MBW];
-          bool hit = first;
-#pragma unroll
-          for (int i = 0; i < MBW; ++i) {
-            lm[i] = fmaxf(max3(s0[i][0], s0[i][1], s0[i][2]),
-                          max3(s0[i][3], s1[i][0], max3(s1[i][1], s1[i][2], s1[i][3])));
-            hit |= lm[i] > TAU;
-          }
-          if (__any(hit)) {
-#pragma unroll
-            for (int i = 0; i < MBW; ++i) {
-              const float cm = max_over_rows(lm[i]);
-              const float d = first ? cm : fmaxf(cm, 0.0f);
-              mu[i] += d;
-              const float al = fast_exp2(-d);
-              lam[i] *= al;
-#pragma unroll
-              for (int db = 0; db < DB; ++db) acc[db][i] *= al;
-              s0[i] -= d;
-              s1[i] -= d;
-              cb[i] = f32x4{-mu[i], -mu[i], -mu[i], -mu[i]};
-            }
-            first = false;
-          }
-        }
-        bf16x8 p[MBW];
-#pragma unroll
-        for (int i = 0; i < MBW; ++i) {
-          const bf16x2 p0 = pack_bf16(fast_exp2(s0[i][0]), fast_exp2(s0[i][1]));
-          const bf16x2 p1 = pack_bf16(fast_exp2(s0[i][2]), fast_exp2(s0[i][3]));
-          const bf16x2 p2 = pack_bf16(fast_exp2(s1[i][0]), fast_exp2(s1[i][1]));
-          const bf16x2 p3 = pack_bf16(fast_exp2(s1[i][2]), fast_exp2(s1[i][3]));
-          lam[i] = add_pair(p3, add_pair(p2, add_pair(p1, add_pair(p0, lam[i]))));
-          p[i] = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-        }
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const __bf16* vrow = &sV[buf][(16 * db + c16) * VROW + ks * 32 + 4 * g];
-          const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(vrow);
-          const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(vrow + 16);
-          const bf16x8 vop = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-#pragma unroll
-          for (int i = 0; i < MBW; ++i) acc[db][i] = mfma_k32(vop, p[i], acc[db][i]);
-        }
-      }
-    }
-    if (t + 1 < ntiles) swrite((t + 1) & 1);
-    __syncthreads();
-  }
+  if (!BOUNDED || online)
+    encode_tiles<D, MBW, KNORM, true>(st, Kp, Vp, n0, n1, tid, wave, lane, wave_active, g, c16, kn2);
+  else
+    encode_tiles<D, MBW, KNORM, false>(st, Kp, Vp, n0, n1, tid, wave, lane, wave_active, g, c16, kn2);
 
   // ---- partial records
   if (wave_active) {
@@ -283,13 +368,13 @@ __global__ __launch_bounds__(256, 2) void encode_split_bf16(EncodeArgs a) {
       const int mblk = mb0 + i;
       if (mblk >= nMB) break;
       const int m = mblk * 16 + c16;
-      const float lt = sum_over_rows(lam[i]);
-      float* rec = a.part + ((lbh * a.J + j) * (int64_t)a.Mp + m) * PS;
+      const float lt = sum_over_rows(st.lam[i]);
+      float* rec = a.part + ((lbh * a.Mp + m) * (int64_t)a.J + j) * PS;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(rec + 16 * db + 4 * g) = acc[db][i];
+      for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(rec + 16 * db + 4 * g) = st.acc[db][i];
       if (g == 0) {
         rec[D] = lt;
-        rec[D + 1] = mu[i];
+        rec[D + 1] = st.mu[i];
       }
     }
   }

@@ -15,7 +15,7 @@ struct EncodeF32Args {
   int64_t q_sb, q_sh, q_off;  // element offset of (b, h)'s rows: b*q_sb + h*q_sh - q_off
   const float* K;
   const float* V;
-  float* part;         // [G][J][Mp][D + 4]
+  float* part;         // [G][Mp][J][D + 4]
   int H, N, M, Mp, J, chunk;
   int64_t bh0;
   float c;             // scale * log2(e)
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void encode_split_f32(EncodeF32Args a) {
     }
   }
   if (m < a.Mp) {
-    float* rec = a.part + ((lbh * a.J + j) * (int64_t)a.Mp + m) * Part<D>::kStride;
+    float* rec = a.part + ((lbh * a.Mp + m) * (int64_t)a.J + j) * Part<D>::kStride;
 #pragma unroll
     for (int d = 0; d < D; ++d) rec[d] = real ? acc[d] : 0.0f;
     rec[D] = real ? lam : 1.0f;

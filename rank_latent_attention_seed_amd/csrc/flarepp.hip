@@ -187,6 +187,26 @@ flarepp_status launched() {
   return hipGetLastError() == hipSuccess ? FLAREPP_OK : FLAREPP_HIP_ERROR;
 }
 
+// Optional per-launch event recording (flarepp_route_profiled); inert when
+// `events` is null.
+struct Recorder {
+  void** events = nullptr;
+  int32_t* kinds = nullptr;
+  int32_t max = 0;
+  int32_t n = 0;
+  bool failed = false;
+  void before(int kind, hipStream_t st) {
+    if (events && n < max) {
+      kinds[n] = kind;
+      failed |= hipEventRecord(static_cast<hipEvent_t>(events[2 * n]), st) != hipSuccess;
+    }
+  }
+  void after(hipStream_t st) {
+    if (events && n < max) failed |= hipEventRecord(static_cast<hipEvent_t>(events[2 * n + 1]), st) != hipSuccess;
+    ++n;
+  }
+};
+
 #define FLAREPP_TRY(x)                          \
   do {                                          \
     const flarepp_status st_ = (x);             \
@@ -197,36 +217,46 @@ flarepp_status launched() {
 
 template <int D>
 flarepp_status run_prep(const Plan& p, const void* src, bool src_bf16, int64_t src_off, int64_t src_blk,
-                        int nblk, __bf16* hi, __bf16* lo, __bf16* zt, float* qn, float c, hipStream_t st) {
+                        int nblk, __bf16* hi, __bf16* lo, __bf16* zt, float* qn, float c, hipStream_t st,
+                        Recorder& rec) {
   PrepArgs a{src, src_bf16 ? 1 : 0, src_off, src_blk, nblk, p.M, p.Mp, hi, lo, zt, qn, c};
   const int64_t n = (int64_t)nblk * p.Mp;
+  rec.before(FLAREPP_KERNEL_PREP, st);
   prep_rows<D><<<dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st>>>(a);
+  rec.after(st);
   return launched();
 }
 
-template <int D, bool KNORM>
-flarepp_status run_encode_bf16(const Plan& p, const EncodeArgs& a, int Gc, hipStream_t st) {
+template <int D, bool KNORM, bool BOUNDED>
+flarepp_status run_encode_bf16(const Plan& p, const EncodeArgs& a, int Gc, hipStream_t st, Recorder& rec,
+                               int kind) {
   const dim3 grid((unsigned)p.J, (unsigned)Gc, (unsigned)cdiv(p.Mp / 16, 4 * p.mbw));
+  rec.before(kind, st);
   switch (p.mbw) {
-    case 1: encode_split_bf16<D, 1, KNORM><<<grid, dim3(256), 0, st>>>(a); break;
-    case 2: encode_split_bf16<D, 2, KNORM><<<grid, dim3(256), 0, st>>>(a); break;
-    case 3: encode_split_bf16<D, 3, KNORM><<<grid, dim3(256), 0, st>>>(a); break;
-    default: encode_split_bf16<D, 4, KNORM><<<grid, dim3(256), 0, st>>>(a); break;
+    case 1: encode_split_bf16<D, 1, KNORM, BOUNDED><<<grid, dim3(256), 0, st>>>(a); break;
+    case 2: encode_split_bf16<D, 2, KNORM, BOUNDED><<<grid, dim3(256), 0, st>>>(a); break;
+    case 3: encode_split_bf16<D, 3, KNORM, BOUNDED><<<grid, dim3(256), 0, st>>>(a); break;
+    default: encode_split_bf16<D, 4, KNORM, BOUNDED><<<grid, dim3(256), 0, st>>>(a); break;
   }
+  rec.after(st);
   return launched();
 }
 
 template <int D>
-flarepp_status run_encode_f32(const Plan& p, const EncodeF32Args& a, int Gc, hipStream_t st) {
+flarepp_status run_encode_f32(const Plan& p, const EncodeF32Args& a, int Gc, hipStream_t st, Recorder& rec,
+                              int kind) {
   const dim3 grid((unsigned)p.J, (unsigned)Gc, (unsigned)cdiv(p.M, 256));
+  rec.before(kind, st);
   encode_split_f32<D><<<grid, dim3(256), 0, st>>>(a);
+  rec.after(st);
   return launched();
 }
 
 template <int D>
-flarepp_status run_merge(const Plan& p, const MergeArgs& a, int Gc, hipStream_t st) {
+flarepp_status run_merge(const Plan& p, const MergeArgs& a, int Gc, hipStream_t st, Recorder& rec) {
   const int rpb = 256 / p.tpr;
   const dim3 grid((unsigned)cdiv(p.Mp, rpb), (unsigned)Gc);
+  rec.before(FLAREPP_KERNEL_MERGE, st);
   switch (p.tpr) {
     case 1: merge_partials<D, 1><<<grid, dim3(256), 0, st>>>(a); break;
     case 2: merge_partials<D, 2><<<grid, dim3(256), 0, st>>>(a); break;
@@ -236,6 +266,7 @@ flarepp_status run_merge(const Plan& p, const MergeArgs& a, int Gc, hipStream_t 
     case 32: merge_partials<D, 32><<<grid, dim3(256), 0, st>>>(a); break;
     default: merge_partials<D, 64><<<grid, dim3(256), 0, st>>>(a); break;
   }
+  rec.after(st);
   return launched();
 }
 
@@ -245,8 +276,9 @@ void launch_decode_mb(const DecodeArgs& a, dim3 grid, hipStream_t st) {
 }
 
 template <int D>
-flarepp_status run_decode_bf16(const Plan& p, const DecodeArgs& a, int Gc, hipStream_t st) {
+flarepp_status run_decode_bf16(const Plan& p, const DecodeArgs& a, int Gc, hipStream_t st, Recorder& rec) {
   const dim3 grid((unsigned)cdiv(p.N, p.dchunk), (unsigned)Gc);
+  rec.before(FLAREPP_KERNEL_DECODE, st);
   switch (p.Mp / 16) {
     case 1: launch_decode_mb<D, 1>(a, grid, st); break;
     case 2: launch_decode_mb<D, 2>(a, grid, st); break;
@@ -265,13 +297,16 @@ flarepp_status run_decode_bf16(const Plan& p, const DecodeArgs& a, int Gc, hipSt
     case 15: launch_decode_mb<D, 15>(a, grid, st); break;
     default: launch_decode_mb<D, 16>(a, grid, st); break;
   }
+  rec.after(st);
   return launched();
 }
 
 template <int D>
-flarepp_status run_decode_f32(const Plan& p, const DecodeF32Args& a, int Gc, hipStream_t st) {
+flarepp_status run_decode_f32(const Plan& p, const DecodeF32Args& a, int Gc, hipStream_t st, Recorder& rec) {
   const dim3 grid((unsigned)cdiv(p.N, 256), (unsigned)Gc);
+  rec.before(FLAREPP_KERNEL_DECODE, st);
   decode_f32<D><<<grid, dim3(256), (size_t)2 * p.M * D * sizeof(float), st>>>(a);
+  rec.after(st);
   return launched();
 }
 
@@ -307,14 +342,14 @@ enum Stage { kSeed, kEncode, kDecode, kRoute, kFlare };
 template <int D>
 flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in, const float* Z_in,
                    const void* K, const void* V, float* Y, float* Qd_out, float* Z_out, void* ws,
-                   hipStream_t st) {
+                   hipStream_t st, Recorder& rec) {
   const int64_t MD = (int64_t)p.M * D, MpD = (int64_t)p.Mp * D;
   const int64_t seed_h = p.nS > 1 ? MD : 0;
   if (p.bf16) {
     __bf16* shi = at<__bf16>(ws, p.o_shi);
     __bf16* slo = at<__bf16>(ws, p.o_slo);
     if (stage == kSeed || stage == kRoute || stage == kFlare)
-      FLAREPP_TRY(run_prep<D>(p, S, true, 0, seed_h, p.nS, shi, slo, nullptr, at<float>(ws, p.o_sqn), p.c, st));
+      FLAREPP_TRY(run_prep<D>(p, S, true, 0, seed_h, p.nS, shi, slo, nullptr, at<float>(ws, p.o_sqn), p.c, st, rec));
     for (int64_t g0 = 0; g0 < p.BH; g0 += p.G) {
       const int Gc = (int)std::min<int64_t>(p.G, p.BH - g0);
       __bf16* qhi = at<__bf16>(ws, p.o_qhi);
@@ -330,9 +365,9 @@ flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in
         e.q_off = 0;
         e.knorm = at<float>(ws, p.o_knorm);
         if (stage == kRoute)
-          FLAREPP_TRY((run_encode_bf16<D, true>(p, e, Gc, st)));
+          FLAREPP_TRY((run_encode_bf16<D, true, false>(p, e, Gc, st, rec, FLAREPP_KERNEL_SEED_ENCODE)));
         else
-          FLAREPP_TRY((run_encode_bf16<D, false>(p, e, Gc, st)));
+          FLAREPP_TRY((run_encode_bf16<D, false, false>(p, e, Gc, st, rec, FLAREPP_KERNEL_SEED_ENCODE)));
         MergeArgs m = merge_args(p, ws, g0);
         if (stage == kFlare) {
           m.out = Z_out;
@@ -348,10 +383,10 @@ flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in
             m.bias = at<float>(ws, p.o_bias);
           }
         }
-        FLAREPP_TRY(run_merge<D>(p, m, Gc, st));
+        FLAREPP_TRY(run_merge<D>(p, m, Gc, st, rec));
       }
       if (stage == kEncode)
-        FLAREPP_TRY(run_prep<D>(p, Qd_in, false, g0 * MD, MD, Gc, qhi, qlo, nullptr, nullptr, p.c, st));
+        FLAREPP_TRY(run_prep<D>(p, Qd_in, false, g0 * MD, MD, Gc, qhi, qlo, nullptr, nullptr, p.c, st, rec));
       if (stage == kEncode || stage == kRoute) {
         EncodeArgs e = encode_args(p, ws, K, V, g0);
         e.q_hi = qhi;
@@ -360,15 +395,15 @@ flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in
         e.q_sh = MpD;
         e.q_off = g0 * MpD;
         e.bias = stage == kRoute ? at<float>(ws, p.o_bias) : nullptr;
-        FLAREPP_TRY((run_encode_bf16<D, false>(p, e, Gc, st)));
+        FLAREPP_TRY((run_encode_bf16<D, false, false>(p, e, Gc, st, rec, FLAREPP_KERNEL_ENCODE)));
         MergeArgs m = merge_args(p, ws, g0);
         m.out = Z_out;
         if (stage == kRoute) m.op_zt = zt;
-        FLAREPP_TRY(run_merge<D>(p, m, Gc, st));
+        FLAREPP_TRY(run_merge<D>(p, m, Gc, st, rec));
       }
       if (stage == kDecode) {
-        FLAREPP_TRY(run_prep<D>(p, Qd_in, false, g0 * MD, MD, Gc, qhi, qlo, nullptr, qnorm, p.c, st));
-        FLAREPP_TRY(run_prep<D>(p, Z_in, false, g0 * MD, MD, Gc, nullptr, nullptr, zt, nullptr, p.c, st));
+        FLAREPP_TRY(run_prep<D>(p, Qd_in, false, g0 * MD, MD, Gc, qhi, qlo, nullptr, qnorm, p.c, st, rec));
+        FLAREPP_TRY(run_prep<D>(p, Z_in, false, g0 * MD, MD, Gc, nullptr, nullptr, zt, nullptr, p.c, st, rec));
       }
       if (stage == kDecode || stage == kRoute || stage == kFlare) {
         DecodeArgs dargs{};
@@ -397,7 +432,7 @@ flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in
         dargs.chunk = p.dchunk;
         dargs.bh0 = g0;
         dargs.c = p.c;
-        FLAREPP_TRY(run_decode_bf16<D>(p, dargs, Gc, st));
+        FLAREPP_TRY(run_decode_bf16<D>(p, dargs, Gc, st, rec));
       }
     }
     return FLAREPP_OK;
@@ -408,7 +443,7 @@ flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in
   float* zf = at<float>(ws, p.o_zf);
   for (int64_t g0 = 0; g0 < p.BH; g0 += p.G) {
     const int Gc = (int)std::min<int64_t>(p.G, p.BH - g0);
-    auto encode = [&](const float* q, int64_t sb, int64_t sh, int64_t off, float* out, float* outl) {
+    auto encode = [&](const float* q, int64_t sb, int64_t sh, int64_t off, float* out, float* outl, int kind) {
       EncodeF32Args e{};
       e.q = q;
       e.q_sb = sb;
@@ -425,37 +460,37 @@ flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in
       e.chunk = p.chunk;
       e.bh0 = g0;
       e.c = p.c;
-      FLAREPP_TRY(run_encode_f32<D>(p, e, Gc, st));
+      FLAREPP_TRY(run_encode_f32<D>(p, e, Gc, st, rec, kind));
       MergeArgs m = merge_args(p, ws, g0);
       m.out = out;
       m.outl = outl;
-      return run_merge<D>(p, m, Gc, st);
+      return run_merge<D>(p, m, Gc, st, rec);
     };
     auto decode = [&](const float* q, int64_t qsb, int64_t qsh, int64_t qoff, const float* z, int64_t zsb,
                       int64_t zsh, int64_t zoff) {
       DecodeF32Args d{q, qsb, qsh, qoff, z, zsb, zsh, zoff, static_cast<const float*>(K), Y,
                       p.H, p.N, p.M, g0, p.c};
-      return run_decode_f32<D>(p, d, Gc, st);
+      return run_decode_f32<D>(p, d, Gc, st, rec);
     };
     const float* Sf = static_cast<const float*>(S);
     const int64_t HMD = (int64_t)p.H * MD;
     switch (stage) {
       case kSeed:
-        FLAREPP_TRY(encode(Sf, 0, seed_h, 0, Qd_out, nullptr));
+        FLAREPP_TRY(encode(Sf, 0, seed_h, 0, Qd_out, nullptr, FLAREPP_KERNEL_SEED_ENCODE));
         break;
       case kEncode:
-        FLAREPP_TRY(encode(Qd_in, HMD, MD, 0, Z_out, nullptr));
+        FLAREPP_TRY(encode(Qd_in, HMD, MD, 0, Z_out, nullptr, FLAREPP_KERNEL_ENCODE));
         break;
       case kDecode:
         FLAREPP_TRY(decode(Qd_in, HMD, MD, 0, Z_in, HMD, MD, 0));
         break;
       case kRoute:
-        FLAREPP_TRY(encode(Sf, 0, seed_h, 0, Qd_out, qf));
-        FLAREPP_TRY(encode(qf, HMD, MD, g0 * MD, Z_out, zf));
+        FLAREPP_TRY(encode(Sf, 0, seed_h, 0, Qd_out, qf, FLAREPP_KERNEL_SEED_ENCODE));
+        FLAREPP_TRY(encode(qf, HMD, MD, g0 * MD, Z_out, zf, FLAREPP_KERNEL_ENCODE));
         FLAREPP_TRY(decode(qf, HMD, MD, g0 * MD, zf, HMD, MD, g0 * MD));
         break;
       case kFlare:
-        FLAREPP_TRY(encode(Sf, 0, seed_h, 0, Z_out, zf));
+        FLAREPP_TRY(encode(Sf, 0, seed_h, 0, Z_out, zf, FLAREPP_KERNEL_ENCODE));
         FLAREPP_TRY(decode(Sf, 0, seed_h, 0, zf, HMD, MD, g0 * MD));
         break;
     }
@@ -465,10 +500,12 @@ flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in
 
 flarepp_status dispatch(const Plan& p, Stage stage, const void* S, const float* Qd_in, const float* Z_in,
                         const void* K, const void* V, float* Y, float* Qd_out, float* Z_out, void* ws,
-                        void* stream) {
+                        void* stream, Recorder* recorder = nullptr) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (p.D == 16) return run<16>(p, stage, S, Qd_in, Z_in, K, V, Y, Qd_out, Z_out, ws, st);
-  return run<32>(p, stage, S, Qd_in, Z_in, K, V, Y, Qd_out, Z_out, ws, st);
+  Recorder inert;
+  Recorder& rec = recorder ? *recorder : inert;
+  if (p.D == 16) return run<16>(p, stage, S, Qd_in, Z_in, K, V, Y, Qd_out, Z_out, ws, st, rec);
+  return run<32>(p, stage, S, Qd_in, Z_in, K, V, Y, Qd_out, Z_out, ws, st, rec);
 }
 
 // Shared argument checks of the compute calls: descriptor, pointers,
@@ -614,6 +651,30 @@ flarepp_status flarepp_flare(const flarepp_desc* desc, const void* Q, const void
   Plan p;
   FLAREPP_TRY(prologue(desc, FLAREPP_OP_FLARE, in, inb, 3, out, outb, req, 2, ws, ws_bytes, &p));
   return dispatch(p, kFlare, Q, nullptr, nullptr, K, V, Y, nullptr, Z_out, ws, stream);
+}
+
+flarepp_status flarepp_route_profiled(const flarepp_desc* desc, const void* S, const void* K, const void* V,
+                                      float* Y, float* Qd_out, float* Z_out, void* ws, size_t ws_bytes,
+                                      void* stream, void** events, int32_t* kinds, int32_t max_launches,
+                                      int32_t* n_launches) {
+  if (!events || !kinds || !n_launches || max_launches < 0) return FLAREPP_INVALID_ARG;
+  FLAREPP_TRY(check_desc(desc));
+  const Sizes z = sizes(desc);
+  const void* in[3] = {S, K, V};
+  const size_t inb[3] = {z.s, z.kv, z.kv};
+  const void* out[3] = {Y, Qd_out, Z_out};
+  const size_t outb[3] = {z.y, z.md, z.md};
+  const bool req[3] = {true, false, false};
+  Plan p;
+  FLAREPP_TRY(prologue(desc, FLAREPP_OP_ROUTE, in, inb, 3, out, outb, req, 3, ws, ws_bytes, &p));
+  Recorder rec;
+  rec.events = events;
+  rec.kinds = kinds;
+  rec.max = max_launches;
+  const flarepp_status st = dispatch(p, kRoute, S, nullptr, nullptr, K, V, Y, Qd_out, Z_out, ws, stream, &rec);
+  *n_launches = rec.n;
+  if (st == FLAREPP_OK && rec.failed) return FLAREPP_HIP_ERROR;
+  return st;
 }
 
 }  // extern "C"

@@ -21,7 +21,7 @@ namespace flarepp {
 // Buffers marked [G] are indexed by the launch-local head lbh = blockIdx.y;
 // the caller's output by the global (b, h) = bh0 + lbh.
 struct MergeArgs {
-  const float* part;   // [G][J][Mp][D + 4]
+  const float* part;   // [G][Mp][J][D + 4]
   int J, Mp, M;
   int64_t bh0;
   float* out;          // [BH][M][D] float32 (the caller's Qd or Z), or null
@@ -41,52 +41,70 @@ struct MergeArgs {
 // float32 / bf16 normal range floor 2^-126.
 constexpr float kBoundSpan = 100.0f;
 
-template <int D, int TPR>
+// Reductions over the T threads that share a latent row (T a power of two,
+// the group aligned within one wave).
+template <int T>
+__device__ __forceinline__ float group_sum(float x) {
+  if (T == 64) return wave_sum(x);
+#pragma unroll
+  for (int off = T / 2; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+template <int T>
+__device__ __forceinline__ float group_max(float x) {
+  if (T == 64) return wave_max(x);
+#pragma unroll
+  for (int off = T / 2; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+
+// One latent row per group of T threads (T = 64 for many splits: one row per
+// wave).  Thread q of a row folds splits q, q + T, ...: a first sweep over
+// the maxima only, then the weighted sums, each unrolled so that its loads are
+// in flight together; the row's records are contiguous, so a wave's loads
+// are coalesced.
+template <int D, int T>
 __global__ __launch_bounds__(256) void merge_partials(MergeArgs a) {
   constexpr int PS = Part<D>::kStride;
-  constexpr int RPB = 256 / TPR;
+  constexpr int RPB = 256 / T;
   const int tid = threadIdx.x;
-  const int r = tid / TPR, q = tid % TPR;
+  const int r = tid / T, q = tid % T;
   const int m = blockIdx.x * RPB + r;
   const int64_t lbh = blockIdx.y, bh = a.bh0 + lbh;
   const bool row_ok = m < a.Mp;
-  const int mm = row_ok ? m : a.Mp - 1;
-  const float* base = a.part + (lbh * a.J * (int64_t)a.Mp + mm) * PS;
-  const int64_t jstride = (int64_t)a.Mp * PS;
+  const float* base = a.part + ((lbh * a.Mp + (row_ok ? m : 0)) * (int64_t)a.J) * PS;
 
   float mx = -INFINITY;
-  for (int jj = q; jj < a.J; jj += TPR) mx = fmaxf(mx, base[jj * jstride + D + 1]);
-#pragma unroll
-  for (int off = TPR / 2; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+#pragma unroll 8
+  for (int jj = q; jj < a.J; jj += T) mx = fmaxf(mx, base[(int64_t)jj * PS + D + 1]);
+  mx = group_max<T>(mx);
 
   float den = 0.0f;
-  float num[D];
+  f32x4 num[D / 4];
 #pragma unroll
-  for (int d = 0; d < D; ++d) num[d] = 0.0f;
-  for (int jj = q; jj < a.J; jj += TPR) {
-    const float* rec = base + jj * jstride;
-    const float w = fast_exp2(rec[D + 1] - mx);
-    den += w * rec[D];
+  for (int d4 = 0; d4 < D / 4; ++d4) num[d4] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+  for (int jj = q; jj < a.J; jj += T) {
+    const float* rec = base + (int64_t)jj * PS;
+    const f32x4 tail = *reinterpret_cast<const f32x4*>(rec + D);
+    const float w = fast_exp2(tail[1] - mx);
+    den += w * tail[0];
 #pragma unroll
-    for (int d4 = 0; d4 < D / 4; ++d4) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(rec + 4 * d4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) num[4 * d4 + e] += w * v[e];
-    }
+    for (int d4 = 0; d4 < D / 4; ++d4) num[d4] += w * *reinterpret_cast<const f32x4*>(rec + 4 * d4);
   }
+  den = group_sum<T>(den);
+  float x[D];
 #pragma unroll
-  for (int off = TPR / 2; off >= 1; off >>= 1) {
-    den += __shfl_xor(den, off);
+  for (int d4 = 0; d4 < D / 4; ++d4)
 #pragma unroll
-    for (int d = 0; d < D; ++d) num[d] += __shfl_xor(num[d], off);
-  }
+    for (int e = 0; e < 4; ++e) x[4 * d4 + e] = group_sum<T>(num[d4][e]);
+
   const bool real = m < a.M;
   const float inv = 1.0f / den;
-  float x[D];
   float n2 = 0.0f;
 #pragma unroll
   for (int d = 0; d < D; ++d) {
-    x[d] = real ? num[d] * inv : 0.0f;
+    x[d] = real ? x[d] * inv : 0.0f;
     n2 += x[d] * x[d];
   }
   const float nrm = sqrtf(n2);
@@ -94,25 +112,30 @@ __global__ __launch_bounds__(256) void merge_partials(MergeArgs a) {
   float kmax2 = 0.0f;
   if (a.bias && a.knorm) {
     const float* kn = a.knorm + lbh * a.Jk;
-    for (int jj = q; jj < a.Jk; jj += TPR) kmax2 = fmaxf(kmax2, kn[jj]);
-#pragma unroll
-    for (int off = TPR / 2; off >= 1; off >>= 1) kmax2 = fmaxf(kmax2, __shfl_xor(kmax2, off));
+    for (int jj = q; jj < a.Jk; jj += T) kmax2 = fmaxf(kmax2, kn[jj]);
+    kmax2 = group_max<T>(kmax2);
   }
   if (!row_ok) return;
 
+  // every thread of the row holds the whole row: thread q writes elements q, q + T, ...
   const int64_t orow = (lbh * a.Mp + m) * D;
+  constexpr int PER = (D + T - 1) / T;
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    if (d % TPR != q) continue;
-    if (a.out && real) a.out[(bh * a.M + m) * D + d] = x[d];
-    if (a.outl && real) a.outl[(lbh * a.M + m) * D + d] = x[d];
+  for (int k = 0; k < PER; ++k) {
+    const int d = q + k * T;
+    if (d >= D) break;
+    float v = x[0];
+#pragma unroll
+    for (int e = 1; e < D; ++e) v = (d == e) ? x[e] : v;
+    if (a.out && real) a.out[(bh * a.M + m) * D + d] = v;
+    if (a.outl && real) a.outl[(lbh * a.M + m) * D + d] = v;
     if (a.op_hi) {
-      const float xs = x[d] * a.c;
+      const float xs = v * a.c;
       const __bf16 hi = (__bf16)xs;
       a.op_hi[orow + d] = hi;
       if (a.op_lo) a.op_lo[orow + d] = (__bf16)(xs - (float)hi);
     }
-    if (a.op_zt) a.op_zt[(lbh * D + d) * (int64_t)a.Mp + m] = (__bf16)x[d];
+    if (a.op_zt) a.op_zt[(lbh * D + d) * (int64_t)a.Mp + m] = (__bf16)v;
   }
   if (q == 0) {
     if (a.qnorm) a.qnorm[lbh * a.Mp + m] = nrm;

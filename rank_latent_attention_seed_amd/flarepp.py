@@ -24,7 +24,8 @@ STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE_TOO_SMALL",
 ABI_VERSION = 1
 SYMBOLS = ("flarepp_abi_version", "flarepp_status_string", "flarepp_workspace_size",
            "flarepp_seed_encode", "flarepp_encode", "flarepp_decode", "flarepp_route",
-           "flarepp_flare")
+           "flarepp_flare", "flarepp_route_profiled")
+KERNEL_KINDS = {0: "prep", 1: "seed_encode", 2: "encode", 3: "merge", 4: "decode"}
 
 
 class FlareppDesc(ctypes.Structure):
@@ -75,6 +76,10 @@ def _lib():
         lib.flarepp_route.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.flarepp_flare.restype = ctypes.c_int
         lib.flarepp_flare.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.flarepp_route_profiled.restype = ctypes.c_int
+        lib.flarepp_route_profiled.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                               ctypes.POINTER(vp), ctypes.POINTER(i32), i32,
+                                               ctypes.POINTER(i32)]
         if lib.flarepp_abi_version() != ABI_VERSION:
             raise RuntimeError("libflarepp ABI version mismatch")
         _LIB = lib
@@ -131,6 +136,15 @@ def flarepp_route(desc, S, K, V, Y, Qd_out, Z_out, ws, ws_bytes, stream) -> int:
 
 def flarepp_flare(desc, Q, K, V, Y, Z_out, ws, ws_bytes, stream) -> int:
     return _lib().flarepp_flare(ctypes.byref(desc), Q, K, V, Y, Z_out, ws, ws_bytes, stream)
+
+
+def flarepp_route_profiled(desc, S, K, V, Y, Qd_out, Z_out, ws, ws_bytes, stream, events, kinds,
+                           max_launches, n_launches) -> int:
+    """events: ctypes array of 2*max_launches hipEvent_t; kinds: ctypes int32 array;
+    n_launches: ctypes.c_int32 (by reference)."""
+    return _lib().flarepp_route_profiled(ctypes.byref(desc), S, K, V, Y, Qd_out, Z_out, ws, ws_bytes,
+                                         stream, events, kinds, max_launches,
+                                         ctypes.byref(n_launches))
 
 
 # ------------------------------------------------------ torch plumbing -----

@@ -94,10 +94,11 @@ def test_scales(fp, scale):
 
 
 def test_large_logits_take_the_online_path(fp):
-    # sigma 4 keys with s = 1: the norm bounds exceed the safe exponent span,
-    # so the encode and decode fall back to exact running maxima.  Values keep
-    # unit scale: the bf16 path's error is ~2^-9 times the spread of V.
-    p = inputs.random_problem(1, 1, 3000, 32, 16, dtype="bf16", scale=1.0, seed=3, sigma=4.0,
+    # sigma 4 keys with s = 1/2: the norm bounds exceed the safe exponent span,
+    # so the encodes fall back to exact running maxima.  Values keep unit
+    # scale: the bf16 path's error is ~2^-9 times the spread of V, amplified in
+    # the decode by s * ||K|| for errors in Qd.
+    p = inputs.random_problem(1, 1, 3000, 32, 16, dtype="bf16", scale=0.5, seed=3, sigma=4.0,
                               sigma_v=1.0)
     run_and_compare(fp, p, label="large logits")
 
