@@ -10,20 +10,22 @@
 // combines per-device latent outputs with their softmax statistics (French
 // technical summary, "Contributions Clés", multi-GPU context parallelism).
 //
-// Work decomposition.  A 256-thread workgroup owns one (b, h, split, latent
-// group); its four waves own MBW 16-latent blocks each and share tiles of TN
-// tokens of K and V.  Tiles travel HBM -> LDS by direct-to-LDS loads (no
-// staging registers) through a ring of four slots: while tile t is consumed,
-// the loads of tiles t+1 and t+2 are in flight and tile t+3's are issued.
-// The slots are distinct LDS variables and the tile loop is unrolled by four,
-// so each access names its slot statically and waiting for tile t's loads
-// (s_waitcnt vmcnt) leaves the younger tiles' loads running.  16-byte chunks
+// Work decomposition.  A workgroup of NW waves (4 or 8) owns one (b, h,
+// split, latent group); each wave owns MBW 16-latent blocks and all share
+// tiles of TN tokens of K and V.  Tiles travel HBM -> LDS by direct-to-LDS
+// loads (no staging registers) through a ring of four slots, with the loads
+// of the two tiles after the one being consumed in flight; the tile loop is
+// unrolled by four so every slot address is static, and waiting for one
+// tile's loads (s_waitcnt vmcnt) leaves the younger tile's loads running.
+// 16-byte chunks
 // of each token row are XOR-swizzled in LDS (the fetching lane picks the
 // chunk that belongs to its slot) so the matrix-core operand reads are free
 // of bank conflicts.  Per 32-token step a wave computes S^T = K Q^T tiles
 // (rows = tokens, cols = latents), turns them into softmax weights in
 // registers, and accumulates O^T += V^T P^T; V's operand comes from the
-// token-major tile through transposing LDS reads (ds_read_b64_tr_b16).
+// token-major tile through transposing LDS reads (ds_read_b64_tr_b16).  The
+// work of a step is software-pipelined over the wave's latent blocks so the
+// matrix core and the VALU overlap (see EncodePipe).
 //
 // Softmax arithmetic.  The query operand arrives pre-multiplied by
 // c = s * log2(e) as a bf16 hi/lo pair (two MFMAs per tile, ~16 mantissa
@@ -37,7 +39,8 @@
 //     every weight and sum finite), at which point acc and lambda are
 //     rescaled.  Both give the same softmax up to rounding (softmax is
 //     invariant to a common shift).
-// lambda_m sums the same bf16-rounded weights that enter the PV product.
+// lambda_m sums the same bf16-rounded weights that enter the PV product
+// (computed on the matrix core as a row of ones times P^T).
 #pragma once
 
 #include "common.h"
@@ -73,25 +76,26 @@ struct KOperand<16> {
   __device__ __forceinline__ static f32x4 mma(T a, T b, f32x4 c) { return mfma_k16(a, b, c); }
 };
 
-// ---- the LDS ring: four K slots and four V slots of one tile each
-// (TN * D = 4096 bf16 = 8 KB for D = 16 and D = 32).
-constexpr int kTileElems = 4096;
-__shared__ __attribute__((aligned(16))) __bf16 enc_k0[kTileElems];
-__shared__ __attribute__((aligned(16))) __bf16 enc_k1[kTileElems];
-__shared__ __attribute__((aligned(16))) __bf16 enc_k2[kTileElems];
-__shared__ __attribute__((aligned(16))) __bf16 enc_k3[kTileElems];
-__shared__ __attribute__((aligned(16))) __bf16 enc_v0[kTileElems];
-__shared__ __attribute__((aligned(16))) __bf16 enc_v1[kTileElems];
-__shared__ __attribute__((aligned(16))) __bf16 enc_v2[kTileElems];
-__shared__ __attribute__((aligned(16))) __bf16 enc_v3[kTileElems];
-template <int I>
-__device__ __forceinline__ __bf16* ring_k() {
-  return I == 0 ? enc_k0 : I == 1 ? enc_k1 : I == 2 ? enc_k2 : enc_k3;
-}
-template <int I>
-__device__ __forceinline__ __bf16* ring_v() {
-  return I == 0 ? enc_v0 : I == 1 ? enc_v1 : I == 2 ? enc_v2 : enc_v3;
-}
+// ---- tile geometry and the LDS ring.  A slot holds one tile of K or V
+// (TE bf16 = TN tokens x D); the ring has four K slots and four V slots in one
+// kernel-local LDS array.  Eight-wave workgroups (one per CU) use 16 KB
+// slots (128 KB ring); four-wave workgroups use 8 KB slots so two fit per CU.
+template <int D, int NW>
+struct Ring {
+  static constexpr int TE = NW == 8 ? 8192 : 4096;  // elements per slot
+  static constexpr int TN = TE / D;                 // tokens per tile
+  static constexpr int SPT = TN / 32;               // 32-token steps per tile
+  static constexpr int DI = TE / 8 / 64 / NW;       // 1 KB loads per wave, operand and tile
+  static constexpr int kDma = 2 * DI;               // loads per wave and tile
+  template <int I>
+  __device__ __forceinline__ static __bf16* k(__bf16* ring) {
+    return ring + I * TE;
+  }
+  template <int I>
+  __device__ __forceinline__ static __bf16* v(__bf16* ring) {
+    return ring + (4 + I) * TE;
+  }
+};
 
 // Swizzle of the 16-byte chunks of token row t (D/8 chunks per row): the
 // chunk holding elements 8u..8u+7 sits at position u ^ swz(t).
@@ -105,139 +109,213 @@ __device__ __forceinline__ int slot_off(int t, int e) {
   return t * D + ((((e >> 3) ^ chunk_swz<D>(t)) << 3) | (e & 7));
 }
 
-#define FLAREPP_LDS(p) ((__attribute__((address_space(3))) void*)(p))
-#define FLAREPP_GLB(p) ((__attribute__((address_space(1))) void*)(p))
 // s_waitcnt with vmcnt <= n (n < 64); lgkmcnt and expcnt are not waited on.
-#define FLAREPP_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | (((n) >> 4) << 14))
+// The empty asm statements keep the compiler from moving memory accesses
+// across the wait.
+#define FLAREPP_WAIT_VM(n)                                                                      \
+  do {                                                                                          \
+    asm volatile("" ::: "memory");                                                              \
+    __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | (((n) >> 4) << 14));    \
+    asm volatile("" ::: "memory");                                                              \
+  } while (0)
 
-// Issue the direct-to-LDS loads of one tile into slot I: each wave fetches
-// 2 KB of K and 2 KB of V (two 1 KB instructions each); lane l of an
-// instruction fills LDS chunk base + 16 l and therefore fetches the (token,
-// chunk) that the swizzle places there.  Tokens past the split re-read the
-// split's last row (they receive zero weight), so every tile issues the same
-// number of loads and the wait counts stay uniform.
-template <int D, int I>
-__device__ __forceinline__ void tile_dma(const __bf16* Kp, const __bf16* Vp, int tb, int n1, int wave, int lane) {
+// Workgroup barrier without the memory wait that __syncthreads() implies
+// (the ring's loads are waited for explicitly, per tile).
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One direct-to-LDS load: every lane fetches 16 bytes from its own global
+// address into LDS at lds_base + 16 * lane.  Written as an asm statement (it
+// has no register results) so that the compiler does not track the LDS
+// write: its own bookkeeping would make every later LDS read of any ring
+// slot wait for all loads in flight, which would serialise the ring.  The
+// ring's waits are explicit (FLAREPP_WAIT_VM before each tile's barrier).
+__device__ __forceinline__ void dma16(const __bf16* src, const __bf16* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
+}
+
+// Issue the direct-to-LDS loads of one tile into slot I: the NW waves split
+// the tile's 16-byte chunks of K and of V (instructions of 1 KB each); lane l
+// of an instruction fills LDS chunk base + 16 l and therefore fetches the
+// (token, chunk) that the swizzle places there.  Tokens past the split
+// re-read the split's last row (they receive zero weight), so every tile
+// issues the same number of loads and the wait counts stay uniform.
+template <int D, int NW, int I>
+__device__ __forceinline__ void tile_dma(__bf16* ring, const __bf16* Kp, const __bf16* Vp, int tb, int n1,
+                                         int wave, int lane) {
+  typedef Ring<D, NW> R;
   constexpr int U = D / 8;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int blk = wave * 2 + i;
+  for (int i = 0; i < R::DI; ++i) {
+    const int blk = wave * R::DI + i;
     const int s = blk * 64 + lane;
     const int t = s / U;
     const int u = (s % U) ^ chunk_swz<D>(t);
     const int64_t src = (int64_t)min(tb + t, n1 - 1) * D + 8 * u;
-    __builtin_amdgcn_global_load_lds(FLAREPP_GLB(Kp + src), FLAREPP_LDS(ring_k<I>() + blk * 512), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(FLAREPP_GLB(Vp + src), FLAREPP_LDS(ring_v<I>() + blk * 512), 16, 0, 0);
+    dma16(Kp + src, R::template k<I>(ring) + blk * 512);
+    dma16(Vp + src, R::template v<I>(ring) + blk * 512);
   }
 }
-constexpr int kDmaPerTile = 4;  // load instructions per wave per tile
 
 // Per-wave register state of the encode: query operands, the shift entering
 // each S^T tile as its accumulator input, the softmax statistics, and O^T.
+// acc[DB] is the sum lambda: its tile is ONES^T P^T, whose row 0 carries the
+// column sums of the bf16 weights (so lambda sums exactly the weights that
+// enter O^T).
 template <int D, int MBW>
 struct EncodeState {
   typedef typename KOperand<D>::T kop_t;
   kop_t qh[MBW], ql[MBW];
   f32x4 cb[MBW];
-  float mu[MBW], lam[MBW];
-  f32x4 acc[D / 16][MBW];
-  bool first;
+  float mu[MBW];
+  f32x4 acc[D / 16 + 1][MBW];
 };
 
-// One 32-token step of one wave: S^T tiles, softmax weights, O^T += V^T P^T.
-// ONLINE: keep a running max (raised lazily); otherwise the shift is a bound.
-// MASK (ragged last step only): tokens at or past n1 get weight zero.
-template <int D, int MBW, bool ONLINE, bool MASK>
-__device__ __forceinline__ void encode_step(EncodeState<D, MBW>& st, const __bf16* sK, const __bf16* sV,
-                                            int ks, int sb, int n1, int g, int c16) {
-  constexpr int KL = KOperand<D>::kLen;
-  constexpr int DB = D / 16;
-  constexpr float TAU = 8.0f;
+// Software pipeline over (step, latent block) pairs.  While block i's softmax
+// runs on the VALU, the matrix core works on the S^T tiles of the next block
+// and on the O^T update of the previous one; those are independent of block
+// i, so the two units overlap within the wave.
+template <int D>
+struct EncodePipe {
   typedef typename KOperand<D>::T kop_t;
-  const kop_t k0 = *reinterpret_cast<const kop_t*>(sK + slot_off<D>(ks * 32 + c16, KL * g));
-  const kop_t k1 = *reinterpret_cast<const kop_t*>(sK + slot_off<D>(ks * 32 + 16 + c16, KL * g));
-  f32x4 s0[MBW], s1[MBW];
-#pragma unroll
-  for (int i = 0; i < MBW; ++i) {
-    s0[i] = KOperand<D>::mma(k0, st.qh[i], st.cb[i]);
-    s1[i] = KOperand<D>::mma(k1, st.qh[i], st.cb[i]);
-    s0[i] = KOperand<D>::mma(k0, st.ql[i], s0[i]);
-    s1[i] = KOperand<D>::mma(k1, st.ql[i], s1[i]);
-  }
-  if (MASK) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const bool o0 = sb + 4 * g + r >= n1, o1 = sb + 16 + 4 * g + r >= n1;
-#pragma unroll
-      for (int i = 0; i < MBW; ++i) {
-        if (o0) s0[i][r] = -INFINITY;
-        if (o1) s1[i][r] = -INFINITY;
-      }
-    }
-  }
-  if (ONLINE) {
-    float lm[MBW];
-    bool hit = st.first;
-#pragma unroll
-    for (int i = 0; i < MBW; ++i) {
-      lm[i] = fmaxf(max3(s0[i][0], s0[i][1], s0[i][2]),
-                    max3(s0[i][3], s1[i][0], max3(s1[i][1], s1[i][2], s1[i][3])));
-      hit |= lm[i] > TAU;
-    }
-    if (__builtin_expect(__any(hit), 0)) {
-#pragma unroll
-      for (int i = 0; i < MBW; ++i) {
-        const float cm = max_over_rows(lm[i]);
-        const float d = st.first ? cm : fmaxf(cm, 0.0f);
-        st.mu[i] += d;
-        const float al = fast_exp2(-d);
-        st.lam[i] *= al;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) st.acc[db][i] *= al;
-        s0[i] -= d;
-        s1[i] -= d;
-        st.cb[i] = f32x4{-st.mu[i], -st.mu[i], -st.mu[i], -st.mu[i]};
-      }
-      st.first = false;
-    }
-  }
-  bf16x8 p[MBW];
-#pragma unroll
-  for (int i = 0; i < MBW; ++i) {
-    const bf16x2 p0 = pack_bf16(fast_exp2(s0[i][0]), fast_exp2(s0[i][1]));
-    const bf16x2 p1 = pack_bf16(fast_exp2(s0[i][2]), fast_exp2(s0[i][3]));
-    const bf16x2 p2 = pack_bf16(fast_exp2(s1[i][0]), fast_exp2(s1[i][1]));
-    const bf16x2 p3 = pack_bf16(fast_exp2(s1[i][2]), fast_exp2(s1[i][3]));
-    st.lam[i] = add_pair(p3, add_pair(p2, add_pair(p1, add_pair(p0, st.lam[i]))));
-    p[i] = bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-  }
-  // V^T operand: lane (row d = 16 db + c16, k-row g) needs V[tok][d] for the
-  // eight tokens of its k-slots; one transposing read gives a lane four
-  // tokens of its column when the 16 lanes of row g supply the 4-token x
-  // 16-column block (lane r: token base + r/4, columns 16 db + 4 (r%4) ..+3).
-  const int vt = ks * 32 + 4 * g + (c16 >> 2);
+  kop_t k0, k1;           // K operands of the current step (two 16-token halves)
+  f32x4 s0, s1;           // S^T tiles of the next (step, block)
+  bf16x8 p;               // weights of the previous block, whose O^T update is pending
+  bf16x8 v[D / 16];       // V^T operands of the previous block's step
+};
+
+// K operands (A of S^T = K Q^T: lane holds token row c16, k-chunk g) of step ks.
+template <int D>
+__device__ __forceinline__ void load_kop(const __bf16* sK, int ks, int g, int c16,
+                                         typename KOperand<D>::T& k0, typename KOperand<D>::T& k1) {
+  constexpr int KL = KOperand<D>::kLen;
+  typedef typename KOperand<D>::T kop_t;
+  k0 = *reinterpret_cast<const kop_t*>(sK + slot_off<D>(ks * 32 + c16, KL * g));
+  k1 = *reinterpret_cast<const kop_t*>(sK + slot_off<D>(ks * 32 + 16 + c16, KL * g));
+}
+
+// V^T operands of step ks: lane (row d = 16 db + c16, k-row g) needs V[tok][d]
+// for the eight tokens of its k-slots; one transposing read gives a lane four
+// tokens of its column when the 16 lanes of row g supply the 4-token x
+// 16-column block (lane r: token base + r/4, columns 16 db + 4 (r%4) ..+3).
+template <int D>
+__device__ __forceinline__ void load_vop(const __bf16* sV, int ks, int g, int c16, bf16x8 (&v)[D / 16]) {
   typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  const int vt = ks * 32 + 4 * g + (c16 >> 2);
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
+  for (int db = 0; db < D / 16; ++db) {
     const int ve = 16 * db + 4 * (c16 & 3);
     const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(sV + slot_off<D>(vt, ve)));
     const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(sV + slot_off<D>(vt + 16, ve)));
-    const bf16x8 vop = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    v[db] = bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+  }
+}
+
+// S^T tiles of latent block i (shift as accumulator input, query as hi + lo).
+template <int D, int MBW>
+__device__ __forceinline__ void block_logits(const EncodeState<D, MBW>& st, int i, typename KOperand<D>::T k0,
+                                             typename KOperand<D>::T k1, f32x4& s0, f32x4& s1) {
+  s0 = KOperand<D>::mma(k0, st.qh[i], st.cb[i]);
+  s1 = KOperand<D>::mma(k1, st.qh[i], st.cb[i]);
+  s0 = KOperand<D>::mma(k0, st.ql[i], s0);
+  s1 = KOperand<D>::mma(k1, st.ql[i], s1);
+}
+
+__device__ __forceinline__ bf16x8 weights(f32x4 s0, f32x4 s1) {
+  const bf16x2 p0 = pack_bf16(fast_exp2(s0[0]), fast_exp2(s0[1]));
+  const bf16x2 p1 = pack_bf16(fast_exp2(s0[2]), fast_exp2(s0[3]));
+  const bf16x2 p2 = pack_bf16(fast_exp2(s1[0]), fast_exp2(s1[1]));
+  const bf16x2 p3 = pack_bf16(fast_exp2(s1[2]), fast_exp2(s1[3]));
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// O^T and lambda updates of block i from its weights p and its step's V^T operands.
+template <int D, int MBW>
+__device__ __forceinline__ void block_update(EncodeState<D, MBW>& st, int i, const bf16x8 (&v)[D / 16], bf16x8 p,
+                                             bf16x8 ones) {
 #pragma unroll
-    for (int i = 0; i < MBW; ++i) st.acc[db][i] = mfma_k32(vop, p[i], st.acc[db][i]);
+  for (int db = 0; db < D / 16; ++db) st.acc[db][i] = mfma_k32(v[db], p, st.acc[db][i]);
+  st.acc[D / 16][i] = mfma_k32(ones, p, st.acc[D / 16][i]);
+}
+
+// One 32-token step (step ks of the K/V slots sK/sV).  kn0/kn1 are the next
+// step's K operands (HAS_NEXT), read by the caller from wherever that step
+// lives.  ONLINE: running max, starting from the exact column max of the
+// split's first step and raised lazily (only when a value exceeds mu + TAU,
+// so weights and sums stay finite); otherwise the shift is a bound.
+// MASK (the split's ragged last step): tokens at or past n1 weigh zero.
+template <int D, int MBW, bool ONLINE, bool MASK, bool HAS_NEXT>
+__device__ __forceinline__ void encode_step(EncodeState<D, MBW>& st, EncodePipe<D>& pp, const __bf16* sV, int ks,
+                                            typename KOperand<D>::T kn0, typename KOperand<D>::T kn1, int sb,
+                                            int n1, int g, int c16, bf16x8 ones) {
+  constexpr int DB = D / 16;
+  constexpr float TAU = 8.0f;
+  bf16x8 v[DB];
+  load_vop<D>(sV, ks, g, c16, v);
+#pragma unroll
+  for (int i = 0; i < MBW; ++i) {
+    f32x4 s0 = pp.s0, s1 = pp.s1;
+    // matrix core: next block's logits, previous block's update
+    if (i + 1 < MBW)
+      block_logits<D, MBW>(st, i + 1, pp.k0, pp.k1, pp.s0, pp.s1);
+    else if (HAS_NEXT)
+      block_logits<D, MBW>(st, 0, kn0, kn1, pp.s0, pp.s1);
+    block_update<D, MBW>(st, i == 0 ? MBW - 1 : i - 1, pp.v, pp.p, ones);
+    // VALU: this block's weights
+    if (MASK) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (sb + 4 * g + r >= n1) s0[r] = -INFINITY;
+        if (sb + 16 + 4 * g + r >= n1) s1[r] = -INFINITY;
+      }
+    }
+    bf16x8 p = weights(s0, s1);
+    // keep the weights ahead of the (rare) rescale branch, in the same
+    // scheduling region as the matrix-core work above
+    asm volatile("" : "+v"(p));
+    if (ONLINE) {
+      const float lm = fmaxf(max3(s1[2], s1[3], max3(s0[3], s1[0], max3(s0[0], s0[1], s0[2]))), s1[1]);
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(lm > TAU) != 0, 0)) {
+        const float d = fmaxf(max_over_rows(lm), 0.0f);
+        st.mu[i] += d;
+        const float al = fast_exp2(-d);
+#pragma unroll
+        for (int db = 0; db <= DB; ++db) st.acc[db][i] *= al;
+        s0 -= d;
+        s1 -= d;
+        if (MBW == 1) {  // the pending logits are this block's next step
+          pp.s0 -= d;
+          pp.s1 -= d;
+        }
+        st.cb[i] = f32x4{-st.mu[i], -st.mu[i], -st.mu[i], -st.mu[i]};
+        p = weights(s0, s1);
+      }
+    }
+    pp.p = p;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) pp.v[db] = v[db];
+  }
+  if (HAS_NEXT) {
+    pp.k0 = kn0;
+    pp.k1 = kn1;
   }
 }
 
 // Largest squared key norm among the tile's tokens seen by this thread
-// (every thread reads two 16-byte chunks; the chunks of one row sit in
-// adjacent lanes).
-template <int D>
+// (the 16-byte chunks of the K tile are spread over the workgroup; the
+// chunks of one row sit in adjacent lanes).
+template <int D, int NW>
 __device__ __forceinline__ float tile_knorm(const __bf16* sK, int tid) {
   constexpr int U = D / 8;
   float best = 0.0f;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(sK + (tid + 256 * h) * 8);
+  for (int h = 0; h < Ring<D, NW>::DI; ++h) {
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(sK + (tid + 64 * NW * h) * 8);
     float ss = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -251,60 +329,132 @@ __device__ __forceinline__ float tile_knorm(const __bf16* sK, int tid) {
   return best;
 }
 
-// One tile of the ring (slot I holds tile t): wait for this wave's loads of
-// tile t, barrier (every wave's part has landed, and every wave has finished
-// tile t-1, whose slot is refilled next), issue tile t+3 into that slot, then
-// consume tile t: whole 32-token steps, and a masked step if the split ends
-// inside the tile.
-template <int D, int MBW, bool KNORM, bool ONLINE, int I>
-__device__ __forceinline__ void encode_tile(EncodeState<D, MBW>& st, const __bf16* Kp, const __bf16* Vp, int t,
-                                            int n0, int n1, int tid, int wave, int lane, bool wave_active,
-                                            int g, int c16, float& kn2) {
-  constexpr int TN = kTileElems / D;
-  FLAREPP_WAIT_VM(2 * kDmaPerTile);
-  __builtin_amdgcn_s_barrier();
-  tile_dma<D, (I + 3) & 3>(Kp, Vp, n0 + (t + 3) * TN, n1, wave, lane);
-  if (KNORM) kn2 = fmaxf(kn2, tile_knorm<D>(ring_k<I>(), tid));
-  if (!wave_active) return;
-  const int tb = n0 + t * TN;
-  const int full = min(TN / 32, (n1 - tb) / 32);
-#pragma unroll 1
-  for (int ks = 0; ks < full; ++ks)
-    encode_step<D, MBW, ONLINE, false>(st, ring_k<I>(), ring_v<I>(), ks, tb + ks * 32, n1, g, c16);
-  if (full < TN / 32 && tb + full * 32 < n1)
-    encode_step<D, MBW, ONLINE, true>(st, ring_k<I>(), ring_v<I>(), full, tb + full * 32, n1, g, c16);
+// Ring protocol.  Tile u+2's loads are issued at the barrier that opens tile
+// u; before it a wave waits for its own loads of tile u (those of tile u+1
+// may still be in flight), so every wave's part of tile u has landed once all
+// have arrived.  The barrier opening tile u is taken at the start of the last
+// step of tile u-1, which still reads tile u-1 and (for the next step's K
+// operands) tile u; the slot refilled there, (u+2) & 3, held tile u-2, which
+// every wave has finished reading.
+template <int D, int NW, int I>
+__device__ __forceinline__ void ring_open(__bf16* ring, const __bf16* Kp, const __bf16* Vp, int u, int n0, int n1,
+                                          int wave, int lane) {
+  constexpr int kWait = Ring<D, NW>::kDma;
+  FLAREPP_WAIT_VM(kWait);
+  ring_barrier();
+  tile_dma<D, NW, (I + 2) & 3>(ring, Kp, Vp, n0 + (u + 2) * Ring<D, NW>::TN, n1, wave, lane);
 }
 
-template <int D, int MBW, bool KNORM, bool ONLINE>
-__device__ __forceinline__ void encode_tiles(EncodeState<D, MBW>& st, const __bf16* Kp, const __bf16* Vp, int n0,
-                                             int n1, int tid, int wave, int lane, bool wave_active, int g, int c16,
-                                             float& kn2) {
-  constexpr int TN = kTileElems / D;
-  const int ntiles = (n1 - n0 + TN - 1) / TN;
-  tile_dma<D, 0>(Kp, Vp, n0, n1, wave, lane);
-  tile_dma<D, 1>(Kp, Vp, n0 + TN, n1, wave, lane);
-  tile_dma<D, 2>(Kp, Vp, n0 + 2 * TN, n1, wave, lane);
-  for (int t = 0; t < ntiles; t += 4) {
-    encode_tile<D, MBW, KNORM, ONLINE, 0>(st, Kp, Vp, t, n0, n1, tid, wave, lane, wave_active, g, c16, kn2);
-    if (t + 1 >= ntiles) break;
-    encode_tile<D, MBW, KNORM, ONLINE, 1>(st, Kp, Vp, t + 1, n0, n1, tid, wave, lane, wave_active, g, c16, kn2);
-    if (t + 2 >= ntiles) break;
-    encode_tile<D, MBW, KNORM, ONLINE, 2>(st, Kp, Vp, t + 2, n0, n1, tid, wave, lane, wave_active, g, c16, kn2);
-    if (t + 3 >= ntiles) break;
-    encode_tile<D, MBW, KNORM, ONLINE, 3>(st, Kp, Vp, t + 3, n0, n1, tid, wave, lane, wave_active, g, c16, kn2);
+// Tile t in slot I (already opened): its steps, the last of which opens tile
+// t+1 (if any) and starts that tile's first logits.
+template <int D, int NW, int MBW, bool KNORM, bool ONLINE, int I>
+__device__ __forceinline__ void encode_tile(EncodeState<D, MBW>& st, EncodePipe<D>& pp, __bf16* ring,
+                                            const __bf16* Kp, const __bf16* Vp, int t, int n0, int n1, int ntiles,
+                                            int tid, int wave, int lane, bool wave_active, int g, int c16,
+                                            bf16x8 ones, float& kn2) {
+  typedef Ring<D, NW> R;
+  typedef typename KOperand<D>::T kop_t;
+  constexpr int J1 = (I + 1) & 3;
+  const int tb = n0 + t * R::TN;
+  const int nsteps = min(R::SPT, (n1 - tb + 31) / 32);
+#pragma unroll 1
+  for (int ks = 0; ks + 1 < nsteps; ++ks) {
+    if (wave_active) {
+      kop_t kn0, kn1;
+      load_kop<D>(R::template k<I>(ring), ks + 1, g, c16, kn0, kn1);
+      encode_step<D, MBW, ONLINE, false, true>(st, pp, R::template v<I>(ring), ks, kn0, kn1, tb + ks * 32, n1, g,
+                                               c16, ones);
+    }
   }
+  const int ks = nsteps - 1;
+  if (t + 1 < ntiles) {
+    ring_open<D, NW, J1>(ring, Kp, Vp, t + 1, n0, n1, wave, lane);
+    if (KNORM) kn2 = fmaxf(kn2, tile_knorm<D, NW>(R::template k<J1>(ring), tid));
+    if (wave_active) {
+      kop_t kn0, kn1;
+      load_kop<D>(R::template k<J1>(ring), 0, g, c16, kn0, kn1);
+      encode_step<D, MBW, ONLINE, false, true>(st, pp, R::template v<I>(ring), ks, kn0, kn1, tb + ks * 32, n1, g,
+                                               c16, ones);
+    }
+  } else if (wave_active) {
+    const kop_t z{};
+    if (tb + (ks + 1) * 32 <= n1)
+      encode_step<D, MBW, ONLINE, false, false>(st, pp, R::template v<I>(ring), ks, z, z, tb + ks * 32, n1, g, c16,
+                                                ones);
+    else
+      encode_step<D, MBW, ONLINE, true, false>(st, pp, R::template v<I>(ring), ks, z, z, tb + ks * 32, n1, g, c16,
+                                               ones);
+  }
+}
+
+template <int D, int NW, int MBW, bool KNORM, bool ONLINE>
+__device__ __forceinline__ void encode_tiles(EncodeState<D, MBW>& st, __bf16* ring, const __bf16* Kp,
+                                             const __bf16* Vp, int n0, int n1, int tid, int wave, int lane,
+                                             bool wave_active, int g, int c16, float& kn2) {
+  typedef Ring<D, NW> R;
+  constexpr int DB = D / 16;
+  const int ntiles = (n1 - n0 + R::TN - 1) / R::TN;
+  // A operand of the lambda tile: row 0 all ones
+  const __bf16 one = c16 == 0 ? (__bf16)1.0f : (__bf16)0.0f;
+  const bf16x8 ones = {one, one, one, one, one, one, one, one};
+  EncodePipe<D> pp;
+  pp.p = bf16x8{};  // no update pending before the first block
+#pragma unroll
+  for (int db = 0; db < DB; ++db) pp.v[db] = bf16x8{};
+
+  tile_dma<D, NW, 0>(ring, Kp, Vp, n0, n1, wave, lane);
+  tile_dma<D, NW, 1>(ring, Kp, Vp, n0 + R::TN, n1, wave, lane);
+  ring_open<D, NW, 0>(ring, Kp, Vp, 0, n0, n1, wave, lane);
+  if (KNORM) kn2 = fmaxf(kn2, tile_knorm<D, NW>(R::template k<0>(ring), tid));
+  if (wave_active) {
+    load_kop<D>(R::template k<0>(ring), 0, g, c16, pp.k0, pp.k1);
+    if (ONLINE) {
+      // the running max starts at the exact column max of the first step
+      // (the shift is still zero here)
+#pragma unroll
+      for (int i = 0; i < MBW; ++i) {
+        f32x4 s0, s1;
+        block_logits<D, MBW>(st, i, pp.k0, pp.k1, s0, s1);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (n0 + 4 * g + r >= n1) s0[r] = -INFINITY;
+          if (n0 + 16 + 4 * g + r >= n1) s1[r] = -INFINITY;
+        }
+        const float lm = fmaxf(max3(s1[2], s1[3], max3(s0[3], s1[0], max3(s0[0], s0[1], s0[2]))), s1[1]);
+        st.mu[i] = max_over_rows(lm);
+        st.cb[i] = f32x4{-st.mu[i], -st.mu[i], -st.mu[i], -st.mu[i]};
+      }
+    }
+    block_logits<D, MBW>(st, 0, pp.k0, pp.k1, pp.s0, pp.s1);
+  }
+  for (int t = 0; t < ntiles; t += 4) {
+    encode_tile<D, NW, MBW, KNORM, ONLINE, 0>(st, pp, ring, Kp, Vp, t, n0, n1, ntiles, tid, wave, lane,
+                                              wave_active, g, c16, ones, kn2);
+    if (t + 1 >= ntiles) break;
+    encode_tile<D, NW, MBW, KNORM, ONLINE, 1>(st, pp, ring, Kp, Vp, t + 1, n0, n1, ntiles, tid, wave, lane,
+                                              wave_active, g, c16, ones, kn2);
+    if (t + 2 >= ntiles) break;
+    encode_tile<D, NW, MBW, KNORM, ONLINE, 2>(st, pp, ring, Kp, Vp, t + 2, n0, n1, ntiles, tid, wave, lane,
+                                              wave_active, g, c16, ones, kn2);
+    if (t + 3 >= ntiles) break;
+    encode_tile<D, NW, MBW, KNORM, ONLINE, 3>(st, pp, ring, Kp, Vp, t + 3, n0, n1, ntiles, tid, wave, lane,
+                                              wave_active, g, c16, ones, kn2);
+  }
+  // the last block's pending update
+  if (wave_active) block_update<D, MBW>(st, MBW - 1, pp.v, pp.p, ones);
   // the ring's trailing loads must land before the workgroup's LDS is released
   FLAREPP_WAIT_VM(0);
 }
 
 // BOUNDED: the shift may come from a.bias (the bound path, with the online
 // path as fallback when a bound is unsafe); otherwise always online.
-template <int D, int MBW, bool KNORM, bool BOUNDED>
-__global__ __launch_bounds__(256, 2) void encode_split_bf16(EncodeArgs a) {
+template <int D, int NW, int MBW, bool KNORM, bool BOUNDED>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void encode_split_bf16(EncodeArgs a) {
   constexpr int DB = D / 16;     // 16-row blocks of O^T
   constexpr int KL = KOperand<D>::kLen;
   typedef typename KOperand<D>::T kop_t;
-  __shared__ float sRed[4];
+  __shared__ __attribute__((aligned(16))) __bf16 ring[8 * Ring<D, NW>::TE];
+  __shared__ float sRed[NW];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -314,7 +464,7 @@ __global__ __launch_bounds__(256, 2) void encode_split_bf16(EncodeArgs a) {
   const int n0 = j * a.chunk;
   const int n1 = min(a.N, n0 + a.chunk);
   const int nMB = a.Mp >> 4;
-  const int mb0 = (blockIdx.z * 4 + wave) * MBW;
+  const int mb0 = (blockIdx.z * NW + wave) * MBW;
   const bool wave_active = mb0 < nMB;
 
   const __bf16* Kp = a.K + bh * (int64_t)a.N * D;
@@ -339,9 +489,8 @@ __global__ __launch_bounds__(256, 2) void encode_split_bf16(EncodeArgs a) {
         st.mu[i] = 0.0f;
       }
       need_online |= !(st.mu[i] <= 1e30f);
-      st.lam[i] = 0.0f;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) st.acc[db][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int db = 0; db <= DB; ++db) st.acc[db][i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
   const bool online = __any(need_online);
@@ -350,15 +499,14 @@ __global__ __launch_bounds__(256, 2) void encode_split_bf16(EncodeArgs a) {
     if (online) st.mu[i] = 0.0f;
     st.cb[i] = f32x4{-st.mu[i], -st.mu[i], -st.mu[i], -st.mu[i]};
   }
-  st.first = online;
   float kn2 = 0.0f;
   // the operand loads above must not be counted with the ring's loads
   FLAREPP_WAIT_VM(0);
 
   if (!BOUNDED || online)
-    encode_tiles<D, MBW, KNORM, true>(st, Kp, Vp, n0, n1, tid, wave, lane, wave_active, g, c16, kn2);
+    encode_tiles<D, NW, MBW, KNORM, true>(st, ring, Kp, Vp, n0, n1, tid, wave, lane, wave_active, g, c16, kn2);
   else
-    encode_tiles<D, MBW, KNORM, false>(st, Kp, Vp, n0, n1, tid, wave, lane, wave_active, g, c16, kn2);
+    encode_tiles<D, NW, MBW, KNORM, false>(st, ring, Kp, Vp, n0, n1, tid, wave, lane, wave_active, g, c16, kn2);
 
   // ---- partial records
   if (wave_active) {
@@ -368,12 +516,11 @@ __global__ __launch_bounds__(256, 2) void encode_split_bf16(EncodeArgs a) {
       const int mblk = mb0 + i;
       if (mblk >= nMB) break;
       const int m = mblk * 16 + c16;
-      const float lt = sum_over_rows(st.lam[i]);
       float* rec = a.part + ((lbh * a.Mp + m) * (int64_t)a.J + j) * PS;
 #pragma unroll
       for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(rec + 16 * db + 4 * g) = st.acc[db][i];
       if (g == 0) {
-        rec[D] = lt;
+        rec[D] = st.acc[DB][i][0];  // row 0 of the lambda tile
         rec[D + 1] = st.mu[i];
       }
     }
@@ -384,8 +531,12 @@ __global__ __launch_bounds__(256, 2) void encode_split_bf16(EncodeArgs a) {
     for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
     if (lane == 0) sRed[wave] = x;
     __syncthreads();
-    if (tid == 0 && blockIdx.z == 0)
-      a.knorm[lbh * a.J + j] = fmaxf(fmaxf(sRed[0], sRed[1]), fmaxf(sRed[2], sRed[3]));
+    if (tid == 0 && blockIdx.z == 0) {
+      float r = sRed[0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) r = fmaxf(r, sRed[w]);
+      a.knorm[lbh * a.J + j] = r;
+    }
   }
 }
 

@@ -44,7 +44,7 @@ struct Plan {
   float c;          // scale * log2(e)
   int G;            // heads per launch group
   int J, chunk;     // splits of N and tokens per split (encode)
-  int mbw;          // 16-latent blocks per wave (bf16 encode)
+  int nw, mbw;      // waves per workgroup and 16-latent blocks per wave (bf16 encode)
   int tpr;          // threads per latent row in the merge
   int dchunk;       // tokens per decode workgroup (bf16)
   int nS;           // seed / fixed-query operand blocks (1 or H)
@@ -97,8 +97,12 @@ Plan make_plan(const flarepp_desc* d, int op) {
   p.G = (int)G;
 
   const int nMB = p.Mp / 16;
-  p.mbw = nMB <= 4 ? 1 : nMB <= 8 ? 2 : nMB <= 12 ? 3 : 4;
-  const int tile = p.bf16 ? 4096 / p.D : 64;
+  // up to 128 latents: four waves; beyond: eight waves of two blocks each
+  // (a wave's registers hold at most two blocks with the pipelined step)
+  p.nw = nMB <= 8 ? 4 : 8;
+  p.mbw = nMB <= 4 ? 1 : 2;
+  // splits are whole encode tiles (8192 or 4096 bf16 of K per tile, by wave count)
+  const int tile = p.bf16 ? (p.nw == 8 ? 8192 : 4096) / p.D : 64;
   const int64_t target = (p.bf16 ? 2 : 4) * int64_t(kComputeUnits);
   int64_t J = std::max<int64_t>(1, cdiv(target, G));
   int env_j;
@@ -230,14 +234,14 @@ flarepp_status run_prep(const Plan& p, const void* src, bool src_bf16, int64_t s
 template <int D, bool KNORM, bool BOUNDED>
 flarepp_status run_encode_bf16(const Plan& p, const EncodeArgs& a, int Gc, hipStream_t st, Recorder& rec,
                                int kind) {
-  const dim3 grid((unsigned)p.J, (unsigned)Gc, (unsigned)cdiv(p.Mp / 16, 4 * p.mbw));
+  const dim3 grid((unsigned)p.J, (unsigned)Gc, (unsigned)cdiv(p.Mp / 16, p.nw * p.mbw));
   rec.before(kind, st);
-  switch (p.mbw) {
-    case 1: encode_split_bf16<D, 1, KNORM, BOUNDED><<<grid, dim3(256), 0, st>>>(a); break;
-    case 2: encode_split_bf16<D, 2, KNORM, BOUNDED><<<grid, dim3(256), 0, st>>>(a); break;
-    case 3: encode_split_bf16<D, 3, KNORM, BOUNDED><<<grid, dim3(256), 0, st>>>(a); break;
-    default: encode_split_bf16<D, 4, KNORM, BOUNDED><<<grid, dim3(256), 0, st>>>(a); break;
-  }
+  if (p.nw == 8)
+    encode_split_bf16<D, 8, 2, KNORM, BOUNDED><<<grid, dim3(512), 0, st>>>(a);
+  else if (p.mbw == 2)
+    encode_split_bf16<D, 4, 2, KNORM, BOUNDED><<<grid, dim3(256), 0, st>>>(a);
+  else
+    encode_split_bf16<D, 4, 1, KNORM, BOUNDED><<<grid, dim3(256), 0, st>>>(a);
   rec.after(st);
   return launched();
 }
@@ -395,7 +399,10 @@ flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in
         e.q_sh = MpD;
         e.q_off = g0 * MpD;
         e.bias = stage == kRoute ? at<float>(ws, p.o_bias) : nullptr;
-        FLAREPP_TRY((run_encode_bf16<D, false, false>(p, e, Gc, st, rec, FLAREPP_KERNEL_ENCODE)));
+        if (stage == kRoute)
+          FLAREPP_TRY((run_encode_bf16<D, false, true>(p, e, Gc, st, rec, FLAREPP_KERNEL_ENCODE)));
+        else
+          FLAREPP_TRY((run_encode_bf16<D, false, false>(p, e, Gc, st, rec, FLAREPP_KERNEL_ENCODE)));
         MergeArgs m = merge_args(p, ws, g0);
         m.out = Z_out;
         if (stage == kRoute) m.op_zt = zt;
