@@ -59,6 +59,48 @@ def test_longseq_sampled_heads(fp):
     run_and_compare(fp, p, heads=heads)
 
 
+def test_million_full_size_sampled(fp):
+    """The million-point workload at full size, in the launch configuration the
+    bench times.  A row of Qd or Z depends only on its own latent, so the oracle
+    computes sampled latent rows exactly (one pass over the 2^20 tokens each):
+    Qd_m = SDPA(S_m, K, V) and Z_m = SDPA(Qd_m, K, V) from the oracle's own
+    Qd_m.  Sampled rows of Y are the oracle's decode of those tokens fed the
+    GPU's float32 Qd and Z, which checks the decode at full size."""
+    import torch
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    p = inputs.make_problem("million")
+    print(f"\n  case million: B{p.B} H{p.H} N{p.N} M{p.M} D{p.D} {p.dtype}", flush=True)
+    S, K, V = to_device(p.S), to_device(p.K), to_device(p.V)
+    Y, Qd, Z = fp.route(S, K, V, p.scale, with_intermediates=True)
+    rng = np.random.default_rng(11)
+    tokens = np.unique(np.concatenate([[0, p.N - 1], rng.choice(p.N, 62, replace=False)]))
+    heads = [(0, 0), (0, 5)]
+    latents = [0, 97, 200, p.M - 1]
+    Yt = torch.stack([Y[b, h][torch.from_numpy(tokens).cuda()] for b, h in heads])
+    torch.cuda.synchronize()
+    Yt, Qd, Z = Yt.cpu().numpy(), Qd.cpu().numpy(), Z.cpu().numpy()
+    del Y
+
+    def rows(bh_m):
+        (b, h), m = bh_m
+        qd = oracle.sdpa(p.S[m:m + 1], p.K[b, h], p.V[b, h], p.scale)
+        z = oracle.sdpa(qd, p.K[b, h], p.V[b, h], p.scale)
+        return qd[0], z[0]
+
+    jobs = [(bh, m) for bh in heads for m in latents]
+    with ThreadPoolExecutor(min(16, len(jobs))) as ex:
+        ref = list(ex.map(rows, jobs))
+    got_q = np.stack([Qd[b, h, m] for (b, h), m in jobs])
+    got_z = np.stack([Z[b, h, m] for (b, h), m in jobs])
+    assert_close("Qd rows", got_q, np.stack([r[0] for r in ref]), p.dtype)
+    assert_close("Z rows", got_z, np.stack([r[1] for r in ref]), p.dtype)
+    y_ref = np.stack([oracle.sdpa(p.K[b, h][tokens], Qd[b, h], Z[b, h], p.scale) for b, h in heads])
+    assert_close("Y rows (decode of the GPU's Qd, Z)", Yt, y_ref, p.dtype)
+
+
 EDGE = [
     # B, H, N, M, D, dtype
     (1, 1, 1, 1, 16, "bf16"),
