@@ -52,7 +52,8 @@ __global__ __launch_bounds__(256, 1) void decode_bf16(DecodeArgs a) {
   constexpr int MP = MB * 16;
   typedef typename KOperand<D>::T kop_t;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g = lane >> 4, c16 = lane & 15;
   const int64_t lbh = blockIdx.y, bh = a.bh0 + lbh;
   const int b = (int)(bh / a.H), h = (int)(bh - (int64_t)b * a.H);
@@ -101,13 +102,7 @@ __global__ __launch_bounds__(256, 1) void decode_bf16(DecodeArgs a) {
   constexpr int CH = MB < 4 ? MB : 4;     // latent blocks per chunk of logits
   constexpr int NCH = (MB + CH - 1) / CH;
 
-  // two 16-token blocks of K in flight ahead of the one being consumed
-  int blk = n0 + wave * 16;
-  kop_t k1 = kload(blk), k2 = kload(blk + 64);
-  for (; blk < n1; blk += 64) {
-    const kop_t kb = k1;
-    k1 = k2;
-    k2 = kload(blk + 128);
+  auto body = [&](const kop_t kb, const int blk) {
     const int tok = blk + c16;
 
     // token norm -> shift
@@ -118,7 +113,7 @@ __global__ __launch_bounds__(256, 1) void decode_bf16(DecodeArgs a) {
       ss = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss, false);
     }
     ss = sum_over_rows(ss);
-    const float mu = a.c * sqrtf(ss) * qmax * (1.0f + 1.0f / 4096.0f);
+    const float mu = a.c * __builtin_amdgcn_sqrtf(ss) * qmax * (1.0f + 1.0f / 4096.0f);
     const bool use_bound = have_bound && !__any(!(2.0f * mu <= kBoundSpan));
     float sh = -mu;
     if (!use_bound) {
@@ -178,12 +173,215 @@ __global__ __launch_bounds__(256, 1) void decode_bf16(DecodeArgs a) {
         for (int db = 0; db < DB; ++db) yacc[db] = mfma_k32(zop[kb2][db], pb, yacc[db]);
       }
     }
-    const float inv = 1.0f / sum_over_rows(lam);
+    const float inv = __builtin_amdgcn_rcpf(sum_over_rows(lam));
     if (tok < n1) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
         *reinterpret_cast<f32x4*>(Yp + (int64_t)tok * D + 16 * db + 4 * g) = yacc[db] * inv;
     }
+  };
+
+  // Two 16-token blocks of K in flight ahead of the one being consumed.  The
+  // loop is unrolled by three so every block's registers are loaded once and
+  // consumed in place (copying a register that a load is still filling would
+  // make the copy wait for that load).
+  // Whole groups of three blocks (blocks past the chunk read its last row and
+  // store nothing), so the loop has a single steady state.
+  constexpr int S = 64;
+  int blk = n0 + wave * 16;
+  kop_t k0 = kload(blk), k1 = kload(blk + S), k2;
+  for (; blk < n1; blk += 3 * S) {
+    k2 = kload(blk + 2 * S);
+    body(k0, blk);
+    k0 = kload(blk + 3 * S);
+    body(k1, blk + S);
+    k1 = kload(blk + 4 * S);
+    body(k2, blk + 2 * S);
+  }
+}
+
+// Paired decode for many latents.  Holding c * Qd (hi/lo) and Z^T for all M
+// latents costs one wave ~190 VGPRs at M = 256 (one wave per SIMD, nothing to
+// hide the MFMA -> exp -> MFMA dependencies).  Here two waves share every
+// 16-token block, each owning MBH of the latent blocks; both compute the
+// same per-token shift, so their partial weight sums and partial Y^T tiles
+// add exactly, and they swap the halves each one stores through a
+// double-buffered LDS exchange (one barrier per block).  When a block needs
+// the exact max over the latents (the bound is unsafe), the two partial
+// maxima are exchanged the same way first.
+constexpr uint32_t kWaitLgkm0 = 0xF | (0x7 << 4) | (0x3 << 14);  // s_waitcnt lgkmcnt(0)
+
+__device__ __forceinline__ void pair_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// RAGGED: some of this wave's latent rows lie at or past M (M is not a
+// multiple of 16, or the blocks do not split evenly); those get weight zero.
+template <int D, int MBH, bool RAGGED>
+__global__ __launch_bounds__(128, 2) void decode_pair_bf16(DecodeArgs a) {
+  constexpr int KL = KOperand<D>::kLen;
+  constexpr int DB = D / 16;
+  constexpr int KBH = (MBH + 1) / 2;  // 32-latent contraction blocks per wave
+  typedef typename KOperand<D>::T kop_t;
+  __shared__ f32x4 sY[2][2][64];      // [buffer][sender][lane]
+  __shared__ float sLam[2][2][16];    // [buffer][sender][token]
+  __shared__ float sMax[2][16];       // [sender][token]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w2 = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int g = lane >> 4, c16 = lane & 15;
+  const int64_t lbh = blockIdx.y, bh = a.bh0 + lbh;
+  const int b = (int)(bh / a.H), h = (int)(bh - (int64_t)b * a.H);
+  const int n0 = blockIdx.x * a.chunk;
+  const int n1 = min(a.N, n0 + a.chunk);
+  const int MB = a.Mp >> 4;
+  const int mb0 = w2 * MBH;  // this wave's first latent block
+
+  // ---- this wave's half of the latent side, in registers
+  const int64_t qo = (int64_t)b * a.q_sb + (int64_t)h * a.q_sh - a.q_off;
+  kop_t qh[MBH], ql[MBH];
+#pragma unroll
+  for (int i = 0; i < MBH; ++i) {
+    if (mb0 + i < MB) {
+      const int64_t o = qo + (int64_t)((mb0 + i) * 16 + c16) * D + KL * g;
+      qh[i] = *reinterpret_cast<const kop_t*>(a.q_hi + o);
+      ql[i] = *reinterpret_cast<const kop_t*>(a.q_lo + o);
+    } else {
+      qh[i] = kop_t{};
+      ql[i] = kop_t{};
+    }
+  }
+  bf16x8 zop[KBH][DB];
+  {
+    const __bf16* zb = a.zt + lbh * (int64_t)a.Mp * D;
+#pragma unroll
+    for (int kb = 0; kb < KBH; ++kb)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const __bf16* zr = zb + (int64_t)(16 * db + c16) * a.Mp + (mb0 + 2 * kb) * 16 + 4 * g;
+        bf16x4 z0 = bf16x4{}, z1 = bf16x4{};
+        if (mb0 + 2 * kb < MB) z0 = *reinterpret_cast<const bf16x4*>(zr);
+        if (2 * kb + 1 < MBH && mb0 + 2 * kb + 1 < MB) z1 = *reinterpret_cast<const bf16x4*>(zr + 16);
+        zop[kb][db] = bf16x8{z0[0], z0[1], z0[2], z0[3], z1[0], z1[1], z1[2], z1[3]};
+      }
+  }
+  float qmax = 0.0f;
+  if (a.qnorm)
+    for (int m = lane; m < a.Mp; m += 64) qmax = fmaxf(qmax, a.qnorm[qo / D + m]);
+  qmax = wave_max(qmax);
+  const bool have_bound = a.qnorm != nullptr;
+  // latent rows of this wave at or past M (the padding of the last block and
+  // whole blocks past the end) get weight zero
+  const int mvalid = a.M - mb0 * 16;
+
+  const __bf16* Kp = a.K + bh * (int64_t)a.N * D;
+  float* Yp = a.Y + bh * (int64_t)a.N * D;
+  auto kload = [&](int blk) {
+    const int tok = min(blk + c16, n1 - 1);
+    return *reinterpret_cast<const kop_t*>(Kp + (int64_t)tok * D + KL * g);
+  };
+
+  auto body = [&](const kop_t kb, const int blk, const int buf) {
+    const int tok = blk + c16;
+
+    // token norm -> shift (identical in both waves)
+    float ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < KL / 2; ++e) {
+      const bf16x2 pr = {kb[2 * e], kb[2 * e + 1]};
+      ss = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss, false);
+    }
+    ss = sum_over_rows(ss);
+    const float mu = a.c * __builtin_amdgcn_sqrtf(ss) * qmax * (1.0f + 1.0f / 4096.0f);
+    const bool use_bound = have_bound && __builtin_amdgcn_ballot_w64(!(2.0f * mu <= kBoundSpan)) == 0;
+    float sh = -mu;
+    if (!use_bound) {
+      // exact max over all latents: this wave's half, then the partner's
+      float lm = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < MBH; ++i) {
+        f32x4 t = KOperand<D>::mma(qh[i], kb, f32x4{0.f, 0.f, 0.f, 0.f});
+        t = KOperand<D>::mma(ql[i], kb, t);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (!RAGGED || i * 16 + 4 * g + r < mvalid) lm = fmaxf(lm, t[r]);
+      }
+      lm = max_over_rows(lm);
+      if (g == 0) sMax[w2][c16] = lm;
+      pair_barrier();
+      sh = -fmaxf(lm, sMax[1 - w2][c16]);
+      pair_barrier();  // both have read sMax before it is written again
+    }
+    const f32x4 cinit = {sh, sh, sh, sh};
+
+    float lam = 0.0f;
+    f32x4 yacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) yacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb2 = 0; kb2 < KBH; ++kb2) {
+      f32x4 L[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = 2 * kb2 + u;
+        if (i < MBH) {
+          L[u] = KOperand<D>::mma(qh[i], kb, cinit);
+          L[u] = KOperand<D>::mma(ql[i], kb, L[u]);
+          if (RAGGED) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (i * 16 + 4 * g + r >= mvalid) L[u][r] = -INFINITY;
+          }
+        } else {
+          L[u] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        }
+      }
+      const bf16x2 p0 = pack_bf16(fast_exp2(L[0][0]), fast_exp2(L[0][1]));
+      const bf16x2 p1 = pack_bf16(fast_exp2(L[0][2]), fast_exp2(L[0][3]));
+      const bf16x2 p2 = pack_bf16(fast_exp2(L[1][0]), fast_exp2(L[1][1]));
+      const bf16x2 p3 = pack_bf16(fast_exp2(L[1][2]), fast_exp2(L[1][3]));
+      lam = add_pair(p3, add_pair(p2, add_pair(p1, add_pair(p0, lam))));
+      const bf16x8 pb = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+#pragma unroll
+      for (int db = 0; db < DB; ++db) yacc[db] = mfma_k32(zop[kb2][db], pb, yacc[db]);
+    }
+    lam = sum_over_rows(lam);
+
+    // swap: wave w2 stores d-block w2 (D = 32) or wave 0 stores all (D = 16)
+    if (g == 0) sLam[buf][w2][c16] = lam;
+    if (w2 == 0) {
+      if (DB == 2) sY[buf][0][lane] = yacc[DB - 1];
+      pair_barrier();
+      const float inv = __builtin_amdgcn_rcpf(lam + sLam[buf][1][c16]);
+      const f32x4 y = yacc[0] + sY[buf][1][lane];
+      if (tok < n1) *reinterpret_cast<f32x4*>(Yp + (int64_t)tok * D + 4 * g) = y * inv;
+    } else {
+      sY[buf][1][lane] = yacc[0];
+      pair_barrier();
+      if (DB == 2) {
+        const float inv = __builtin_amdgcn_rcpf(lam + sLam[buf][0][c16]);
+        const f32x4 y = yacc[DB - 1] + sY[buf][0][lane];
+        if (tok < n1) *reinterpret_cast<f32x4*>(Yp + (int64_t)tok * D + 16 + 4 * g) = y * inv;
+      }
+    }
+  };
+
+  // two blocks in flight ahead; unrolled by three (see decode_bf16), and by
+  // two more for the exchange buffer's parity
+  constexpr int S = 16;
+  int blk = n0;
+  kop_t k0 = kload(blk), k1 = kload(blk + S), k2;
+  for (int it = 0; blk < n1; blk += 3 * S, ++it) {
+    const int par = it & 1;  // blocks 3 it .. 3 it + 2 use buffers par, !par, par
+    k2 = kload(blk + 2 * S);
+    body(k0, blk, par);
+    k0 = kload(blk + 3 * S);
+    body(k1, blk + S, par ^ 1);
+    k1 = kload(blk + 4 * S);
+    body(k2, blk + 2 * S, par);
   }
 }
 

@@ -243,29 +243,34 @@ __device__ __forceinline__ void block_update(EncodeState<D, MBW>& st, int i, con
   st.acc[D / 16][i] = mfma_k32(ones, p, st.acc[D / 16][i]);
 }
 
-// One 32-token step (step ks of the K/V slots sK/sV).  kn0/kn1 are the next
-// step's K operands (HAS_NEXT), read by the caller from wherever that step
-// lives.  ONLINE: running max, starting from the exact column max of the
-// split's first step and raised lazily (only when a value exceeds mu + TAU,
-// so weights and sums stay finite); otherwise the shift is a bound.
+// One 32-token step (step ks of the V slot sV).  sKn / ksn locate the next
+// step's K operands (HAS_NEXT).  Operand loads are placed right after the
+// last use of the registers they replace: the next step's K after the last
+// logits of this step's K, this step's V after the previous block's pending
+// update; the pipeline registers are then overwritten in place instead of
+// copied every step.  ONLINE: running max, starting from the exact column
+// max of the split's first step and raised lazily (only when a value exceeds
+// mu + TAU, so weights and sums stay finite); otherwise the shift is a bound.
 // MASK (the split's ragged last step): tokens at or past n1 weigh zero.
 template <int D, int MBW, bool ONLINE, bool MASK, bool HAS_NEXT>
 __device__ __forceinline__ void encode_step(EncodeState<D, MBW>& st, EncodePipe<D>& pp, const __bf16* sV, int ks,
-                                            typename KOperand<D>::T kn0, typename KOperand<D>::T kn1, int sb,
-                                            int n1, int g, int c16, bf16x8 ones) {
+                                            const __bf16* sKn, int ksn, int sb, int n1, int g, int c16,
+                                            bf16x8 ones) {
   constexpr int DB = D / 16;
   constexpr float TAU = 8.0f;
-  bf16x8 v[DB];
-  load_vop<D>(sV, ks, g, c16, v);
+  if (HAS_NEXT && MBW == 1) load_kop<D>(sKn, ksn, g, c16, pp.k0, pp.k1);
 #pragma unroll
   for (int i = 0; i < MBW; ++i) {
     f32x4 s0 = pp.s0, s1 = pp.s1;
     // matrix core: next block's logits, previous block's update
-    if (i + 1 < MBW)
+    if (i + 1 < MBW) {
       block_logits<D, MBW>(st, i + 1, pp.k0, pp.k1, pp.s0, pp.s1);
-    else if (HAS_NEXT)
-      block_logits<D, MBW>(st, 0, kn0, kn1, pp.s0, pp.s1);
+      if (HAS_NEXT && i + 2 == MBW) load_kop<D>(sKn, ksn, g, c16, pp.k0, pp.k1);
+    } else if (HAS_NEXT) {
+      block_logits<D, MBW>(st, 0, pp.k0, pp.k1, pp.s0, pp.s1);
+    }
     block_update<D, MBW>(st, i == 0 ? MBW - 1 : i - 1, pp.v, pp.p, ones);
+    if (i == 0) load_vop<D>(sV, ks, g, c16, pp.v);
     // VALU: this block's weights
     if (MASK) {
 #pragma unroll
@@ -297,12 +302,6 @@ __device__ __forceinline__ void encode_step(EncodeState<D, MBW>& st, EncodePipe<
       }
     }
     pp.p = p;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) pp.v[db] = v[db];
-  }
-  if (HAS_NEXT) {
-    pp.k0 = kn0;
-    pp.k1 = kn1;
   }
 }
 
@@ -359,31 +358,24 @@ __device__ __forceinline__ void encode_tile(EncodeState<D, MBW>& st, EncodePipe<
   const int nsteps = min(R::SPT, (n1 - tb + 31) / 32);
 #pragma unroll 1
   for (int ks = 0; ks + 1 < nsteps; ++ks) {
-    if (wave_active) {
-      kop_t kn0, kn1;
-      load_kop<D>(R::template k<I>(ring), ks + 1, g, c16, kn0, kn1);
-      encode_step<D, MBW, ONLINE, false, true>(st, pp, R::template v<I>(ring), ks, kn0, kn1, tb + ks * 32, n1, g,
-                                               c16, ones);
-    }
+    if (wave_active)
+      encode_step<D, MBW, ONLINE, false, true>(st, pp, R::template v<I>(ring), ks, R::template k<I>(ring), ks + 1,
+                                               tb + ks * 32, n1, g, c16, ones);
   }
   const int ks = nsteps - 1;
   if (t + 1 < ntiles) {
     ring_open<D, NW, J1>(ring, Kp, Vp, t + 1, n0, n1, wave, lane);
     if (KNORM) kn2 = fmaxf(kn2, tile_knorm<D, NW>(R::template k<J1>(ring), tid));
-    if (wave_active) {
-      kop_t kn0, kn1;
-      load_kop<D>(R::template k<J1>(ring), 0, g, c16, kn0, kn1);
-      encode_step<D, MBW, ONLINE, false, true>(st, pp, R::template v<I>(ring), ks, kn0, kn1, tb + ks * 32, n1, g,
-                                               c16, ones);
-    }
+    if (wave_active)
+      encode_step<D, MBW, ONLINE, false, true>(st, pp, R::template v<I>(ring), ks, R::template k<J1>(ring), 0,
+                                               tb + ks * 32, n1, g, c16, ones);
   } else if (wave_active) {
-    const kop_t z{};
     if (tb + (ks + 1) * 32 <= n1)
-      encode_step<D, MBW, ONLINE, false, false>(st, pp, R::template v<I>(ring), ks, z, z, tb + ks * 32, n1, g, c16,
-                                                ones);
+      encode_step<D, MBW, ONLINE, false, false>(st, pp, R::template v<I>(ring), ks, nullptr, 0, tb + ks * 32, n1, g,
+                                                c16, ones);
     else
-      encode_step<D, MBW, ONLINE, true, false>(st, pp, R::template v<I>(ring), ks, z, z, tb + ks * 32, n1, g, c16,
-                                               ones);
+      encode_step<D, MBW, ONLINE, true, false>(st, pp, R::template v<I>(ring), ks, nullptr, 0, tb + ks * 32, n1, g,
+                                               c16, ones);
   }
 }
 
@@ -456,7 +448,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void encode_split_bf16(EncodeArgs 
   __shared__ __attribute__((aligned(16))) __bf16 ring[8 * Ring<D, NW>::TE];
   __shared__ float sRed[NW];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int g = lane >> 4, c16 = lane & 15;
   const int j = blockIdx.x;
   const int64_t lbh = blockIdx.y, bh = a.bh0 + lbh;

@@ -47,6 +47,7 @@ struct Plan {
   int nw, mbw;      // waves per workgroup and 16-latent blocks per wave (bf16 encode)
   int tpr;          // threads per latent row in the merge
   int dchunk;       // tokens per decode workgroup (bf16)
+  bool dpair;       // paired decode (two waves per token block)
   int nS;           // seed / fixed-query operand blocks (1 or H)
   size_t o_shi, o_slo, o_sqn, o_part, o_knorm, o_qhi, o_qlo, o_qnorm, o_bias, o_zt, o_qf, o_zf, total;
 };
@@ -114,8 +115,25 @@ Plan make_plan(const flarepp_desc* d, int op) {
   int tpr = 1;
   while (tpr < p.J && tpr < 64) tpr *= 2;
   p.tpr = tpr;
-  const int64_t dwg = std::max<int64_t>(1, cdiv(2 * int64_t(kComputeUnits), G));
-  p.dchunk = (int)(cdiv(cdiv(d->N, dwg), 64) * 64);
+  // decode: beyond 8 latent blocks two waves share each token block (paired
+  // kernel, four 2-wave workgroups per CU); otherwise one 4-wave workgroup
+  // per CU pair of SIMDs, 64-token rounds
+  p.dpair = nMB > 8;
+  int env_p;
+  // FLAREPP_DECODE_PAIR: 1 = paired kernel, 2 = single-wave kernel
+  if (env_int("FLAREPP_DECODE_PAIR", &env_p)) p.dpair = nMB > 8 && env_p == 1;
+  if (p.dpair) {
+    // six 2-wave workgroups per CU: three waves per SIMD at <= 168 VGPRs,
+    // all resident at once (one round)
+    int per_cu = 6;
+    int env_w;
+    if (env_int("FLAREPP_DECODE_WG_PER_CU", &env_w) && env_w > 0) per_cu = env_w;
+    const int64_t dwg = std::max<int64_t>(1, cdiv(per_cu * int64_t(kComputeUnits), G));
+    p.dchunk = (int)(cdiv(cdiv(d->N, dwg), 16) * 16);
+  } else {
+    const int64_t dwg = std::max<int64_t>(1, cdiv(2 * int64_t(kComputeUnits), G));
+    p.dchunk = (int)(cdiv(cdiv(d->N, dwg), 64) * 64);
+  }
 
   // workspace layout
   const size_t G_ = (size_t)p.G, Mp = (size_t)p.Mp, D = (size_t)p.D;
@@ -283,6 +301,26 @@ template <int D>
 flarepp_status run_decode_bf16(const Plan& p, const DecodeArgs& a, int Gc, hipStream_t st, Recorder& rec) {
   const dim3 grid((unsigned)cdiv(p.N, p.dchunk), (unsigned)Gc);
   rec.before(FLAREPP_KERNEL_DECODE, st);
+  if (p.dpair) {
+    const int mbh = (p.Mp / 16 + 1) / 2;
+    if (p.M == 2 * mbh * 16) {
+      switch (mbh) {
+        case 5: decode_pair_bf16<D, 5, false><<<grid, dim3(128), 0, st>>>(a); break;
+        case 6: decode_pair_bf16<D, 6, false><<<grid, dim3(128), 0, st>>>(a); break;
+        case 7: decode_pair_bf16<D, 7, false><<<grid, dim3(128), 0, st>>>(a); break;
+        default: decode_pair_bf16<D, 8, false><<<grid, dim3(128), 0, st>>>(a); break;
+      }
+    } else {
+      switch (mbh) {
+        case 5: decode_pair_bf16<D, 5, true><<<grid, dim3(128), 0, st>>>(a); break;
+        case 6: decode_pair_bf16<D, 6, true><<<grid, dim3(128), 0, st>>>(a); break;
+        case 7: decode_pair_bf16<D, 7, true><<<grid, dim3(128), 0, st>>>(a); break;
+        default: decode_pair_bf16<D, 8, true><<<grid, dim3(128), 0, st>>>(a); break;
+      }
+    }
+    rec.after(st);
+    return launched();
+  }
   switch (p.Mp / 16) {
     case 1: launch_decode_mb<D, 1>(a, grid, st); break;
     case 2: launch_decode_mb<D, 2>(a, grid, st); break;
