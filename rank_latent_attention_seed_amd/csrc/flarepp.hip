@@ -104,7 +104,9 @@ Plan make_plan(const flarepp_desc* d, int op) {
   p.mbw = nMB <= 4 ? 1 : 2;
   // splits are whole encode tiles (8192 or 4096 bf16 of K per tile, by wave count)
   const int tile = p.bf16 ? (p.nw == 8 ? 8192 : 4096) / p.D : 64;
-  const int64_t target = (p.bf16 ? 2 : 4) * int64_t(kComputeUnits);
+  // encode workgroups per head group: one round over the CUs (eight-wave
+  // workgroups use 128 KB of LDS, one per CU; four-wave ones fit two)
+  const int64_t target = (p.bf16 ? (p.nw == 8 ? 1 : 2) : 4) * int64_t(kComputeUnits);
   int64_t J = std::max<int64_t>(1, cdiv(target, G));
   int env_j;
   if (env_int("FLAREPP_SPLITS", &env_j)) J = env_j;
@@ -242,7 +244,7 @@ flarepp_status run_prep(const Plan& p, const void* src, bool src_bf16, int64_t s
                         int nblk, __bf16* hi, __bf16* lo, __bf16* zt, float* qn, float c, hipStream_t st,
                         Recorder& rec) {
   PrepArgs a{src, src_bf16 ? 1 : 0, src_off, src_blk, nblk, p.M, p.Mp, hi, lo, zt, qn, c};
-  const int64_t n = (int64_t)nblk * p.Mp;
+  const int64_t n = (int64_t)nblk * p.Mp * D;  // one thread per element
   rec.before(FLAREPP_KERNEL_PREP, st);
   prep_rows<D><<<dim3((unsigned)cdiv(n, 256)), dim3(256), 0, st>>>(a);
   rec.after(st);
@@ -276,9 +278,14 @@ flarepp_status run_encode_f32(const Plan& p, const EncodeF32Args& a, int Gc, hip
 
 template <int D>
 flarepp_status run_merge(const Plan& p, const MergeArgs& a, int Gc, hipStream_t st, Recorder& rec) {
+  rec.before(FLAREPP_KERNEL_MERGE, st);
+  if (p.J > 64 && p.J <= 512) {  // one row per workgroup, records held in registers
+    merge_rows256<D><<<dim3((unsigned)p.Mp, (unsigned)Gc), dim3(256), 0, st>>>(a);
+    rec.after(st);
+    return launched();
+  }
   const int rpb = 256 / p.tpr;
   const dim3 grid((unsigned)cdiv(p.Mp, rpb), (unsigned)Gc);
-  rec.before(FLAREPP_KERNEL_MERGE, st);
   switch (p.tpr) {
     case 1: merge_partials<D, 1><<<grid, dim3(256), 0, st>>>(a); break;
     case 2: merge_partials<D, 2><<<grid, dim3(256), 0, st>>>(a); break;

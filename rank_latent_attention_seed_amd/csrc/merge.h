@@ -150,6 +150,91 @@ __global__ __launch_bounds__(256) void merge_partials(MergeArgs a) {
   }
 }
 
+// The same merge with one latent row per 256-thread workgroup, for many
+// splits (128 < J <= 512): thread q holds records q and q + 256 in registers,
+// so the records are read once; the maxima, then the weighted sums, are
+// reduced over the workgroup (DPP within waves, LDS across the four).
+// Wave 0 finishes the row: lane d < D owns element d.
+template <int D>
+__global__ __launch_bounds__(256) void merge_rows256(MergeArgs a) {
+  constexpr int PS = Part<D>::kStride;
+  constexpr int NV = PS / 4;  // float4s per record
+  __shared__ float sRed[4][D + 1];
+  __shared__ float sMax[4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m = blockIdx.x;
+  const int64_t lbh = blockIdx.y, bh = a.bh0 + lbh;
+  const float* base = a.part + ((lbh * a.Mp + m) * (int64_t)a.J) * PS;
+
+  const bool h0 = tid < a.J, h1 = tid + 256 < a.J;
+  f32x4 r0[NV], r1[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    r0[v] = h0 ? *reinterpret_cast<const f32x4*>(base + (int64_t)tid * PS + 4 * v) : f32x4{0.f, 0.f, 0.f, 0.f};
+    r1[v] = h1 ? *reinterpret_cast<const f32x4*>(base + (int64_t)(tid + 256) * PS + 4 * v)
+               : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // record tail: lambda at D, mu at D + 1
+  const float mu0 = h0 ? r0[D / 4][1] : -INFINITY, mu1 = h1 ? r1[D / 4][1] : -INFINITY;
+  float mx = wave_max(fmaxf(mu0, mu1));
+  if (lane == 0) sMax[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(sMax[0], sMax[1]), fmaxf(sMax[2], sMax[3]));
+  const float w0 = h0 ? fast_exp2(mu0 - mx) : 0.0f, w1 = h1 ? fast_exp2(mu1 - mx) : 0.0f;
+#pragma unroll
+  for (int v = 0; v < D / 4; ++v) {
+    const f32x4 y = w0 * r0[v] + w1 * r1[v];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float t = wave_sum(y[e]);
+      if (lane == 0) sRed[wave][4 * v + e] = t;
+    }
+  }
+  {
+    const float t = wave_sum(w0 * r0[D / 4][0] + w1 * r1[D / 4][0]);
+    if (lane == 0) sRed[wave][D] = t;
+  }
+  float kmax2 = 0.0f;
+  if (a.bias && a.knorm && wave == 0) {
+    const float* kn = a.knorm + lbh * a.Jk;
+    for (int jj = lane; jj < a.Jk; jj += 64) kmax2 = fmaxf(kmax2, kn[jj]);
+    kmax2 = wave_max(kmax2);
+  }
+  __syncthreads();
+  if (wave != 0) return;
+
+  const bool real = m < a.M;
+  const float den = sRed[0][D] + sRed[1][D] + sRed[2][D] + sRed[3][D];
+  const int d = lane < D ? lane : 0;
+  float x = (sRed[0][d] + sRed[1][d] + sRed[2][d] + sRed[3][d]) / den;
+  if (!real || lane >= D) x = 0.0f;
+  const float nrm = sqrtf(wave_sum(x * x));
+  if (lane < D) {
+    const int64_t orow = (lbh * a.Mp + m) * D;
+    if (a.out && real) a.out[(bh * a.M + m) * D + d] = x;
+    if (a.outl && real) a.outl[(lbh * a.M + m) * D + d] = x;
+    if (a.op_hi) {
+      const float xs = x * a.c;
+      const __bf16 hi = (__bf16)xs;
+      a.op_hi[orow + d] = hi;
+      if (a.op_lo) a.op_lo[orow + d] = (__bf16)(xs - (float)hi);
+    }
+    if (a.op_zt) a.op_zt[(lbh * D + d) * (int64_t)a.Mp + m] = (__bf16)x;
+  }
+  if (lane == 0) {
+    if (a.qnorm) a.qnorm[lbh * a.Mp + m] = nrm;
+    if (a.bias) {
+      float bnd = INFINITY;
+      if (a.knorm) {
+        bnd = a.c * nrm * sqrtf(kmax2) * (1.0f + 1.0f / 4096.0f);
+        if (!(2.0f * bnd <= kBoundSpan)) bnd = INFINITY;
+      }
+      a.bias[lbh * a.Mp + m] = bnd;
+    }
+  }
+}
+
 // Operands from a caller's rows (float32 or bf16): nblk blocks of M x D rows,
 // block k starting at element src_off + k * src_blk -> [nblk][Mp][D] bf16 hi/lo
 // of c * row, [nblk][D][Mp] bf16 of the row (transposed) and row norms; rows
@@ -166,37 +251,34 @@ struct PrepArgs {
   float c;
 };
 
+// One thread per element: a row's D elements are D adjacent lanes, whose
+// squared sum gives the row norm.
 template <int D>
 __global__ __launch_bounds__(256) void prep_rows(PrepArgs a) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)a.nblk * a.Mp) return;
-  const int64_t blk = idx / a.Mp;
-  const int m = (int)(idx - blk * a.Mp);
-  float x[D];
-  float n2 = 0.0f;
-#pragma unroll
-  for (int d = 0; d < D; ++d) {
-    float v = 0.0f;
-    if (m < a.M) {
-      const int64_t s = a.src_off + blk * a.src_blk + (int64_t)m * D + d;
-      v = a.src_bf16 ? (float)reinterpret_cast<const __bf16*>(a.src)[s]
-                     : reinterpret_cast<const float*>(a.src)[s];
-    }
-    x[d] = v;
-    n2 += v * v;
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rows = (int64_t)a.nblk * a.Mp;
+  const int64_t idx = e / D;  // row (over all blocks)
+  const int d = (int)(e % D);
+  const bool live = idx < rows;  // whole rows are live or not (D divides 64)
+  const int64_t blk = live ? idx / a.Mp : 0;
+  const int m = live ? (int)(idx - blk * a.Mp) : 0;
+  float v = 0.0f;
+  if (live && m < a.M) {
+    const int64_t s = a.src_off + blk * a.src_blk + (int64_t)m * D + d;
+    v = a.src_bf16 ? (float)reinterpret_cast<const __bf16*>(a.src)[s] : reinterpret_cast<const float*>(a.src)[s];
   }
-  const int64_t orow = idx * D;
+  float n2 = v * v;
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    if (a.op_hi) {
-      const float xs = x[d] * a.c;
-      const __bf16 hi = (__bf16)xs;
-      a.op_hi[orow + d] = hi;
-      if (a.op_lo) a.op_lo[orow + d] = (__bf16)(xs - (float)hi);
-    }
-    if (a.op_zt) a.op_zt[(blk * D + d) * (int64_t)a.Mp + m] = (__bf16)x[d];
+  for (int off = D / 2; off >= 1; off >>= 1) n2 += __shfl_xor(n2, off);
+  if (!live) return;
+  if (a.op_hi) {
+    const float xs = v * a.c;
+    const __bf16 hi = (__bf16)xs;
+    a.op_hi[idx * D + d] = hi;
+    if (a.op_lo) a.op_lo[idx * D + d] = (__bf16)(xs - (float)hi);
   }
-  if (a.qnorm) a.qnorm[idx] = sqrtf(n2);
+  if (a.op_zt) a.op_zt[(blk * D + d) * (int64_t)a.Mp + m] = (__bf16)v;
+  if (a.qnorm && d == 0) a.qnorm[idx] = sqrtf(n2);
 }
 
 }  // namespace flarepp
