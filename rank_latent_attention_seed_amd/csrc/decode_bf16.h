@@ -21,7 +21,8 @@
 // the MFMA accumulator input and no per-score max is taken.  Otherwise the
 // block first takes the exact max over m in a logits-only pass.  Either way
 // the weights are the softmax up to rounding; the sum uses the same
-// bf16-rounded weights that enter Z^T P^T.  Logits are produced and consumed
+// bf16-rounded weights that enter Z^T P^T (a matrix-core product with a tile
+// of ones).  Logits are produced and consumed
 // four 16-latent blocks at a time so they stay in VGPRs.
 #pragma once
 
@@ -102,6 +103,10 @@ __global__ __launch_bounds__(256, 1) void decode_bf16(DecodeArgs a) {
   constexpr int CH = MB < 4 ? MB : 4;     // latent blocks per chunk of logits
   constexpr int NCH = (MB + CH - 1) / CH;
 
+  // A operand of the weight-sum tile: all ones, so every row of ONES P^T is
+  // the per-token sum of the same bf16 weights that enter Z^T P^T
+  const bf16x8 ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                       (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
   auto body = [&](const kop_t kb, const int blk) {
     const int tok = blk + c16;
 
@@ -131,7 +136,7 @@ __global__ __launch_bounds__(256, 1) void decode_bf16(DecodeArgs a) {
     }
     const f32x4 cinit = {sh, sh, sh, sh};
 
-    float lam = 0.0f;
+    f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
     f32x4 yacc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) yacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -167,13 +172,13 @@ __global__ __launch_bounds__(256, 1) void decode_bf16(DecodeArgs a) {
           p2 = pack_bf16(fast_exp2(L[2 * i2 + 1][0]), fast_exp2(L[2 * i2 + 1][1]));
           p3 = pack_bf16(fast_exp2(L[2 * i2 + 1][2]), fast_exp2(L[2 * i2 + 1][3]));
         }
-        lam = add_pair(p3, add_pair(p2, add_pair(p1, add_pair(p0, lam))));
         const bf16x8 pb = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 #pragma unroll
         for (int db = 0; db < DB; ++db) yacc[db] = mfma_k32(zop[kb2][db], pb, yacc[db]);
+        lacc = mfma_k32(ones, pb, lacc);
       }
     }
-    const float inv = __builtin_amdgcn_rcpf(sum_over_rows(lam));
+    const float inv = __builtin_amdgcn_rcpf(lacc[0]);
     if (tok < n1) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -284,6 +289,10 @@ __global__ __launch_bounds__(128, 2) void decode_pair_bf16(DecodeArgs a) {
     return *reinterpret_cast<const kop_t*>(Kp + (int64_t)tok * D + KL * g);
   };
 
+  // A operand of the weight-sum tile: all ones, so every row of ONES P^T is
+  // the per-token sum of the same bf16 weights that enter Z^T P^T
+  const bf16x8 ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                       (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
   auto body = [&](const kop_t kb, const int blk, const int buf) {
     const int tok = blk + c16;
 
@@ -317,7 +326,7 @@ __global__ __launch_bounds__(128, 2) void decode_pair_bf16(DecodeArgs a) {
     }
     const f32x4 cinit = {sh, sh, sh, sh};
 
-    float lam = 0.0f;
+    f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
     f32x4 yacc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) yacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -343,12 +352,12 @@ __global__ __launch_bounds__(128, 2) void decode_pair_bf16(DecodeArgs a) {
       const bf16x2 p1 = pack_bf16(fast_exp2(L[0][2]), fast_exp2(L[0][3]));
       const bf16x2 p2 = pack_bf16(fast_exp2(L[1][0]), fast_exp2(L[1][1]));
       const bf16x2 p3 = pack_bf16(fast_exp2(L[1][2]), fast_exp2(L[1][3]));
-      lam = add_pair(p3, add_pair(p2, add_pair(p1, add_pair(p0, lam))));
       const bf16x8 pb = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 #pragma unroll
       for (int db = 0; db < DB; ++db) yacc[db] = mfma_k32(zop[kb2][db], pb, yacc[db]);
+      lacc = mfma_k32(ones, pb, lacc);
     }
-    lam = sum_over_rows(lam);
+    const float lam = lacc[0];
 
     // swap: wave w2 stores d-block w2 (D = 32) or wave 0 stores all (D = 16)
     if (g == 0) sLam[buf][w2][c16] = lam;

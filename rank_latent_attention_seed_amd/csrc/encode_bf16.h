@@ -133,10 +133,13 @@ __device__ __forceinline__ void ring_barrier() {
 // write: its own bookkeeping would make every later LDS read of any ring
 // slot wait for all loads in flight, which would serialise the ring.  The
 // ring's waits are explicit (FLAREPP_WAIT_VM before each tile's barrier).
+// M0 (the LDS base of the load) is set and consumed inside the statement; the
+// compiler treats M0 as reserved and uses it nowhere else in this library
+// (tests/test_kernel_asm.py checks the generated code for that).
 __device__ __forceinline__ void dma16(const __bf16* src, const __bf16* lds_base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory");
 }
 
 // Issue the direct-to-LDS loads of one tile into slot I: the NW waves split
@@ -352,7 +355,6 @@ __device__ __forceinline__ void encode_tile(EncodeState<D, MBW>& st, EncodePipe<
                                             int tid, int wave, int lane, bool wave_active, int g, int c16,
                                             bf16x8 ones, float& kn2) {
   typedef Ring<D, NW> R;
-  typedef typename KOperand<D>::T kop_t;
   constexpr int J1 = (I + 1) & 3;
   const int tb = n0 + t * R::TN;
   const int nsteps = min(R::SPT, (n1 - tb + 31) / 32);

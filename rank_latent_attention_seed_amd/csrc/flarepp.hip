@@ -31,7 +31,6 @@ using namespace flarepp;
 namespace {
 
 constexpr int kComputeUnits = 256;                  // MI355X
-constexpr int64_t kGroupKVBytes = int64_t(128) << 20;  // K + V of one launch group
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -88,10 +87,11 @@ Plan make_plan(const flarepp_desc* d, int op) {
   p.bf16 = d->dtype == FLAREPP_BF16;
   p.c = d->scale * 1.4426950408889634f;
   p.nS = d->seed_head_stride ? p.H : 1;
-  const int elem = p.bf16 ? 2 : 4;
 
-  const int64_t kv = 2 * d->N * d->D * elem;
-  int64_t G = std::max<int64_t>(1, kGroupKVBytes / kv);
+  // All heads in one launch group by default: larger launches have shorter
+  // tails, and the split partials stay small because the split count per head
+  // shrinks with the group (one round of encode workgroups per group).
+  int64_t G = p.BH;
   int env_g;
   if (env_int("FLAREPP_HEAD_GROUP", &env_g)) G = env_g;
   G = std::min<int64_t>(G, std::min<int64_t>(p.BH, 65535));
