@@ -15,6 +15,8 @@ synchronisations; rank 0 prints one JSON line.  The line carries:
 * roofline = the dominant kernel's algorithmic HBM bytes per launch over its
   average launch duration, from HIP events recorded around every kernel by
   flarepp_route_profiled over K further steps;
+* route_over_flare = the route's time over fixed-query FLARE's (Qd := S: one
+  encode and one decode) on the same inputs;
 * cpu_baseline = the oracle (single-threaded C, fp64) on a bounded sample of
   the same problem (one head, the first 393216 tokens: ~13 s).
 
@@ -116,6 +118,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="million")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="after the timed runs, copy MIB MiB device-to-device once (a kernel of known "
+                         "traffic, for scaling hardware byte counters)")
     ap.add_argument("--cpu-sample", type=int, default=393216,
                     help="tokens of one head for the oracle baseline (0 = skip)")
     args = ap.parse_args()
@@ -181,6 +186,30 @@ def main() -> int:
     log(f"[bench] {args.steps} steps: {ms:.3f} ms/step (wall {wall:.2f} s), "
         f"{value / 1e9:.3f} G token*heads/s, {100 * mfma_frac:.1f}% of bf16 MFMA peak")
 
+    # ---- fixed-query FLARE (Qd := S: one encode, one decode) on the same
+    # inputs, K steps, for the route / FLARE time ratio
+    fbytes = fp.flarepp_workspace_size(desc, fp.OP_FLARE)
+    fws = torch.empty(max(fbytes, 1), dtype=torch.uint8, device="cuda")
+
+    def flare_step():
+        st = fp.flarepp_flare(desc, ptrs[0], ptrs[1], ptrs[2], ptrs[3], None, fws.data_ptr(), fbytes, stream)
+        if st != 0:
+            raise fp.FlareppError(st, "flarepp_flare")
+
+    for _ in range(args.warmup):
+        flare_step()
+    torch.cuda.synchronize()
+    ev = HipEvents(2)
+    ev.hip.hipEventRecord(ev.arr[0], stream)
+    for _ in range(args.steps):
+        flare_step()
+    ev.hip.hipEventRecord(ev.arr[1], stream)
+    torch.cuda.synchronize()
+    flare_ms = ev.elapsed_ms(0, 1) / args.steps
+    ev.close()
+    del fws
+    log(f"[bench] fixed-query FLARE: {flare_ms:.3f} ms/step; route / FLARE = {ms / flare_ms:.3f}")
+
     # ---- per-kernel durations: K more steps through flarepp_route_profiled
     max_l = 256
     kev = HipEvents(2 * max_l)
@@ -233,6 +262,16 @@ def main() -> int:
         "avg_launch_us": round(kstats[dom]["avg_us"], 2),
     }
 
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {args.calibrate_copy} MiB done")
+        del src, dst
+
     cpu = None
     if args.cpu_sample > 0:
         log(f"[bench] oracle baseline on {args.cpu_sample} tokens ...")
@@ -255,6 +294,8 @@ def main() -> int:
         "config": {"workload": p.name, "B": p.B, "H": p.H, "N": p.N, "M": p.M, "D": p.D,
                    "scale": p.scale, "outputs": "fp32", "global_batch": p.B, "seq_len": p.N},
         "mfma_frac_of_bf16_peak": mfma_frac,
+        "flare_fixed_query_ms_per_step": flare_ms,
+        "route_over_flare": ms / flare_ms,
         "kernels": kstats,
         "roofline": roofline,
         "cpu_baseline": cpu,
