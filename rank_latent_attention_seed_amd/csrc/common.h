@@ -40,10 +40,30 @@ __device__ __forceinline__ bf16x2 pack_bf16(float lo, float hi) {
   return r;
 }
 
-// Sum of a packed bf16 pair, accumulated in fp32: acc + p.x + p.y.
-__device__ __forceinline__ float add_pair(bf16x2 p, float acc) {
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(p, ones, acc, false);
+// Raw buffer resources: loads whose VGPR offset (plus the instruction offset)
+// is at or past num_records bytes return zeros and such stores are dropped
+// by the hardware, so a stream that ends mid-block needs no clamped
+// addresses or guarded stores.  The range check does not include the scalar
+// offset, so every offset that must be checked goes in the VGPR offset (the
+// helpers below pass a scalar offset of zero).  Word 3 selects the 32-bit
+// data format.
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+// 16- or 8-byte load at byte offset off (range-checked).
+template <typename T>
+__device__ __forceinline__ T buffer_load(__amdgpu_buffer_rsrc_t r, int off) {
+  static_assert(sizeof(T) == 16 || sizeof(T) == 8, "16- or 8-byte loads");
+  if constexpr (sizeof(T) == 16)
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  else
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+// 16-byte store at byte offset off (range-checked).
+__device__ __forceinline__ void buffer_store(f32x4 v, __amdgpu_buffer_rsrc_t r, int off) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
 }
 
 // Reductions across the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48),

@@ -91,15 +91,14 @@ __global__ __launch_bounds__(256, 1) void decode_bf16(DecodeArgs a) {
   const bool have_bound = a.qnorm != nullptr;
   const bool ragged_m = a.M < MP;
 
-  const __bf16* Kp = a.K + bh * (int64_t)a.N * D;
-  float* Yp = a.Y + bh * (int64_t)a.N * D;
-  // Branch-free loads: a token past the chunk reads the chunk's last row
-  // (its results are never stored), so loads can stay in flight across
-  // iterations.
-  auto kload = [&](int blk) {
-    const int tok = min(blk + c16, n1 - 1);
-    return *reinterpret_cast<const kop_t*>(Kp + (int64_t)tok * D + KL * g);
-  };
+  // K and Y of this workgroup's tokens as buffer resources: tokens past n1
+  // read as zeros and their stores are dropped, so loads need no clamping
+  // and stay in flight across iterations
+  const int nt = max(n1 - n0, 0);
+  const __amdgpu_buffer_rsrc_t Kr = buffer_rsrc(a.K + (bh * (int64_t)a.N + n0) * D, (uint32_t)nt * D * 2);
+  const __amdgpu_buffer_rsrc_t Yr = buffer_rsrc(a.Y + (bh * (int64_t)a.N + n0) * D, (uint32_t)nt * D * 4);
+  const int kvoff = ((wave * 16 + c16) * D + KL * g) * 2;  // blk - n0 = wave * 16 + 64 j
+  auto kload = [&](int blk) { return buffer_load<kop_t>(Kr, kvoff + (blk - n0 - wave * 16) * D * 2); };
   constexpr int CH = MB < 4 ? MB : 4;     // latent blocks per chunk of logits
   constexpr int NCH = (MB + CH - 1) / CH;
 
@@ -108,7 +107,6 @@ __global__ __launch_bounds__(256, 1) void decode_bf16(DecodeArgs a) {
   const bf16x8 ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
                        (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
   auto body = [&](const kop_t kb, const int blk) {
-    const int tok = blk + c16;
 
     // token norm -> shift
     float ss = 0.0f;
@@ -179,11 +177,9 @@ __global__ __launch_bounds__(256, 1) void decode_bf16(DecodeArgs a) {
       }
     }
     const float inv = __builtin_amdgcn_rcpf(lacc[0]);
-    if (tok < n1) {
+    const int yoff = ((blk - n0 + c16) * D + 4 * g) * 4;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        *reinterpret_cast<f32x4*>(Yp + (int64_t)tok * D + 16 * db + 4 * g) = yacc[db] * inv;
-    }
+    for (int db = 0; db < DB; ++db) buffer_store(yacc[db] * inv, Yr, yoff + 64 * db);
   };
 
   // Two 16-token blocks of K in flight ahead of the one being consumed.  The
@@ -282,19 +278,19 @@ __global__ __launch_bounds__(128, 2) void decode_pair_bf16(DecodeArgs a) {
   // whole blocks past the end) get weight zero
   const int mvalid = a.M - mb0 * 16;
 
-  const __bf16* Kp = a.K + bh * (int64_t)a.N * D;
-  float* Yp = a.Y + bh * (int64_t)a.N * D;
-  auto kload = [&](int blk) {
-    const int tok = min(blk + c16, n1 - 1);
-    return *reinterpret_cast<const kop_t*>(Kp + (int64_t)tok * D + KL * g);
-  };
+  // K and Y of this workgroup's tokens as buffer resources: tokens past n1
+  // read as zeros and their stores are dropped
+  const int nt = max(n1 - n0, 0);
+  const __amdgpu_buffer_rsrc_t Kr = buffer_rsrc(a.K + (bh * (int64_t)a.N + n0) * D, (uint32_t)nt * D * 2);
+  const __amdgpu_buffer_rsrc_t Yr = buffer_rsrc(a.Y + (bh * (int64_t)a.N + n0) * D, (uint32_t)nt * D * 4);
+  const int kvoff = (c16 * D + KL * g) * 2;
+  auto kload = [&](int blk) { return buffer_load<kop_t>(Kr, kvoff + (blk - n0) * D * 2); };
 
   // A operand of the weight-sum tile: all ones, so every row of ONES P^T is
   // the per-token sum of the same bf16 weights that enter Z^T P^T
   const bf16x8 ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
                        (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
   auto body = [&](const kop_t kb, const int blk, const int buf) {
-    const int tok = blk + c16;
 
     // token norm -> shift (identical in both waves)
     float ss = 0.0f;
@@ -361,19 +357,20 @@ __global__ __launch_bounds__(128, 2) void decode_pair_bf16(DecodeArgs a) {
 
     // swap: wave w2 stores d-block w2 (D = 32) or wave 0 stores all (D = 16)
     if (g == 0) sLam[buf][w2][c16] = lam;
+    const int yoff = ((blk - n0 + c16) * D + 4 * g) * 4;
     if (w2 == 0) {
       if (DB == 2) sY[buf][0][lane] = yacc[DB - 1];
       pair_barrier();
       const float inv = __builtin_amdgcn_rcpf(lam + sLam[buf][1][c16]);
       const f32x4 y = yacc[0] + sY[buf][1][lane];
-      if (tok < n1) *reinterpret_cast<f32x4*>(Yp + (int64_t)tok * D + 4 * g) = y * inv;
+      buffer_store(y * inv, Yr, yoff);
     } else {
       sY[buf][1][lane] = yacc[0];
       pair_barrier();
       if (DB == 2) {
         const float inv = __builtin_amdgcn_rcpf(lam + sLam[buf][0][c16]);
         const f32x4 y = yacc[DB - 1] + sY[buf][0][lane];
-        if (tok < n1) *reinterpret_cast<f32x4*>(Yp + (int64_t)tok * D + 16 + 4 * g) = y * inv;
+        buffer_store(y * inv, Yr, yoff + 64);
       }
     }
   };

@@ -61,6 +61,10 @@ bool env_int(const char* name, int* out) {
   return true;
 }
 
+// Tokens per decode workgroup at most: the workgroup's rows of Y (D <= 32
+// float32) must fit a buffer resource's 32-bit byte count.
+constexpr int64_t kMaxDecodeChunk = (int64_t(1) << 31) / (32 * 4) / 64 * 64;
+
 flarepp_status check_desc(const flarepp_desc* d) {
   if (!d) return FLAREPP_INVALID_ARG;
   if (d->B < 1 || d->H < 1 || d->N < 1 || d->M < 1 || d->D < 1) return FLAREPP_INVALID_ARG;
@@ -131,10 +135,10 @@ Plan make_plan(const flarepp_desc* d, int op) {
     int env_w;
     if (env_int("FLAREPP_DECODE_WG_PER_CU", &env_w) && env_w > 0) per_cu = env_w;
     const int64_t dwg = std::max<int64_t>(1, cdiv(per_cu * int64_t(kComputeUnits), G));
-    p.dchunk = (int)(cdiv(cdiv(d->N, dwg), 16) * 16);
+    p.dchunk = (int)std::min<int64_t>(cdiv(cdiv(d->N, dwg), 16) * 16, kMaxDecodeChunk);
   } else {
     const int64_t dwg = std::max<int64_t>(1, cdiv(2 * int64_t(kComputeUnits), G));
-    p.dchunk = (int)(cdiv(cdiv(d->N, dwg), 64) * 64);
+    p.dchunk = (int)std::min<int64_t>(cdiv(cdiv(d->N, dwg), 64) * 64, kMaxDecodeChunk);
   }
 
   // workspace layout

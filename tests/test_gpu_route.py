@@ -212,6 +212,35 @@ def test_deterministic_and_split_invariant(fp, monkeypatch):
         assert torch.equal(x, y), "head grouping changed results"
 
 
+@pytest.mark.parametrize("M", [256, 64])
+def test_writes_stay_inside_outputs(fp, M):
+    """Y, Qd and Z are written exactly: sentinel-filled space after each stays
+    untouched, and Y matches a plain call (paired and single-wave decode,
+    token counts that end mid-block and mid-workgroup)."""
+    import torch
+
+    p = inputs.random_problem(1, 3, 1001, M, 32, dtype="bf16", seed=M)
+    print(f"\n  case guard M{M}", flush=True)
+    S, K, V = to_device(p.S), to_device(p.K), to_device(p.V)
+    d = fp.desc_for(S, K, p.scale)
+    n = fp.flarepp_workspace_size(d, fp.OP_ROUTE)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    guard = 4096
+    ny, nq = p.B * p.H * p.N * p.D, p.B * p.H * p.M * p.D
+    Y = torch.full((ny + guard,), 12345.0, dtype=torch.float32, device="cuda")
+    Qd = torch.full((nq + guard,), 12345.0, dtype=torch.float32, device="cuda")
+    Z = torch.full((nq + guard,), 12345.0, dtype=torch.float32, device="cuda")
+    st = fp.flarepp_route(d, S.data_ptr(), K.data_ptr(), V.data_ptr(), Y.data_ptr(), Qd.data_ptr(),
+                          Z.data_ptr(), ws.data_ptr(), n, None)
+    assert st == 0
+    Y2 = fp.route(S, K, V, p.scale)
+    torch.cuda.synchronize()
+    for name, t, m in (("Y", Y, ny), ("Qd", Qd, nq), ("Z", Z, nq)):
+        assert bool((t[m:] == 12345.0).all()), f"{name}: write past the end"
+        assert bool(torch.isfinite(t[:m]).all())
+    assert torch.equal(Y[:ny].view_as(Y2), Y2)
+
+
 def test_outputs_only_y(fp):
     import torch
 
