@@ -95,6 +95,12 @@ class Oracle:
         lib.oracle_route.restype = ci
         lib.oracle_flare.argtypes = [i64, i64, i64, i64, i64, ci, dbl, i64, vp, vp, vp, vp, vp]
         lib.oracle_flare.restype = ci
+        lib.oracle_sdpa_backward.argtypes = [vp, ci, i64, vp, ci, vp, ci, i64, i64, i64, dbl, vp, vp, vp,
+                                             vp]
+        lib.oracle_sdpa_backward.restype = ci
+        lib.oracle_route_backward.argtypes = [i64, i64, i64, i64, i64, ci, dbl, i64, vp, vp, vp, vp, vp,
+                                              vp, vp]
+        lib.oracle_route_backward.restype = ci
         self._lib = lib
         self.path = path
 
@@ -162,6 +168,49 @@ class Oracle:
         return Z, Y
 
 
+    def sdpa_backward(self, q, k, v, s: float, dout):
+        """Gradients (dq, dk, dv) of <dout, SDPA(q, k, v, s)> (float64 arrays)."""
+        q, qt = _typed(q)
+        k, kt = _typed(k)
+        v, vt = _typed(v)
+        dout = np.ascontiguousarray(dout, dtype=np.float64)
+        nq, d = q.shape
+        nk, dv = v.shape
+        if k.shape != (nk, d) or dout.shape != (nq, dv):
+            raise ValueError("shape mismatch")
+        dq = np.zeros((nq, d))
+        dk = np.zeros((nk, d))
+        dvv = np.zeros((nk, dv))
+        rc = self._lib.oracle_sdpa_backward(_ptr(q), qt, nq, _ptr(k), kt, _ptr(v), vt, nk, d, dv,
+                                            float(s), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dvv))
+        if rc != 0:
+            raise ValueError("oracle_sdpa_backward rejected its arguments")
+        return dq, dk, dvv
+
+    def route_backward(self, S, K, V, s: float, dY):
+        """Gradients (dS, dK, dV) of <dY, Y> for the route Y(S, K, V); dS has
+        the shape of S (a shared seed block collects the gradient of every
+        (b, h)).  float64 results."""
+        K, kt = _typed(K)
+        V, vt = _typed(V)
+        S, st = _typed(S)
+        if not (kt == vt == st):
+            raise TypeError("S, K and V must share one dtype")
+        B, H, N, D = K.shape
+        M, stride = _heads(S, H, D)
+        dY = np.ascontiguousarray(dY, dtype=np.float64)
+        if dY.shape != K.shape:
+            raise ValueError("dY must be B x H x N x D")
+        dS = np.empty(S.shape, dtype=np.float64)
+        dK = np.empty(K.shape, dtype=np.float64)
+        dV = np.empty(K.shape, dtype=np.float64)
+        rc = self._lib.oracle_route_backward(B, H, N, M, D, kt, float(s), stride, _ptr(S), _ptr(K),
+                                             _ptr(V), _ptr(dY), _ptr(dS), _ptr(dK), _ptr(dV))
+        if rc != 0:
+            raise ValueError("oracle_route_backward rejected its arguments")
+        return dS, dK, dV
+
+
 _default: Oracle | None = None
 
 
@@ -184,3 +233,11 @@ def route(S, K, V, s):
 
 def flare(Q, K, V, s):
     return default().flare(Q, K, V, s)
+
+
+def sdpa_backward(q, k, v, s, dout):
+    return default().sdpa_backward(q, k, v, s, dout)
+
+
+def route_backward(S, K, V, s, dY):
+    return default().route_backward(S, K, V, s, dY)
