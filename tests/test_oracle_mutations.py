@@ -19,8 +19,10 @@ MUTATIONS = {
         "rc |= oracle_sdpa(Kbh, dtype, N, z, ORACLE_F64, qd, ORACLE_F64, M, D, D,",
     ),
     "dot_skips_first_dim": (
-        "for (int64_t e = 0; e < d; ++e)\n                dot +=",
-        "for (int64_t e = 1; e < d; ++e)\n                dot +=",
+        "for (int64_t e = 0; e < d; ++e)\n                dot += oracle_load(q, q_dtype, i * d + e) *\n"
+        "                       oracle_load(k, k_dtype, j * d + e);\n            logit[j]",
+        "for (int64_t e = 1; e < d; ++e)\n                dot += oracle_load(q, q_dtype, i * d + e) *\n"
+        "                       oracle_load(k, k_dtype, j * d + e);\n            logit[j]",
     ),
     "denominator_drops_last_key": ("denom += logit[j];", "denom += (j + 1 < nk) ? logit[j] : 0.0;"),
     "no_max_subtraction": ("logit[j] = exp(logit[j] - lmax);", "logit[j] = exp(logit[j]);"),
