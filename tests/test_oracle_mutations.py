@@ -11,8 +11,10 @@ import oracle_pins
 MUTATIONS = {
     "scale_dropped": ("logit[j] = s * dot;", "logit[j] = dot;"),
     "stage2_uses_seeds": (
-        "rc |= oracle_sdpa(qd, ORACLE_F64, M, Kbh, dtype, Vbh, dtype, N, D, D, s, z);",
-        "rc |= oracle_sdpa(Sh, dtype, M, Kbh, dtype, Vbh, dtype, N, D, D, s, z);",
+        "/* stage 2: the routing queries compress the same tokens */\n"
+        "            rc |= oracle_sdpa(qd, ORACLE_F64, M, Kbh, dtype, Vbh, dtype, N, D, D, s, z);",
+        "/* stage 2: the routing queries compress the same tokens */\n"
+        "            rc |= oracle_sdpa(Sh, dtype, M, Kbh, dtype, Vbh, dtype, N, D, D, s, z);",
     ),
     "decode_keys_values_swapped": (
         "rc |= oracle_sdpa(Kbh, dtype, N, qd, ORACLE_F64, z, ORACLE_F64, M, D, D,",
@@ -36,8 +38,12 @@ MUTATIONS = {
         "const void *Kbh = oracle_offset(K, dtype, b * N * D);\n            const void *Vbh = oracle_offset(V, dtype, b * N * D);\n            /* stage 1",
     ),
     "per_head_seeds_ignored": (
-        "const void *Sh = oracle_offset(S, dtype, h * q_head_stride);",
-        "const void *Sh = oracle_offset(S, dtype, 0);",
+        "const void *Sh = oracle_offset(S, dtype, h * q_head_stride);\n"
+        "            const void *Kbh = oracle_offset(K, dtype, bh * N * D);\n"
+        "            const void *Vbh = oracle_offset(V, dtype, bh * N * D);\n            /* stage 1",
+        "const void *Sh = oracle_offset(S, dtype, 0);\n"
+        "            const void *Kbh = oracle_offset(K, dtype, bh * N * D);\n"
+        "            const void *Vbh = oracle_offset(V, dtype, bh * N * D);\n            /* stage 1",
     ),
     "stage3_scale_is_one": (
         "rc |= oracle_sdpa(Kbh, dtype, N, qd, ORACLE_F64, z, ORACLE_F64, M, D, D,\n"
