@@ -79,7 +79,8 @@ typedef enum flarepp_op {
     FLAREPP_OP_ENCODE = 1,
     FLAREPP_OP_DECODE = 2,
     FLAREPP_OP_ROUTE = 3,
-    FLAREPP_OP_FLARE = 4
+    FLAREPP_OP_FLARE = 4,
+    FLAREPP_OP_ROUTE_BACKWARD = 5
 } flarepp_op;
 
 /* Limits of this build. */
@@ -156,6 +157,28 @@ flarepp_status flarepp_route(const flarepp_desc *desc, const void *S, const void
 flarepp_status flarepp_flare(const flarepp_desc *desc, const void *Q, const void *K,
                              const void *V, float *Y, float *Z_out, void *ws, size_t ws_bytes,
                              void *stream);
+
+/*
+ * Backward of the route: given dY (B x H x N x D fp32), the gradient of a
+ * scalar loss with respect to Y = route(S, K, V), writes the gradients
+ *     dS  (shape of S: M x D, or H x M x D with per-head seeds; a seed block
+ *          shared by several (b, h) receives the sum of their gradients),
+ *     dK, dV  (B x H x N x D),
+ * all fp32.  The forward is recomputed inside the call.  It is the chain
+ * rule through the three SDPA stages in reverse -- decode (queries K, keys
+ * Qd, values Z), encode (queries Qd), seed encode (queries S) -- with Qd's
+ * gradient collecting its two uses (encode query, decode key); for one SDPA
+ * O = softmax(s Q K^T) V with upstream dO: dV = P^T dO, dL = P o (dO V^T -
+ * rowsum(dO o O)), dQ = s dL K, dK = s dL^T Q.  The pages measure FLARE++
+ * per training step (French technical summary, "Résultats"), i.e. forward
+ * and this backward.  FLAREPP_F32 descriptors only (FLAREPP_UNSUPPORTED
+ * otherwise); float32 arithmetic.  Workspace: flarepp_workspace_size with
+ * FLAREPP_OP_ROUTE_BACKWARD.  Inputs S, K, V, dY; outputs dS, dK, dV must
+ * not overlap them, each other or the workspace.
+ */
+flarepp_status flarepp_route_backward(const flarepp_desc *desc, const void *S, const void *K,
+                                      const void *V, const float *dY, float *dS, float *dK,
+                                      float *dV, void *ws, size_t ws_bytes, void *stream);
 
 /* Kernel kinds reported by flarepp_route_profiled. */
 typedef enum flarepp_kernel_kind {

@@ -25,6 +25,7 @@
 #include "encode_bf16.h"
 #include "f32_path.h"
 #include "merge.h"
+#include "backward_f32.h"
 
 using namespace flarepp;
 
@@ -41,12 +42,15 @@ struct Plan {
   int B, H, N, M, D, Mp;
   bool bf16;
   float c;          // scale * log2(e)
+  float s;          // scale
   int G;            // heads per launch group
   int J, chunk;     // splits of N and tokens per split (encode)
   int nw, mbw;      // waves per workgroup and 16-latent blocks per wave (bf16 encode)
   int tpr;          // threads per latent row in the merge
   int dchunk;       // tokens per decode workgroup (bf16)
   bool dpair;       // paired decode (two waves per token block)
+  // backward (float32) workspace regions
+  size_t o_lse1, o_lse2, o_tlse, o_tdel, o_dz, o_dq3, o_dq, o_del;
   int nS;           // seed / fixed-query operand blocks (1 or H)
   size_t o_shi, o_slo, o_sqn, o_part, o_knorm, o_qhi, o_qlo, o_qnorm, o_bias, o_zt, o_qf, o_zf, total;
 };
@@ -90,6 +94,7 @@ Plan make_plan(const flarepp_desc* d, int op) {
   p.Mp = (int)cdiv(d->M, 16) * 16;
   p.bf16 = d->dtype == FLAREPP_BF16;
   p.c = d->scale * 1.4426950408889634f;
+  p.s = d->scale;
   p.nS = d->seed_head_stride ? p.H : 1;
 
   // All heads in one launch group by default: larger launches have shorter
@@ -146,6 +151,7 @@ Plan make_plan(const flarepp_desc* d, int op) {
   const size_t opnd = Mp * D * 2;  // one bf16 Mp x D block
   const bool route = op == FLAREPP_OP_ROUTE, seed = op == FLAREPP_OP_SEED_ENCODE;
   const bool enc = op == FLAREPP_OP_ENCODE, dec = op == FLAREPP_OP_DECODE, flare = op == FLAREPP_OP_FLARE;
+  const bool bwd = op == FLAREPP_OP_ROUTE_BACKWARD;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -155,7 +161,20 @@ Plan make_plan(const flarepp_desc* d, int op) {
   const size_t none = SIZE_MAX;
   p.o_shi = p.o_slo = p.o_sqn = p.o_part = p.o_knorm = p.o_qhi = p.o_qlo = p.o_qnorm = p.o_bias =
       p.o_zt = p.o_qf = p.o_zf = none;
-  if (p.bf16) {
+  p.o_lse1 = p.o_lse2 = p.o_tlse = p.o_tdel = p.o_dz = p.o_dq3 = p.o_dq = p.o_del = none;
+  if (bwd) {  // float32 only (checked by the entry point)
+    p.o_part = take(G_ * p.J * Mp * std::max<size_t>(D + 4, 2 * D) * 4);
+    p.o_qf = take(G_ * p.M * D * 4);
+    p.o_zf = take(G_ * p.M * D * 4);
+    p.o_lse1 = take(G_ * Mp * 4);
+    p.o_lse2 = take(G_ * Mp * 4);
+    p.o_tlse = take(G_ * (size_t)p.N * 4);
+    p.o_tdel = take(G_ * (size_t)p.N * 4);
+    p.o_dz = take(G_ * p.M * D * 4);
+    p.o_dq3 = take(G_ * p.M * D * 4);
+    p.o_dq = take(G_ * p.M * D * 4);
+    p.o_del = take(G_ * Mp * 4);
+  } else if (p.bf16) {
     if (route || seed || flare) {
       p.o_shi = take(p.nS * opnd);
       p.o_slo = take(p.nS * opnd);
@@ -554,6 +573,170 @@ flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in
   return FLAREPP_OK;
 }
 
+// Backward of the route (float32): the forward's stages 1 and 2 with their
+// log-sum-exp statistics, then per stage a token pass (dK, dV) and a latent
+// pass (split partials of the latent gradients) with their reduction, in
+// reverse order.
+template <int D>
+flarepp_status run_backward(const Plan& p, const float* S, const float* K, const float* V, const float* dY,
+                            float* dS, float* dK, float* dV, void* ws, hipStream_t st) {
+  Recorder rec;
+  const int64_t MD = (int64_t)p.M * D, HMD = (int64_t)p.H * MD;
+  const int64_t seed_h = p.nS > 1 ? MD : 0;
+  const int nz = (int)cdiv((int64_t)p.nS * MD, 256);
+  fill_zero<<<nz, 256, 0, st>>>(dS, (int64_t)p.nS * MD);
+  FLAREPP_TRY(launched());
+  float* qf = at<float>(ws, p.o_qf);
+  float* zf = at<float>(ws, p.o_zf);
+  float* part = at<float>(ws, p.o_part);
+  float* dz = at<float>(ws, p.o_dz);
+  float* dq3 = at<float>(ws, p.o_dq3);
+  float* dq = at<float>(ws, p.o_dq);
+  float* del = at<float>(ws, p.o_del);
+  for (int64_t g0 = 0; g0 < p.BH; g0 += p.G) {
+    const int Gc = (int)std::min<int64_t>(p.G, p.BH - g0);
+    // ---- forward stages 1 and 2 with statistics
+    auto encode = [&](const float* q, int64_t sb, int64_t sh, int64_t off, float* outl, float* lse) {
+      EncodeF32Args e{};
+      e.q = q;
+      e.q_sb = sb;
+      e.q_sh = sh;
+      e.q_off = off;
+      e.K = K;
+      e.V = V;
+      e.part = part;
+      e.H = p.H;
+      e.N = p.N;
+      e.M = p.M;
+      e.Mp = p.Mp;
+      e.J = p.J;
+      e.chunk = p.chunk;
+      e.bh0 = g0;
+      e.c = p.c;
+      FLAREPP_TRY(run_encode_f32<D>(p, e, Gc, st, rec, FLAREPP_KERNEL_ENCODE));
+      MergeArgs m = merge_args(p, ws, g0);
+      m.outl = outl;
+      m.lse = lse;
+      return run_merge<D>(p, m, Gc, st, rec);
+    };
+    FLAREPP_TRY(encode(S, 0, seed_h, 0, qf, at<float>(ws, p.o_lse1)));
+    FLAREPP_TRY(encode(qf, HMD, MD, g0 * MD, zf, at<float>(ws, p.o_lse2)));
+
+    const dim3 tok_grid((unsigned)cdiv(p.N, 256), (unsigned)Gc);
+    const dim3 lat_grid((unsigned)p.J, (unsigned)Gc, (unsigned)cdiv(p.M, 256));
+    auto reduce = [&](int R, int field0, const float* add_to, float* out, const float* dot_with, float* delta,
+                      int seed_blocks) {
+      BwdReduceArgs r{part, p.J, R, field0, p.M, p.Mp, Gc, p.H, g0, add_to, out, dot_with, delta, seed_blocks};
+      const int64_t rows = (int64_t)(seed_blocks ? seed_blocks : Gc) * p.M;
+      bwd_reduce<D><<<(unsigned)cdiv(rows * D, 256), 256, 0, st>>>(r);
+      return launched();
+    };
+    // ---- stage 3 (decode): queries K, keys Qd, values Z
+    {
+      BwdTokArgs t{};
+      t.q = qf;
+      t.q_sb = HMD;
+      t.q_sh = MD;
+      t.q_off = g0 * MD;
+      t.lat2 = zf;
+      t.K = K;
+      t.dY = dY;
+      t.dK = dK;
+      t.tlse = at<float>(ws, p.o_tlse);
+      t.tdelta = at<float>(ws, p.o_tdel);
+      t.H = p.H;
+      t.N = p.N;
+      t.M = p.M;
+      t.Mp = p.Mp;
+      t.bh0 = g0;
+      t.c = p.c;
+      t.s = p.s;
+      t.acc_dk = 0;
+      t.acc_dv = 0;
+      bwd_decode_tokens<D><<<tok_grid, 256, 0, st>>>(t);
+      FLAREPP_TRY(launched());
+      BwdLatArgs l{};
+      l.q = qf;
+      l.q_sb = HMD;
+      l.q_sh = MD;
+      l.q_off = g0 * MD;
+      l.lat2 = zf;
+      l.K = K;
+      l.dY = dY;
+      l.tlse = t.tlse;
+      l.tdelta = t.tdelta;
+      l.part = part;
+      l.H = p.H;
+      l.N = p.N;
+      l.M = p.M;
+      l.Mp = p.Mp;
+      l.J = p.J;
+      l.chunk = p.chunk;
+      l.bh0 = g0;
+      l.c = p.c;
+      l.s = p.s;
+      bwd_latents<D, true><<<lat_grid, 256, 0, st>>>(l);
+      FLAREPP_TRY(launched());
+      FLAREPP_TRY(reduce(2 * D, D, nullptr, dz, zf, del, 0));    // dZ, delta_2 = <dZ, Z>
+      FLAREPP_TRY(reduce(2 * D, 0, nullptr, dq3, nullptr, nullptr, 0));  // dQd from the decode
+    }
+    // ---- stages 2 and 1 (encode, seed encode)
+    auto enc_stage = [&](const float* q, int64_t sb, int64_t sh, int64_t off, const float* dO, const float* lse,
+                         int accumulate_dv) {
+      BwdTokArgs t{};
+      t.q = q;
+      t.q_sb = sb;
+      t.q_sh = sh;
+      t.q_off = off;
+      t.lat2 = dO;
+      t.lse = lse;
+      t.delta = del;
+      t.K = K;
+      t.V = V;
+      t.dK = dK;
+      t.dV = dV;
+      t.H = p.H;
+      t.N = p.N;
+      t.M = p.M;
+      t.Mp = p.Mp;
+      t.bh0 = g0;
+      t.c = p.c;
+      t.s = p.s;
+      t.acc_dk = 1;  // the decode wrote dK first
+      t.acc_dv = accumulate_dv;
+      bwd_encode_tokens<D><<<tok_grid, 256, 0, st>>>(t);
+      FLAREPP_TRY(launched());
+      BwdLatArgs l{};
+      l.q = q;
+      l.q_sb = sb;
+      l.q_sh = sh;
+      l.q_off = off;
+      l.lat2 = dO;
+      l.lse = lse;
+      l.delta = del;
+      l.K = K;
+      l.V = V;
+      l.part = part;
+      l.H = p.H;
+      l.N = p.N;
+      l.M = p.M;
+      l.Mp = p.Mp;
+      l.J = p.J;
+      l.chunk = p.chunk;
+      l.bh0 = g0;
+      l.c = p.c;
+      l.s = p.s;
+      bwd_latents<D, false><<<lat_grid, 256, 0, st>>>(l);
+      return launched();
+    };
+    FLAREPP_TRY(enc_stage(qf, HMD, MD, g0 * MD, dz, at<float>(ws, p.o_lse2), 0));
+    FLAREPP_TRY(reduce(D, 0, dq3, dq, qf, del, 0));  // dQd = encode + decode parts, delta_1 = <dQd, Qd>
+    FLAREPP_TRY(enc_stage(S, 0, seed_h, 0, dq, at<float>(ws, p.o_lse1), 1));
+    FLAREPP_TRY(reduce(D, 0, nullptr, dS, nullptr, nullptr, p.nS));
+  }
+  return FLAREPP_OK;
+}
+
 flarepp_status dispatch(const Plan& p, Stage stage, const void* S, const float* Qd_in, const float* Z_in,
                         const void* K, const void* V, float* Y, float* Qd_out, float* Z_out, void* ws,
                         void* stream, Recorder* recorder = nullptr) {
@@ -634,7 +817,8 @@ const char* flarepp_status_string(flarepp_status s) {
 flarepp_status flarepp_workspace_size(const flarepp_desc* desc, int32_t op, size_t* bytes) {
   if (!bytes) return FLAREPP_INVALID_ARG;
   FLAREPP_TRY(check_desc(desc));
-  if (op < FLAREPP_OP_SEED_ENCODE || op > FLAREPP_OP_FLARE) return FLAREPP_INVALID_ARG;
+  if (op < FLAREPP_OP_SEED_ENCODE || op > FLAREPP_OP_ROUTE_BACKWARD) return FLAREPP_INVALID_ARG;
+  if (op == FLAREPP_OP_ROUTE_BACKWARD && desc->dtype != FLAREPP_F32) return FLAREPP_UNSUPPORTED;
   *bytes = make_plan(desc, op).total;
   return FLAREPP_OK;
 }
@@ -707,6 +891,26 @@ flarepp_status flarepp_flare(const flarepp_desc* desc, const void* Q, const void
   Plan p;
   FLAREPP_TRY(prologue(desc, FLAREPP_OP_FLARE, in, inb, 3, out, outb, req, 2, ws, ws_bytes, &p));
   return dispatch(p, kFlare, Q, nullptr, nullptr, K, V, Y, nullptr, Z_out, ws, stream);
+}
+
+flarepp_status flarepp_route_backward(const flarepp_desc* desc, const void* S, const void* K, const void* V,
+                                      const float* dY, float* dS, float* dK, float* dV, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  FLAREPP_TRY(check_desc(desc));
+  if (desc->dtype != FLAREPP_F32) return FLAREPP_UNSUPPORTED;
+  const Sizes z = sizes(desc);
+  const void* in[4] = {S, K, V, dY};
+  const size_t inb[4] = {z.s, z.kv, z.kv, z.y};
+  const void* out[3] = {dS, dK, dV};
+  const size_t outb[3] = {z.s, z.kv, z.kv};
+  const bool req[3] = {true, true, true};
+  Plan p;
+  FLAREPP_TRY(prologue(desc, FLAREPP_OP_ROUTE_BACKWARD, in, inb, 4, out, outb, req, 3, ws, ws_bytes, &p));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const float *Sf = static_cast<const float*>(S), *Kf = static_cast<const float*>(K),
+              *Vf = static_cast<const float*>(V);
+  if (p.D == 16) return run_backward<16>(p, Sf, Kf, Vf, dY, dS, dK, dV, ws, st);
+  return run_backward<32>(p, Sf, Kf, Vf, dY, dS, dK, dV, ws, st);
 }
 
 flarepp_status flarepp_route_profiled(const flarepp_desc* desc, const void* S, const void* K, const void* V,

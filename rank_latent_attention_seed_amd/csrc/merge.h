@@ -34,6 +34,7 @@ struct MergeArgs {
   int Jk;
   float* bias;         // [G][Mp] bound c ||row|| max||K|| for the next encode (+inf if unsafe), or null
   float c;
+  float* lse;          // [G][Mp] log-sum-exp of the row's softmax, log2 units (mu + log2 lambda), or null
 };
 
 // Largest exponent span (log2 units) a bound-shifted softmax may cover: with
@@ -138,6 +139,7 @@ __global__ __launch_bounds__(256) void merge_partials(MergeArgs a) {
     if (a.op_zt) a.op_zt[(lbh * D + d) * (int64_t)a.Mp + m] = (__bf16)v;
   }
   if (q == 0) {
+    if (a.lse) a.lse[lbh * a.Mp + m] = mx + log2f(den);
     if (a.qnorm) a.qnorm[lbh * a.Mp + m] = nrm;
     if (a.bias) {
       float bnd = INFINITY;
@@ -223,6 +225,7 @@ __global__ __launch_bounds__(256) void merge_rows256(MergeArgs a) {
     if (a.op_zt) a.op_zt[(lbh * D + d) * (int64_t)a.Mp + m] = (__bf16)x;
   }
   if (lane == 0) {
+    if (a.lse) a.lse[lbh * a.Mp + m] = mx + log2f(den);
     if (a.qnorm) a.qnorm[lbh * a.Mp + m] = nrm;
     if (a.bias) {
       float bnd = INFINITY;

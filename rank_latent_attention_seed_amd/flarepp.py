@@ -18,13 +18,13 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(_PKG, "libflarepp.so")
 
 F32, BF16 = 0, 1
-OP_SEED_ENCODE, OP_ENCODE, OP_DECODE, OP_ROUTE, OP_FLARE = range(5)
+OP_SEED_ENCODE, OP_ENCODE, OP_DECODE, OP_ROUTE, OP_FLARE, OP_ROUTE_BACKWARD = range(6)
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE_TOO_SMALL", 4: "ALIASING",
           5: "HIP_ERROR"}
 ABI_VERSION = 1
 SYMBOLS = ("flarepp_abi_version", "flarepp_status_string", "flarepp_workspace_size",
            "flarepp_seed_encode", "flarepp_encode", "flarepp_decode", "flarepp_route",
-           "flarepp_flare", "flarepp_route_profiled")
+           "flarepp_flare", "flarepp_route_backward", "flarepp_route_profiled")
 KERNEL_KINDS = {0: "prep", 1: "seed_encode", 2: "encode", 3: "merge", 4: "decode"}
 
 
@@ -76,6 +76,8 @@ def _lib():
         lib.flarepp_route.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.flarepp_flare.restype = ctypes.c_int
         lib.flarepp_flare.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.flarepp_route_backward.restype = ctypes.c_int
+        lib.flarepp_route_backward.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.flarepp_route_profiled.restype = ctypes.c_int
         lib.flarepp_route_profiled.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                                ctypes.POINTER(vp), ctypes.POINTER(i32), i32,
@@ -136,6 +138,11 @@ def flarepp_route(desc, S, K, V, Y, Qd_out, Z_out, ws, ws_bytes, stream) -> int:
 
 def flarepp_flare(desc, Q, K, V, Y, Z_out, ws, ws_bytes, stream) -> int:
     return _lib().flarepp_flare(ctypes.byref(desc), Q, K, V, Y, Z_out, ws, ws_bytes, stream)
+
+
+def flarepp_route_backward(desc, S, K, V, dY, dS, dK, dV, ws, ws_bytes, stream) -> int:
+    return _lib().flarepp_route_backward(ctypes.byref(desc), S, K, V, dY, dS, dK, dV, ws, ws_bytes,
+                                         stream)
 
 
 def flarepp_route_profiled(desc, S, K, V, Y, Qd_out, Z_out, ws, ws_bytes, stream, events, kinds,
@@ -227,6 +234,22 @@ def route(S, K, V, scale, *, with_intermediates=False, workspace: Workspace | No
     _check(flarepp_route(desc, _ptr(S), _ptr(K), _ptr(V), _ptr(Y), _ptr(Qd), _ptr(Z), _ptr(buf),
                          nbytes, _stream(stream)), "flarepp_route")
     return (Y, Qd, Z) if with_intermediates else Y
+
+
+def route_backward(S, K, V, scale, dY, *, workspace: Workspace | None = None, stream=None):
+    """(dS, dK, dV): gradients of <dY, route(S, K, V)> for float32 GPU tensors."""
+    torch = _torch()
+    for t, n in ((S, "S"), (K, "K"), (V, "V"), (dY, "dY")):
+        _require(t, n)
+    desc = desc_for(S, K, scale)
+    dS = torch.empty_like(S, dtype=torch.float32)
+    dK = torch.empty(K.shape, dtype=torch.float32, device=K.device)
+    dV = torch.empty(K.shape, dtype=torch.float32, device=K.device)
+    ws = workspace or Workspace(K.device)
+    buf, nbytes = ws.get(flarepp_workspace_size(desc, OP_ROUTE_BACKWARD))
+    _check(flarepp_route_backward(desc, _ptr(S), _ptr(K), _ptr(V), _ptr(dY), _ptr(dS), _ptr(dK),
+                                  _ptr(dV), _ptr(buf), nbytes, _stream(stream)), "flarepp_route_backward")
+    return dS, dK, dV
 
 
 def seed_encode(S, K, V, scale, *, workspace: Workspace | None = None, stream=None):

@@ -49,7 +49,7 @@ def ws_status(d, op):
 
 
 @pytest.mark.parametrize("op", range(5))
-def test_workspace_sizes(op):
+def test_workspace_sizes(op):  # forward ops (the backward is float32 only: test_backward_validation)
     st, n_bf16 = ws_status(desc(), op)
     assert st == OK
     st, n_f32 = ws_status(desc(dtype=fp.F32), op)
@@ -117,3 +117,24 @@ def test_stage_validation():
     assert fp.flarepp_flare(d, addr(0), None, addr(2), addr(3), None, addr(6), n, None) == INVALID_ARG
     assert fp.library().flarepp_route(None, addr(0), addr(1), addr(2), addr(3), None, None, addr(6),
                                       1 << 30, None) == INVALID_ARG
+
+
+def test_backward_validation():
+    d = desc(dtype=fp.F32)
+    st, n = ws_status(d, fp.OP_ROUTE_BACKWARD)
+    assert st == OK and n > 0
+    assert ws_status(desc(), fp.OP_ROUTE_BACKWARD)[0] == UNSUPPORTED  # float32 only
+
+    def bwd(dd=d, S=addr(0), K=addr(1), V=addr(2), dY=addr(3), dS=addr(4), dK=addr(5), dV=addr(7),
+            ws=addr(6), nbytes=n):
+        return fp.flarepp_route_backward(dd, S, K, V, dY, dS, dK, dV, ws, nbytes, None)
+
+    # every case fails validation on the host, before any HIP call
+    assert bwd(dd=desc()) == UNSUPPORTED
+    assert bwd(dS=None) == INVALID_ARG
+    assert bwd(dY=None) == INVALID_ARG
+    assert bwd(dV=addr(7) + 4) == INVALID_ARG      # misaligned
+    assert bwd(nbytes=n - 1) == WS_SMALL
+    assert bwd(dK=addr(2) + 256) == ALIASING       # output inside V
+    assert bwd(dV=addr(5) + 16) == ALIASING        # two outputs overlap
+    assert bwd(dS=addr(6)) == ALIASING             # output inside the workspace
