@@ -15,6 +15,10 @@ synchronisations; rank 0 prints one JSON line.  The line carries:
 * roofline = the dominant kernel's algorithmic HBM bytes per launch over its
   average launch duration, from HIP events recorded around every kernel by
   flarepp_route_profiled over K further steps;
+* backward = flarepp_route_backward (float32) on the same shapes: time per
+  call and algorithmic TFLOP/s (30 M D flops per token*head: five D-length
+  contractions per latent-token pair in each of the three stages) against
+  the float32 vector peak;
 * route_over_flare = the route's time over fixed-query FLARE's (Qd := S: one
   encode and one decode) on the same inputs;
 * cpu_baseline = the oracle (single-threaded C, fp64) on a bounded sample of
@@ -37,6 +41,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, published
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "rank_latent_attention_seed_amd", "csrc")
 
@@ -118,6 +123,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="million")
+    ap.add_argument("--backward-steps", type=int, default=3,
+                    help="timed calls of the float32 backward on the same shapes (0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the timed runs, copy MIB MiB device-to-device once (a kernel of known "
                          "traffic, for scaling hardware byte counters)")
@@ -262,6 +269,48 @@ def main() -> int:
         "avg_launch_us": round(kstats[dom]["avg_us"], 2),
     }
 
+    # ---- backward of the route (float32): the same workload with float32
+    # copies of the (bf16-valued) inputs and a seeded upstream dY
+    bwd = None
+    if args.backward_steps > 0:
+        Sf, Kf, Vf = S.float(), K.float(), V.float()
+        del Y
+        dY = torch.randn(Kf.shape, generator=torch.Generator(device="cuda").manual_seed(7), device="cuda")
+        dS, dK, dV = torch.empty_like(Sf), torch.empty_like(Kf), torch.empty_like(Vf)
+        bdesc = fp.desc_for(Sf, Kf, p.scale)
+        bbytes = fp.flarepp_workspace_size(bdesc, fp.OP_ROUTE_BACKWARD)
+        bws = torch.empty(max(bbytes, 1), dtype=torch.uint8, device="cuda")
+        bptr = [t.data_ptr() for t in (Sf, Kf, Vf, dY, dS, dK, dV)]
+
+        def bstep():
+            st = fp.flarepp_route_backward(bdesc, *bptr, bws.data_ptr(), bbytes, stream)
+            if st != 0:
+                raise fp.FlareppError(st, "flarepp_route_backward")
+
+        bstep()
+        torch.cuda.synchronize()
+        ev = HipEvents(2)
+        ev.hip.hipEventRecord(ev.arr[0], stream)
+        for _ in range(args.backward_steps):
+            bstep()
+        ev.hip.hipEventRecord(ev.arr[1], stream)
+        torch.cuda.synchronize()
+        bms = ev.elapsed_ms(0, 1) / args.backward_steps
+        ev.close()
+        bflops = 30.0 * p.M * p.D * tokens_heads  # 3 stages x 10 M D (logits, dP, dV, dQ, dK)
+        btf = bflops / (bms * 1e-3) / 1e12
+        bwd = {
+            "op": "flarepp_route_backward", "dtype": "f32",
+            "workload": f"{p.name} shapes, float32 copies of the inputs, seeded dY",
+            "steps": args.backward_steps, "ms_per_step": bms, "value": tokens_heads / (bms * 1e-3),
+            "unit": "token*heads/s",
+            "roofline": {"bound": "alu", "achieved": round(btf, 2), "peak": FP32_VECTOR_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(btf / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": None,
+                         "algorithmic_flops_per_step": bflops},
+        }
+        log(f"[bench] backward (float32): {bms:.2f} ms/step, {btf:.2f} TFLOP/s algorithmic")
+        del Sf, Kf, Vf, dY, dS, dK, dV, bws
+
     if args.calibrate_copy > 0:
         n = args.calibrate_copy << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
@@ -298,6 +347,7 @@ def main() -> int:
         "route_over_flare": ms / flare_ms,
         "kernels": kstats,
         "roofline": roofline,
+        "backward": bwd,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
