@@ -80,7 +80,8 @@ typedef enum flarepp_op {
     FLAREPP_OP_DECODE = 2,
     FLAREPP_OP_ROUTE = 3,
     FLAREPP_OP_FLARE = 4,
-    FLAREPP_OP_ROUTE_BACKWARD = 5
+    FLAREPP_OP_ROUTE_BACKWARD = 5,
+    FLAREPP_OP_SPECTRUM = 6
 } flarepp_op;
 
 /* Limits of this build. */
@@ -179,6 +180,28 @@ flarepp_status flarepp_flare(const flarepp_desc *desc, const void *Q, const void
 flarepp_status flarepp_route_backward(const flarepp_desc *desc, const void *S, const void *K,
                                       const void *V, const float *dY, float *dS, float *dK,
                                       float *dV, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Spectrum of each head's mixing matrix W = W_dec W_enc (N x N, rank <= M):
+ * its nonzero eigenvalues are those of the M x M product W_enc W_dec, where
+ * W_enc = softmax over tokens of s Qd K^T (the encode weights) and W_dec =
+ * softmax over latents of s K Qd^T (the decode weights), Qd the route's
+ * synthesised queries -- the eigendecomposition in O(M^3 + M^2 N) of the
+ * FLARE summary ("FLARE: Fast Low-rank Attention Routing Engine", section
+ * "Спектральный анализ"; mixing matrix: "Матрица коммуникации низкого
+ * ранга").  Because both factors are softmaxes of the same logits, W_enc
+ * W_dec is similar to the symmetric positive semidefinite G = F F^T with
+ * F_mn = sqrt(W_enc[m, n] W_dec[n, m]); its eigenvalues are real, in
+ * [0, 1], the largest 1.  The library forms G on the GPU (O(M^2 N)) and finds
+ * its eigenvalues by cyclic Jacobi (float32; off-diagonal norm below 1e-6 of
+ * the whole, or 30 sweeps).
+ *   eig (output): B x H x M fp32, each head's eigenvalues by decreasing value.
+ *   sym_out (optional output): B x H x M x M fp32, the matrix G.
+ * Both dtypes; workspace: flarepp_workspace_size with FLAREPP_OP_SPECTRUM.
+ */
+flarepp_status flarepp_spectrum(const flarepp_desc *desc, const void *S, const void *K,
+                                const void *V, float *eig, float *sym_out, void *ws,
+                                size_t ws_bytes, void *stream);
 
 /* Kernel kinds reported by flarepp_route_profiled. */
 typedef enum flarepp_kernel_kind {

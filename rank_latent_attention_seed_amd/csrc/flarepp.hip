@@ -26,6 +26,7 @@
 #include "f32_path.h"
 #include "merge.h"
 #include "backward_f32.h"
+#include "spectral.h"
 
 using namespace flarepp;
 
@@ -51,6 +52,9 @@ struct Plan {
   bool dpair;       // paired decode (two waves per token block)
   // backward (float32) workspace regions
   size_t o_lse1, o_lse2, o_tlse, o_tdel, o_dz, o_dq3, o_dq, o_del;
+  // spectrum: Gram partials [G][Jg][M][M] over Jg token splits of gchunk, and the reduced [G][M][M]
+  int Jg, gchunk;
+  size_t o_gpart, o_mat;
   int nS;           // seed / fixed-query operand blocks (1 or H)
   size_t o_shi, o_slo, o_sqn, o_part, o_knorm, o_qhi, o_qlo, o_qnorm, o_bias, o_zt, o_qf, o_zf, total;
 };
@@ -152,6 +156,13 @@ Plan make_plan(const flarepp_desc* d, int op) {
   const bool route = op == FLAREPP_OP_ROUTE, seed = op == FLAREPP_OP_SEED_ENCODE;
   const bool enc = op == FLAREPP_OP_ENCODE, dec = op == FLAREPP_OP_DECODE, flare = op == FLAREPP_OP_FLARE;
   const bool bwd = op == FLAREPP_OP_ROUTE_BACKWARD;
+  const bool spec = op == FLAREPP_OP_SPECTRUM;
+  {
+    int64_t jg = std::max<int64_t>(1, cdiv(int64_t(kComputeUnits), G));
+    jg = std::min<int64_t>(jg, cdiv(d->N, 32));
+    p.gchunk = (int)(cdiv(cdiv(d->N, jg), 32) * 32);
+    p.Jg = (int)cdiv(d->N, p.gchunk);
+  }
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -162,6 +173,7 @@ Plan make_plan(const flarepp_desc* d, int op) {
   p.o_shi = p.o_slo = p.o_sqn = p.o_part = p.o_knorm = p.o_qhi = p.o_qlo = p.o_qnorm = p.o_bias =
       p.o_zt = p.o_qf = p.o_zf = none;
   p.o_lse1 = p.o_lse2 = p.o_tlse = p.o_tdel = p.o_dz = p.o_dq3 = p.o_dq = p.o_del = none;
+  p.o_gpart = p.o_mat = none;
   if (bwd) {  // float32 only (checked by the entry point)
     p.o_part = take(G_ * p.J * Mp * std::max<size_t>(D + 4, 2 * D) * 4);
     p.o_qf = take(G_ * p.M * D * 4);
@@ -175,19 +187,19 @@ Plan make_plan(const flarepp_desc* d, int op) {
     p.o_dq = take(G_ * p.M * D * 4);
     p.o_del = take(G_ * Mp * 4);
   } else if (p.bf16) {
-    if (route || seed || flare) {
+    if (route || seed || flare || spec) {
       p.o_shi = take(p.nS * opnd);
       p.o_slo = take(p.nS * opnd);
       if (flare) p.o_sqn = take(p.nS * Mp * 4);
     }
     if (!dec) p.o_part = take(G_ * p.J * Mp * (D + 4) * 4);
-    if (route) p.o_knorm = take(G_ * p.J * 4);
-    if (route || enc || dec) {
+    if (route || spec) p.o_knorm = take(G_ * p.J * 4);
+    if (route || enc || dec || spec) {
       p.o_qhi = take(G_ * opnd);
       p.o_qlo = take(G_ * opnd);
     }
-    if (route || dec) p.o_qnorm = take(G_ * Mp * 4);
-    if (route) p.o_bias = take(G_ * Mp * 4);
+    if (route || dec || spec) p.o_qnorm = take(G_ * Mp * 4);
+    if (route || spec) p.o_bias = take(G_ * Mp * 4);
     if (route || dec || flare) p.o_zt = take(G_ * opnd);
   } else {
     if (!dec) p.o_part = take(G_ * p.J * Mp * (D + 4) * 4);
@@ -196,6 +208,13 @@ Plan make_plan(const flarepp_desc* d, int op) {
       p.o_zf = take(G_ * p.M * D * 4);
     }
     if (flare) p.o_zf = take(G_ * p.M * D * 4);
+  }
+  if (spec) {
+    if (p.o_qf == none) p.o_qf = take(G_ * p.M * D * 4);
+    p.o_lse2 = take(G_ * Mp * 4);
+    p.o_tlse = take(G_ * (size_t)p.N * 4);
+    p.o_gpart = take(G_ * p.Jg * (size_t)p.M * p.M * 4);
+    p.o_mat = take(G_ * (size_t)p.M * p.M * 4);
   }
   p.total = off;
   return p;
@@ -409,7 +428,30 @@ EncodeArgs encode_args(const Plan& p, void* ws, const void* K, const void* V, in
 
 // ---------------------------------------------------------------- stages --
 
-enum Stage { kSeed, kEncode, kDecode, kRoute, kFlare };
+enum Stage { kSeed, kEncode, kDecode, kRoute, kFlare, kSpectrum };
+
+// Spectrum of one launch group (stages 1 and 2 already ran: Qd rows in the
+// o_qf staging buffer, the encode's log-sum-exp in o_lse2).
+template <int D, typename KT>
+flarepp_status run_spectral(const Plan& p, const void* K, int64_t g0, int Gc, void* ws, float* eig, float* sym_out,
+                            hipStream_t st) {
+  float* qf = at<float>(ws, p.o_qf);
+  float* tlse = at<float>(ws, p.o_tlse);
+  float* gpart = at<float>(ws, p.o_gpart);
+  float* mat = at<float>(ws, p.o_mat);
+  SpecTokArgs t{qf, K, tlse, p.H, p.N, p.M, g0, p.c};
+  spectral_tokens<D, KT><<<dim3((unsigned)cdiv(p.N, 256), (unsigned)Gc), 256, 0, st>>>(t);
+  FLAREPP_TRY(launched());
+  SpecGramArgs g{qf, K, at<float>(ws, p.o_lse2), tlse, gpart, p.H, p.N, p.M, p.Mp, p.Jg, p.gchunk, g0, p.c};
+  spectral_gram<D, KT><<<dim3((unsigned)p.Jg, (unsigned)Gc), 1024, 0, st>>>(g);
+  FLAREPP_TRY(launched());
+  SpecReduceArgs r{gpart, mat, sym_out, Gc, p.Jg, p.M, g0};
+  spectral_reduce<<<(unsigned)cdiv((int64_t)Gc * p.M * p.M, 256), 256, 0, st>>>(r);
+  FLAREPP_TRY(launched());
+  JacobiArgs j{mat, eig, p.M, 30, g0, 1e-6f};
+  jacobi_eigvals<<<(unsigned)Gc, 256, 0, st>>>(j);
+  return launched();
+}
 
 template <int D>
 flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in, const float* Z_in,
@@ -420,7 +462,7 @@ flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in
   if (p.bf16) {
     __bf16* shi = at<__bf16>(ws, p.o_shi);
     __bf16* slo = at<__bf16>(ws, p.o_slo);
-    if (stage == kSeed || stage == kRoute || stage == kFlare)
+    if (stage == kSeed || stage == kRoute || stage == kFlare || stage == kSpectrum)
       FLAREPP_TRY(run_prep<D>(p, S, true, 0, seed_h, p.nS, shi, slo, nullptr, at<float>(ws, p.o_sqn), p.c, st, rec));
     for (int64_t g0 = 0; g0 < p.BH; g0 += p.G) {
       const int Gc = (int)std::min<int64_t>(p.G, p.BH - g0);
@@ -428,7 +470,8 @@ flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in
       __bf16* qlo = at<__bf16>(ws, p.o_qlo);
       __bf16* zt = at<__bf16>(ws, p.o_zt);
       float* qnorm = at<float>(ws, p.o_qnorm);
-      if (stage == kSeed || stage == kRoute || stage == kFlare) {
+      const bool routed = stage == kRoute || stage == kSpectrum;  // stages 1 and 2 as in the route
+      if (stage == kSeed || routed || stage == kFlare) {
         EncodeArgs e = encode_args(p, ws, K, V, g0);
         e.q_hi = shi;
         e.q_lo = slo;
@@ -436,7 +479,7 @@ flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in
         e.q_sh = p.nS > 1 ? MpD : 0;
         e.q_off = 0;
         e.knorm = at<float>(ws, p.o_knorm);
-        if (stage == kRoute)
+        if (routed)
           FLAREPP_TRY((run_encode_bf16<D, true, false>(p, e, Gc, st, rec, FLAREPP_KERNEL_SEED_ENCODE)));
         else
           FLAREPP_TRY((run_encode_bf16<D, false, false>(p, e, Gc, st, rec, FLAREPP_KERNEL_SEED_ENCODE)));
@@ -446,7 +489,8 @@ flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in
           m.op_zt = zt;
         } else {
           m.out = Qd_out;
-          if (stage == kRoute) {
+          if (stage == kSpectrum) m.outl = at<float>(ws, p.o_qf);
+          if (routed) {
             m.op_hi = qhi;
             m.op_lo = qlo;
             m.qnorm = qnorm;
@@ -459,23 +503,26 @@ flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in
       }
       if (stage == kEncode)
         FLAREPP_TRY(run_prep<D>(p, Qd_in, false, g0 * MD, MD, Gc, qhi, qlo, nullptr, nullptr, p.c, st, rec));
-      if (stage == kEncode || stage == kRoute) {
+      if (stage == kEncode || routed) {
         EncodeArgs e = encode_args(p, ws, K, V, g0);
         e.q_hi = qhi;
         e.q_lo = qlo;
         e.q_sb = (int64_t)p.H * MpD;
         e.q_sh = MpD;
         e.q_off = g0 * MpD;
-        e.bias = stage == kRoute ? at<float>(ws, p.o_bias) : nullptr;
-        if (stage == kRoute)
+        e.bias = routed ? at<float>(ws, p.o_bias) : nullptr;
+        if (routed)
           FLAREPP_TRY((run_encode_bf16<D, false, true>(p, e, Gc, st, rec, FLAREPP_KERNEL_ENCODE)));
         else
           FLAREPP_TRY((run_encode_bf16<D, false, false>(p, e, Gc, st, rec, FLAREPP_KERNEL_ENCODE)));
         MergeArgs m = merge_args(p, ws, g0);
-        m.out = Z_out;
+        m.out = stage == kSpectrum ? nullptr : Z_out;  // (Z_out carries the spectrum's matrix output)
         if (stage == kRoute) m.op_zt = zt;
+        if (stage == kSpectrum) m.lse = at<float>(ws, p.o_lse2);
         FLAREPP_TRY(run_merge<D>(p, m, Gc, st, rec));
       }
+      if (stage == kSpectrum)  // Y carries the eigenvalue output, Z_out the optional matrix
+        FLAREPP_TRY((run_spectral<D, __bf16>(p, K, g0, Gc, ws, Y, Z_out, st)));
       if (stage == kDecode) {
         FLAREPP_TRY(run_prep<D>(p, Qd_in, false, g0 * MD, MD, Gc, qhi, qlo, nullptr, qnorm, p.c, st, rec));
         FLAREPP_TRY(run_prep<D>(p, Z_in, false, g0 * MD, MD, Gc, nullptr, nullptr, zt, nullptr, p.c, st, rec));
@@ -518,7 +565,8 @@ flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in
   float* zf = at<float>(ws, p.o_zf);
   for (int64_t g0 = 0; g0 < p.BH; g0 += p.G) {
     const int Gc = (int)std::min<int64_t>(p.G, p.BH - g0);
-    auto encode = [&](const float* q, int64_t sb, int64_t sh, int64_t off, float* out, float* outl, int kind) {
+    auto encode = [&](const float* q, int64_t sb, int64_t sh, int64_t off, float* out, float* outl, int kind,
+                      float* lse = nullptr) {
       EncodeF32Args e{};
       e.q = q;
       e.q_sb = sb;
@@ -539,6 +587,7 @@ flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in
       MergeArgs m = merge_args(p, ws, g0);
       m.out = out;
       m.outl = outl;
+      m.lse = lse;
       return run_merge<D>(p, m, Gc, st, rec);
     };
     auto decode = [&](const float* q, int64_t qsb, int64_t qsh, int64_t qoff, const float* z, int64_t zsb,
@@ -567,6 +616,12 @@ flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in
       case kFlare:
         FLAREPP_TRY(encode(Sf, 0, seed_h, 0, Z_out, zf, FLAREPP_KERNEL_ENCODE));
         FLAREPP_TRY(decode(Sf, 0, seed_h, 0, zf, HMD, MD, g0 * MD));
+        break;
+      case kSpectrum:
+        FLAREPP_TRY(encode(Sf, 0, seed_h, 0, nullptr, qf, FLAREPP_KERNEL_SEED_ENCODE));
+        FLAREPP_TRY(encode(qf, HMD, MD, g0 * MD, nullptr, nullptr, FLAREPP_KERNEL_ENCODE,
+                           at<float>(ws, p.o_lse2)));
+        FLAREPP_TRY((run_spectral<D, float>(p, K, g0, Gc, ws, Y, Z_out, st)));
         break;
     }
   }
@@ -817,7 +872,7 @@ const char* flarepp_status_string(flarepp_status s) {
 flarepp_status flarepp_workspace_size(const flarepp_desc* desc, int32_t op, size_t* bytes) {
   if (!bytes) return FLAREPP_INVALID_ARG;
   FLAREPP_TRY(check_desc(desc));
-  if (op < FLAREPP_OP_SEED_ENCODE || op > FLAREPP_OP_ROUTE_BACKWARD) return FLAREPP_INVALID_ARG;
+  if (op < FLAREPP_OP_SEED_ENCODE || op > FLAREPP_OP_SPECTRUM) return FLAREPP_INVALID_ARG;
   if (op == FLAREPP_OP_ROUTE_BACKWARD && desc->dtype != FLAREPP_F32) return FLAREPP_UNSUPPORTED;
   *bytes = make_plan(desc, op).total;
   return FLAREPP_OK;
@@ -891,6 +946,21 @@ flarepp_status flarepp_flare(const flarepp_desc* desc, const void* Q, const void
   Plan p;
   FLAREPP_TRY(prologue(desc, FLAREPP_OP_FLARE, in, inb, 3, out, outb, req, 2, ws, ws_bytes, &p));
   return dispatch(p, kFlare, Q, nullptr, nullptr, K, V, Y, nullptr, Z_out, ws, stream);
+}
+
+flarepp_status flarepp_spectrum(const flarepp_desc* desc, const void* S, const void* K, const void* V, float* eig,
+                                float* sym_out, void* ws, size_t ws_bytes, void* stream) {
+  FLAREPP_TRY(check_desc(desc));
+  const Sizes z = sizes(desc);
+  const size_t ne = (size_t)desc->B * desc->H * desc->M * 4;
+  const void* in[3] = {S, K, V};
+  const size_t inb[3] = {z.s, z.kv, z.kv};
+  const void* out[2] = {eig, sym_out};
+  const size_t outb[2] = {ne, ne * (size_t)desc->M};
+  const bool req[2] = {true, false};
+  Plan p;
+  FLAREPP_TRY(prologue(desc, FLAREPP_OP_SPECTRUM, in, inb, 3, out, outb, req, 2, ws, ws_bytes, &p));
+  return dispatch(p, kSpectrum, S, nullptr, nullptr, K, V, eig, nullptr, sym_out, ws, stream);
 }
 
 flarepp_status flarepp_route_backward(const flarepp_desc* desc, const void* S, const void* K, const void* V,

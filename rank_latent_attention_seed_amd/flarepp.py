@@ -18,13 +18,13 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(_PKG, "libflarepp.so")
 
 F32, BF16 = 0, 1
-OP_SEED_ENCODE, OP_ENCODE, OP_DECODE, OP_ROUTE, OP_FLARE, OP_ROUTE_BACKWARD = range(6)
+OP_SEED_ENCODE, OP_ENCODE, OP_DECODE, OP_ROUTE, OP_FLARE, OP_ROUTE_BACKWARD, OP_SPECTRUM = range(7)
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE_TOO_SMALL", 4: "ALIASING",
           5: "HIP_ERROR"}
 ABI_VERSION = 1
 SYMBOLS = ("flarepp_abi_version", "flarepp_status_string", "flarepp_workspace_size",
            "flarepp_seed_encode", "flarepp_encode", "flarepp_decode", "flarepp_route",
-           "flarepp_flare", "flarepp_route_backward", "flarepp_route_profiled")
+           "flarepp_flare", "flarepp_route_backward", "flarepp_spectrum", "flarepp_route_profiled")
 KERNEL_KINDS = {0: "prep", 1: "seed_encode", 2: "encode", 3: "merge", 4: "decode"}
 
 
@@ -78,6 +78,8 @@ def _lib():
         lib.flarepp_flare.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.flarepp_route_backward.restype = ctypes.c_int
         lib.flarepp_route_backward.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.flarepp_spectrum.restype = ctypes.c_int
+        lib.flarepp_spectrum.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.flarepp_route_profiled.restype = ctypes.c_int
         lib.flarepp_route_profiled.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                                ctypes.POINTER(vp), ctypes.POINTER(i32), i32,
@@ -138,6 +140,10 @@ def flarepp_route(desc, S, K, V, Y, Qd_out, Z_out, ws, ws_bytes, stream) -> int:
 
 def flarepp_flare(desc, Q, K, V, Y, Z_out, ws, ws_bytes, stream) -> int:
     return _lib().flarepp_flare(ctypes.byref(desc), Q, K, V, Y, Z_out, ws, ws_bytes, stream)
+
+
+def flarepp_spectrum(desc, S, K, V, eig, sym_out, ws, ws_bytes, stream) -> int:
+    return _lib().flarepp_spectrum(ctypes.byref(desc), S, K, V, eig, sym_out, ws, ws_bytes, stream)
 
 
 def flarepp_route_backward(desc, S, K, V, dY, dS, dK, dV, ws, ws_bytes, stream) -> int:
@@ -250,6 +256,24 @@ def route_backward(S, K, V, scale, dY, *, workspace: Workspace | None = None, st
     _check(flarepp_route_backward(desc, _ptr(S), _ptr(K), _ptr(V), _ptr(dY), _ptr(dS), _ptr(dK),
                                   _ptr(dV), _ptr(buf), nbytes, _stream(stream)), "flarepp_route_backward")
     return dS, dK, dV
+
+
+def spectrum(S, K, V, scale, *, with_matrix=False, workspace: Workspace | None = None, stream=None):
+    """Eigenvalues (B x H x M, decreasing) of each head's W_enc W_dec; with
+    with_matrix also the symmetric matrix G similar to it (B x H x M x M)."""
+    torch = _torch()
+    for t, n in ((S, "S"), (K, "K"), (V, "V")):
+        _require(t, n)
+    desc = desc_for(S, K, scale)
+    B, H, N, D = K.shape
+    M = desc.M
+    eig = torch.empty((B, H, M), dtype=torch.float32, device=K.device)
+    G = torch.empty((B, H, M, M), dtype=torch.float32, device=K.device) if with_matrix else None
+    ws = workspace or Workspace(K.device)
+    buf, nbytes = ws.get(flarepp_workspace_size(desc, OP_SPECTRUM))
+    _check(flarepp_spectrum(desc, _ptr(S), _ptr(K), _ptr(V), _ptr(eig), _ptr(G), _ptr(buf), nbytes,
+                            _stream(stream)), "flarepp_spectrum")
+    return (eig, G) if with_matrix else eig
 
 
 def seed_encode(S, K, V, scale, *, workspace: Workspace | None = None, stream=None):

@@ -138,3 +138,21 @@ def test_backward_validation():
     assert bwd(dK=addr(2) + 256) == ALIASING       # output inside V
     assert bwd(dV=addr(5) + 16) == ALIASING        # two outputs overlap
     assert bwd(dS=addr(6)) == ALIASING             # output inside the workspace
+
+
+def test_spectrum_validation():
+    for dt in (fp.BF16, fp.F32):
+        st, n = ws_status(desc(dtype=dt), fp.OP_SPECTRUM)
+        assert st == OK and n > 0
+    d = desc()
+    n = ws_status(d, fp.OP_SPECTRUM)[1]
+
+    def spec(eig=addr(4), sym=addr(5), ws=addr(6), nbytes=n, K=addr(1)):
+        return fp.flarepp_spectrum(d, addr(0), K, addr(2), eig, sym, ws, nbytes, None)
+
+    # every case fails validation on the host, before any HIP call
+    assert spec(eig=None) == INVALID_ARG
+    assert spec(K=None) == INVALID_ARG
+    assert spec(nbytes=n - 1) == WS_SMALL
+    assert spec(eig=addr(1) + 64) == ALIASING        # output inside K
+    assert spec(sym=addr(4) + 16) == ALIASING        # outputs overlap
