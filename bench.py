@@ -19,6 +19,9 @@ synchronisations; rank 0 prints one JSON line.  The line carries:
   call and algorithmic TFLOP/s (30 M D flops per token*head: five D-length
   contractions per latent-token pair in each of the three stages) against
   the float32 vector peak;
+* spectrum = flarepp_spectrum on the same inputs: time per call (forming the
+  M x M matrix over all tokens and its Jacobi eigenvalues) and the mean of
+  the four largest eigenvalues per head;
 * route_over_flare = the route's time over fixed-query FLARE's (Qd := S: one
   encode and one decode) on the same inputs;
 * cpu_baseline = the oracle (single-threaded C, fp64) on a bounded sample of
@@ -125,6 +128,8 @@ def main() -> int:
     ap.add_argument("--workload", default="million")
     ap.add_argument("--backward-steps", type=int, default=3,
                     help="timed calls of the float32 backward on the same shapes (0 = skip)")
+    ap.add_argument("--spectrum-steps", type=int, default=2,
+                    help="timed calls of the mixing-matrix spectrum on the same inputs (0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the timed runs, copy MIB MiB device-to-device once (a kernel of known "
                          "traffic, for scaling hardware byte counters)")
@@ -311,6 +316,38 @@ def main() -> int:
         log(f"[bench] backward (float32): {bms:.2f} ms/step, {btf:.2f} TFLOP/s algorithmic")
         del Sf, Kf, Vf, dY, dS, dK, dV, bws
 
+    # ---- spectrum of every head's mixing matrix (bf16 inputs as the route)
+    spec = None
+    if args.spectrum_steps > 0:
+        eig = torch.empty((p.B, p.H, p.M), dtype=torch.float32, device="cuda")
+        sbytes = fp.flarepp_workspace_size(desc, fp.OP_SPECTRUM)
+        sws = torch.empty(max(sbytes, 1), dtype=torch.uint8, device="cuda")
+
+        def sstep():
+            st = fp.flarepp_spectrum(desc, ptrs[0], ptrs[1], ptrs[2], eig.data_ptr(), None, sws.data_ptr(),
+                                     sbytes, stream)
+            if st != 0:
+                raise fp.FlareppError(st, "flarepp_spectrum")
+
+        sstep()
+        torch.cuda.synchronize()
+        ev = HipEvents(2)
+        ev.hip.hipEventRecord(ev.arr[0], stream)
+        for _ in range(args.spectrum_steps):
+            sstep()
+        ev.hip.hipEventRecord(ev.arr[1], stream)
+        torch.cuda.synchronize()
+        sms = ev.elapsed_ms(0, 1) / args.spectrum_steps
+        ev.close()
+        sflops = 2.0 * p.M * p.M * tokens_heads  # the M x M product F F^T over all tokens
+        stf = sflops / (sms * 1e-3) / 1e12
+        top = eig[:, :, :4].mean(dim=(0, 1)).tolist()
+        spec = {"op": "flarepp_spectrum", "ms_per_step": sms, "steps": args.spectrum_steps,
+                "gram_tflops": round(stf, 2), "fp32_vector_peak_tflops": FP32_VECTOR_PEAK_TFLOPS,
+                "mean_top4_eigenvalues": [round(x, 6) for x in top]}
+        log(f"[bench] spectrum: {sms:.2f} ms/step, Gram {stf:.2f} TFLOP/s; mean top eigenvalues {top}")
+        del sws, eig
+
     if args.calibrate_copy > 0:
         n = args.calibrate_copy << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
@@ -348,6 +385,7 @@ def main() -> int:
         "kernels": kstats,
         "roofline": roofline,
         "backward": bwd,
+        "spectrum": spec,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
