@@ -176,6 +176,7 @@ struct EncodeState {
   kop_t qh[MBW], ql[MBW];
   f32x4 cb[MBW];
   float mu[MBW];
+  float qn2[MBW];  // ||c Q_m||^2 of the lane's latent (from the hi + lo operand)
   f32x4 acc[D / 16 + 1][MBW];
 };
 
@@ -308,16 +309,19 @@ __device__ __forceinline__ void encode_step(EncodeState<D, MBW>& st, EncodePipe<
   }
 }
 
-// Largest squared key norm among the tile's tokens seen by this thread
-// (the 16-byte chunks of the K tile are spread over the workgroup; the
-// chunks of one row sit in adjacent lanes).
-template <int D, int NW>
-__device__ __forceinline__ float tile_knorm(const __bf16* sK, int tid) {
+// Largest squared key norm among the tokens of the K tile in slot I whose
+// 16-byte chunks this lane loaded itself (the chunks of one token row are
+// loaded by adjacent lanes), valid as soon as this wave's loads of the tile
+// have landed.
+template <int D, int NW, int I>
+__device__ __forceinline__ float own_knorm(const __bf16* ring, int wave, int lane) {
+  typedef Ring<D, NW> R;
   constexpr int U = D / 8;
   float best = 0.0f;
 #pragma unroll
-  for (int h = 0; h < Ring<D, NW>::DI; ++h) {
-    const bf16x8 x = *reinterpret_cast<const bf16x8*>(sK + (tid + 64 * NW * h) * 8);
+  for (int i = 0; i < R::DI; ++i) {
+    const int blk = wave * R::DI + i;
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(R::template k<I>(const_cast<__bf16*>(ring)) + blk * 512 + 8 * lane);
     float ss = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -331,6 +335,9 @@ __device__ __forceinline__ float tile_knorm(const __bf16* sK, int tid) {
   return best;
 }
 
+// s_waitcnt lgkmcnt(0) (vmcnt and expcnt not waited on).
+constexpr uint32_t kEncWaitLgkm0 = 0xF | (0x7 << 4) | (0x3 << 14);
+
 // Ring protocol.  Tile u+2's loads are issued at the barrier that opens tile
 // u; before it a wave waits for its own loads of tile u (those of tile u+1
 // may still be in flight), so every wave's part of tile u has landed once all
@@ -338,22 +345,46 @@ __device__ __forceinline__ float tile_knorm(const __bf16* sK, int tid) {
 // step of tile u-1, which still reads tile u-1 and (for the next step's K
 // operands) tile u; the slot refilled there, (u+2) & 3, held tile u-2, which
 // every wave has finished reading.
-template <int D, int NW, int I>
-__device__ __forceinline__ void ring_open(__bf16* ring, const __bf16* Kp, const __bf16* Vp, int u, int n0, int n1,
-                                          int wave, int lane) {
+//
+// TNORM: the barrier also publishes the largest squared key norm of tile u.
+// Each wave reduces the norms of the chunks it loaded itself (landed after
+// its wait) and stores the result in sKm[u & 1][wave] before the barrier;
+// after it every wave takes the maximum over the NW entries.  Two buffers
+// suffice: the entries of tile u are read right after the barrier that opens
+// it, and rewritten (for tile u + 2) only after the next barrier.
+template <int D, int NW, int I, bool TNORM>
+__device__ __forceinline__ float ring_open(__bf16* ring, float* sKm, const __bf16* Kp, const __bf16* Vp, int u,
+                                           int n0, int n1, int wave, int lane) {
   constexpr int kWait = Ring<D, NW>::kDma;
   FLAREPP_WAIT_VM(kWait);
+  float* slot = sKm + (u & 1) * NW;
+  if (TNORM) {
+    const float part = wave_max(own_knorm<D, NW, I>(ring, wave, lane));
+    if (lane == 0) slot[wave] = part;
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kEncWaitLgkm0);  // the entry is in LDS before the barrier
+  }
   ring_barrier();
   tile_dma<D, NW, (I + 2) & 3>(ring, Kp, Vp, n0 + (u + 2) * Ring<D, NW>::TN, n1, wave, lane);
+  float km2 = 0.0f;
+  if (TNORM) {
+    km2 = slot[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) km2 = fmaxf(km2, slot[w]);
+  }
+  return km2;
 }
 
 // Tile t in slot I (already opened): its steps, the last of which opens tile
-// t+1 (if any) and starts that tile's first logits.
-template <int D, int NW, int MBW, bool KNORM, bool ONLINE, int I>
-__device__ __forceinline__ void encode_tile(EncodeState<D, MBW>& st, EncodePipe<D>& pp, __bf16* ring,
-                                            const __bf16* Kp, const __bf16* Vp, int t, int n0, int n1, int ntiles,
-                                            int tid, int wave, int lane, bool wave_active, int g, int c16,
-                                            bf16x8 ones, float& kn2) {
+// t+1 (if any) and starts that tile's first logits.  CHECK: every step
+// compares its scores with the running max (encode_step's online rule).
+// With TNORM, km2 holds the largest squared key norm of tile t on entry and
+// that of tile t+1 on exit.
+template <int D, int NW, int MBW, bool TNORM, bool CHECK, int I>
+__device__ __forceinline__ void encode_tile_steps(EncodeState<D, MBW>& st, EncodePipe<D>& pp, __bf16* ring,
+                                                  float* sKm, const __bf16* Kp, const __bf16* Vp, int t, int n0,
+                                                  int n1, int ntiles, int wave, int lane, bool wave_active, int g,
+                                                  int c16, bf16x8 ones, float& km2) {
   typedef Ring<D, NW> R;
   constexpr int J1 = (I + 1) & 3;
   const int tb = n0 + t * R::TN;
@@ -361,32 +392,69 @@ __device__ __forceinline__ void encode_tile(EncodeState<D, MBW>& st, EncodePipe<
 #pragma unroll 1
   for (int ks = 0; ks + 1 < nsteps; ++ks) {
     if (wave_active)
-      encode_step<D, MBW, ONLINE, false, true>(st, pp, R::template v<I>(ring), ks, R::template k<I>(ring), ks + 1,
-                                               tb + ks * 32, n1, g, c16, ones);
+      encode_step<D, MBW, CHECK, false, true>(st, pp, R::template v<I>(ring), ks, R::template k<I>(ring), ks + 1,
+                                              tb + ks * 32, n1, g, c16, ones);
   }
   const int ks = nsteps - 1;
   if (t + 1 < ntiles) {
-    ring_open<D, NW, J1>(ring, Kp, Vp, t + 1, n0, n1, wave, lane);
-    if (KNORM) kn2 = fmaxf(kn2, tile_knorm<D, NW>(R::template k<J1>(ring), tid));
+    km2 = ring_open<D, NW, J1, TNORM>(ring, sKm, Kp, Vp, t + 1, n0, n1, wave, lane);
     if (wave_active)
-      encode_step<D, MBW, ONLINE, false, true>(st, pp, R::template v<I>(ring), ks, R::template k<J1>(ring), 0,
-                                               tb + ks * 32, n1, g, c16, ones);
+      encode_step<D, MBW, CHECK, false, true>(st, pp, R::template v<I>(ring), ks, R::template k<J1>(ring), 0,
+                                              tb + ks * 32, n1, g, c16, ones);
   } else if (wave_active) {
     if (tb + (ks + 1) * 32 <= n1)
-      encode_step<D, MBW, ONLINE, false, false>(st, pp, R::template v<I>(ring), ks, nullptr, 0, tb + ks * 32, n1, g,
-                                                c16, ones);
-    else
-      encode_step<D, MBW, ONLINE, true, false>(st, pp, R::template v<I>(ring), ks, nullptr, 0, tb + ks * 32, n1, g,
+      encode_step<D, MBW, CHECK, false, false>(st, pp, R::template v<I>(ring), ks, nullptr, 0, tb + ks * 32, n1, g,
                                                c16, ones);
+    else
+      encode_step<D, MBW, CHECK, true, false>(st, pp, R::template v<I>(ring), ks, nullptr, 0, tb + ks * 32, n1, g,
+                                              c16, ones);
   }
 }
 
-template <int D, int NW, int MBW, bool KNORM, bool ONLINE>
-__device__ __forceinline__ void encode_tiles(EncodeState<D, MBW>& st, __bf16* ring, const __bf16* Kp,
-                                             const __bf16* Vp, int n0, int n1, int tid, int wave, int lane,
+// Tile rule of the online path.  A score of latent m in a tile is at most
+// ||c Q_m|| max_n ||K_n|| - mu_m (Cauchy-Schwarz, log2 units, maximum over
+// the tile's tokens); when that bound is at most TAU_SKIP for every latent of
+// the wave, no weight of the tile can exceed 2^TAU_SKIP (sums stay far from
+// the float range), and the per-step comparison with the running max is
+// skipped for the whole tile.  Otherwise (or for non-finite norms) every
+// step checks.
+template <int D, int MBW>
+__device__ __forceinline__ bool tile_needs_check(const EncodeState<D, MBW>& st, float km2) {
+  constexpr float TAU_SKIP = 32.0f;
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < MBW; ++i) {
+    // ||c Q_m|| sqrt(km2) <= mu_m + TAU_SKIP, squared (both sides >= 0)
+    const float lim = st.mu[i] + TAU_SKIP;
+    bad |= !(lim >= 0.0f && st.qn2[i] * km2 <= lim * lim);
+  }
+  return __builtin_amdgcn_ballot_w64(bad) != 0;
+}
+
+template <int D, int NW, int MBW, bool KNORM, bool ONLINE, bool SKIP, int I>
+__device__ __forceinline__ void encode_tile(EncodeState<D, MBW>& st, EncodePipe<D>& pp, __bf16* ring, float* sKm,
+                                            const __bf16* Kp, const __bf16* Vp, int t, int n0, int n1, int ntiles,
+                                            int wave, int lane, bool wave_active, int g, int c16, bf16x8 ones,
+                                            float& km2, float& kn2) {
+  constexpr bool TNORM = KNORM || (ONLINE && SKIP);
+  if (KNORM) kn2 = fmaxf(kn2, km2);
+  if (ONLINE && (!SKIP || tile_needs_check<D, MBW>(st, km2)))
+    encode_tile_steps<D, NW, MBW, TNORM, true, I>(st, pp, ring, sKm, Kp, Vp, t, n0, n1, ntiles, wave, lane,
+                                                  wave_active, g, c16, ones, km2);
+  else
+    encode_tile_steps<D, NW, MBW, TNORM, false, I>(st, pp, ring, sKm, Kp, Vp, t, n0, n1, ntiles, wave, lane,
+                                                   wave_active, g, c16, ones, km2);
+}
+
+// SKIP: the online path applies the tile rule (tile_needs_check); otherwise
+// every step of the online path checks.
+template <int D, int NW, int MBW, bool KNORM, bool ONLINE, bool SKIP>
+__device__ __forceinline__ void encode_tiles(EncodeState<D, MBW>& st, __bf16* ring, float* sKm, const __bf16* Kp,
+                                             const __bf16* Vp, int n0, int n1, int wave, int lane,
                                              bool wave_active, int g, int c16, float& kn2) {
   typedef Ring<D, NW> R;
   constexpr int DB = D / 16;
+  constexpr bool TNORM = KNORM || (ONLINE && SKIP);
   const int ntiles = (n1 - n0 + R::TN - 1) / R::TN;
   // A operand of the lambda tile: row 0 all ones
   const __bf16 one = c16 == 0 ? (__bf16)1.0f : (__bf16)0.0f;
@@ -398,8 +466,7 @@ __device__ __forceinline__ void encode_tiles(EncodeState<D, MBW>& st, __bf16* ri
 
   tile_dma<D, NW, 0>(ring, Kp, Vp, n0, n1, wave, lane);
   tile_dma<D, NW, 1>(ring, Kp, Vp, n0 + R::TN, n1, wave, lane);
-  ring_open<D, NW, 0>(ring, Kp, Vp, 0, n0, n1, wave, lane);
-  if (KNORM) kn2 = fmaxf(kn2, tile_knorm<D, NW>(R::template k<0>(ring), tid));
+  float km2 = ring_open<D, NW, 0, TNORM>(ring, sKm, Kp, Vp, 0, n0, n1, wave, lane);
   if (wave_active) {
     load_kop<D>(R::template k<0>(ring), 0, g, c16, pp.k0, pp.k1);
     if (ONLINE) {
@@ -422,17 +489,17 @@ __device__ __forceinline__ void encode_tiles(EncodeState<D, MBW>& st, __bf16* ri
     block_logits<D, MBW>(st, 0, pp.k0, pp.k1, pp.s0, pp.s1);
   }
   for (int t = 0; t < ntiles; t += 4) {
-    encode_tile<D, NW, MBW, KNORM, ONLINE, 0>(st, pp, ring, Kp, Vp, t, n0, n1, ntiles, tid, wave, lane,
-                                              wave_active, g, c16, ones, kn2);
+    encode_tile<D, NW, MBW, KNORM, ONLINE, SKIP, 0>(st, pp, ring, sKm, Kp, Vp, t, n0, n1, ntiles, wave, lane,
+                                              wave_active, g, c16, ones, km2, kn2);
     if (t + 1 >= ntiles) break;
-    encode_tile<D, NW, MBW, KNORM, ONLINE, 1>(st, pp, ring, Kp, Vp, t + 1, n0, n1, ntiles, tid, wave, lane,
-                                              wave_active, g, c16, ones, kn2);
+    encode_tile<D, NW, MBW, KNORM, ONLINE, SKIP, 1>(st, pp, ring, sKm, Kp, Vp, t + 1, n0, n1, ntiles, wave, lane,
+                                              wave_active, g, c16, ones, km2, kn2);
     if (t + 2 >= ntiles) break;
-    encode_tile<D, NW, MBW, KNORM, ONLINE, 2>(st, pp, ring, Kp, Vp, t + 2, n0, n1, ntiles, tid, wave, lane,
-                                              wave_active, g, c16, ones, kn2);
+    encode_tile<D, NW, MBW, KNORM, ONLINE, SKIP, 2>(st, pp, ring, sKm, Kp, Vp, t + 2, n0, n1, ntiles, wave, lane,
+                                              wave_active, g, c16, ones, km2, kn2);
     if (t + 3 >= ntiles) break;
-    encode_tile<D, NW, MBW, KNORM, ONLINE, 3>(st, pp, ring, Kp, Vp, t + 3, n0, n1, ntiles, tid, wave, lane,
-                                              wave_active, g, c16, ones, kn2);
+    encode_tile<D, NW, MBW, KNORM, ONLINE, SKIP, 3>(st, pp, ring, sKm, Kp, Vp, t + 3, n0, n1, ntiles, wave, lane,
+                                              wave_active, g, c16, ones, km2, kn2);
   }
   // the last block's pending update
   if (wave_active) block_update<D, MBW>(st, MBW - 1, pp.v, pp.p, ones);
@@ -448,7 +515,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void encode_split_bf16(EncodeArgs 
   constexpr int KL = KOperand<D>::kLen;
   typedef typename KOperand<D>::T kop_t;
   __shared__ __attribute__((aligned(16))) __bf16 ring[8 * Ring<D, NW>::TE];
-  __shared__ float sRed[NW];
+  __shared__ float sKm[2 * NW];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -484,6 +551,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void encode_split_bf16(EncodeArgs 
         st.mu[i] = 0.0f;
       }
       need_online |= !(st.mu[i] <= 1e30f);
+      float ss = 0.0f;
+#pragma unroll
+      for (int e = 0; e < KL; ++e) {
+        const float x = (float)st.qh[i][e] + (float)st.ql[i][e];
+        ss = fmaf(x, x, ss);
+      }
+      st.qn2[i] = sum_over_rows(ss);
 #pragma unroll
       for (int db = 0; db <= DB; ++db) st.acc[db][i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -499,9 +573,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void encode_split_bf16(EncodeArgs 
   FLAREPP_WAIT_VM(0);
 
   if (!BOUNDED || online)
-    encode_tiles<D, NW, MBW, KNORM, true>(st, ring, Kp, Vp, n0, n1, tid, wave, lane, wave_active, g, c16, kn2);
+    encode_tiles<D, NW, MBW, KNORM, true, !BOUNDED>(st, ring, sKm, Kp, Vp, n0, n1, wave, lane, wave_active, g, c16, kn2);
   else
-    encode_tiles<D, NW, MBW, KNORM, false>(st, ring, Kp, Vp, n0, n1, tid, wave, lane, wave_active, g, c16, kn2);
+    encode_tiles<D, NW, MBW, KNORM, false, false>(st, ring, sKm, Kp, Vp, n0, n1, wave, lane, wave_active, g, c16, kn2);
 
   // ---- partial records
   if (wave_active) {
@@ -520,19 +594,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void encode_split_bf16(EncodeArgs 
       }
     }
   }
-  if (KNORM) {
-    float x = kn2;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-    if (lane == 0) sRed[wave] = x;
-    __syncthreads();
-    if (tid == 0 && blockIdx.z == 0) {
-      float r = sRed[0];
-#pragma unroll
-      for (int w = 1; w < NW; ++w) r = fmaxf(r, sRed[w]);
-      a.knorm[lbh * a.J + j] = r;
-    }
-  }
+  // kn2 is the maximum of the tile maxima, the same in every lane
+  if (KNORM && tid == 0 && blockIdx.z == 0) a.knorm[lbh * a.J + j] = kn2;
 }
 
 }  // namespace flarepp
