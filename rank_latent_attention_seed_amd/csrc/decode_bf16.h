@@ -37,6 +37,9 @@ struct DecodeArgs {
   const __bf16* q_lo;   // Mp x D blocks of bf16(c * Qd - hi)
   int64_t q_sb, q_sh, q_off;  // (b, h)'s block starts at element b*q_sb + h*q_sh - q_off
   const float* qnorm;   // ||Qd_m|| with the same block layout divided by D, or null
+  const float* knorm;   // [G][Jk] largest squared key norm of each split of the head (from the seed
+                        // encode), or null
+  int Jk;
   const __bf16* zt;     // [G][D][Mp] bf16(Z), transposed (G = heads of this launch)
   const __bf16* K;      // B x H x N x D
   float* Y;             // B x H x N x D
@@ -44,6 +47,19 @@ struct DecodeArgs {
   int64_t bh0;
   float c;
 };
+
+// One shift for every token of the head: mu_g = c max_n ||K_n|| max_m ||Qd_m||
+// bounds every logit of the head (Cauchy-Schwarz, with a relative margin for
+// the rounding of the hi/lo operand); when 2 mu_g <= kBoundSpan all logits lie
+// in [-2 mu_g, 0] after the shift and no per-token norm is needed.  Needs the
+// split key norms of the head (a.knorm) and the latent norms; +inf otherwise.
+__device__ __forceinline__ float head_shift(const DecodeArgs& a, int64_t lbh, float qmax, int lane) {
+  if (!a.knorm || !a.qnorm) return INFINITY;
+  float k2 = 0.0f;
+  for (int j = lane; j < a.Jk; j += 64) k2 = fmaxf(k2, a.knorm[lbh * a.Jk + j]);
+  k2 = wave_max(k2);
+  return a.c * __builtin_sqrtf(k2) * qmax * (1.0f + 1.0f / 4096.0f);
+}
 
 template <int D, int MB>
 __global__ __launch_bounds__(256, 1) void decode_bf16(DecodeArgs a) {
@@ -90,6 +106,8 @@ __global__ __launch_bounds__(256, 1) void decode_bf16(DecodeArgs a) {
   qmax = wave_max(qmax);
   const bool have_bound = a.qnorm != nullptr;
   const bool ragged_m = a.M < MP;
+  const float mu_g = head_shift(a, lbh, qmax, lane);
+  const bool gshift = 2.0f * mu_g <= kBoundSpan;
 
   // K and Y of this workgroup's tokens as buffer resources: tokens past n1
   // read as zeros and their stores are dropped, so loads need no clamping
@@ -108,29 +126,32 @@ __global__ __launch_bounds__(256, 1) void decode_bf16(DecodeArgs a) {
                        (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
   auto body = [&](const kop_t kb, const int blk) {
 
-    // token norm -> shift
-    float ss = 0.0f;
+    float sh = -mu_g;
+    if (!gshift) {
+      // token norm -> shift
+      float ss = 0.0f;
 #pragma unroll
-    for (int e = 0; e < KL / 2; ++e) {
-      const bf16x2 pr = {kb[2 * e], kb[2 * e + 1]};
-      ss = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss, false);
-    }
-    ss = sum_over_rows(ss);
-    const float mu = a.c * __builtin_amdgcn_sqrtf(ss) * qmax * (1.0f + 1.0f / 4096.0f);
-    const bool use_bound = have_bound && !__any(!(2.0f * mu <= kBoundSpan));
-    float sh = -mu;
-    if (!use_bound) {
-      // exact max over the latents: a logits-only pass
-      float lm = -INFINITY;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        f32x4 t = KOperand<D>::mma(qh[mb], kb, f32x4{0.f, 0.f, 0.f, 0.f});
-        t = KOperand<D>::mma(ql[mb], kb, t);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (!ragged_m || mb < MB - 1 || (MB - 1) * 16 + 4 * g + r < a.M) lm = fmaxf(lm, t[r]);
+      for (int e = 0; e < KL / 2; ++e) {
+        const bf16x2 pr = {kb[2 * e], kb[2 * e + 1]};
+        ss = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss, false);
       }
-      sh = -max_over_rows(lm);
+      ss = sum_over_rows(ss);
+      const float mu = a.c * __builtin_amdgcn_sqrtf(ss) * qmax * (1.0f + 1.0f / 4096.0f);
+      const bool use_bound = have_bound && !__any(!(2.0f * mu <= kBoundSpan));
+      sh = -mu;
+      if (!use_bound) {
+        // exact max over the latents: a logits-only pass
+        float lm = -INFINITY;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          f32x4 t = KOperand<D>::mma(qh[mb], kb, f32x4{0.f, 0.f, 0.f, 0.f});
+          t = KOperand<D>::mma(ql[mb], kb, t);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (!ragged_m || mb < MB - 1 || (MB - 1) * 16 + 4 * g + r < a.M) lm = fmaxf(lm, t[r]);
+        }
+        sh = -max_over_rows(lm);
+      }
     }
     const f32x4 cinit = {sh, sh, sh, sh};
 
@@ -274,6 +295,8 @@ __global__ __launch_bounds__(128, 2) void decode_pair_bf16(DecodeArgs a) {
     for (int m = lane; m < a.Mp; m += 64) qmax = fmaxf(qmax, a.qnorm[qo / D + m]);
   qmax = wave_max(qmax);
   const bool have_bound = a.qnorm != nullptr;
+  const float mu_g = head_shift(a, lbh, qmax, lane);
+  const bool gshift = 2.0f * mu_g <= kBoundSpan;  // the same in both waves
   // latent rows of this wave at or past M (the padding of the last block and
   // whole blocks past the end) get weight zero
   const int mvalid = a.M - mb0 * 16;
@@ -292,33 +315,36 @@ __global__ __launch_bounds__(128, 2) void decode_pair_bf16(DecodeArgs a) {
                        (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
   auto body = [&](const kop_t kb, const int blk, const int buf) {
 
-    // token norm -> shift (identical in both waves)
-    float ss = 0.0f;
+    float sh = -mu_g;
+    if (!gshift) {
+      // token norm -> shift (identical in both waves)
+      float ss = 0.0f;
 #pragma unroll
-    for (int e = 0; e < KL / 2; ++e) {
-      const bf16x2 pr = {kb[2 * e], kb[2 * e + 1]};
-      ss = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss, false);
-    }
-    ss = sum_over_rows(ss);
-    const float mu = a.c * __builtin_amdgcn_sqrtf(ss) * qmax * (1.0f + 1.0f / 4096.0f);
-    const bool use_bound = have_bound && __builtin_amdgcn_ballot_w64(!(2.0f * mu <= kBoundSpan)) == 0;
-    float sh = -mu;
-    if (!use_bound) {
-      // exact max over all latents: this wave's half, then the partner's
-      float lm = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < MBH; ++i) {
-        f32x4 t = KOperand<D>::mma(qh[i], kb, f32x4{0.f, 0.f, 0.f, 0.f});
-        t = KOperand<D>::mma(ql[i], kb, t);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (!RAGGED || i * 16 + 4 * g + r < mvalid) lm = fmaxf(lm, t[r]);
+      for (int e = 0; e < KL / 2; ++e) {
+        const bf16x2 pr = {kb[2 * e], kb[2 * e + 1]};
+        ss = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss, false);
       }
-      lm = max_over_rows(lm);
-      if (g == 0) sMax[w2][c16] = lm;
-      pair_barrier();
-      sh = -fmaxf(lm, sMax[1 - w2][c16]);
-      pair_barrier();  // both have read sMax before it is written again
+      ss = sum_over_rows(ss);
+      const float mu = a.c * __builtin_amdgcn_sqrtf(ss) * qmax * (1.0f + 1.0f / 4096.0f);
+      const bool use_bound = have_bound && __builtin_amdgcn_ballot_w64(!(2.0f * mu <= kBoundSpan)) == 0;
+      sh = -mu;
+      if (!use_bound) {
+        // exact max over all latents: this wave's half, then the partner's
+        float lm = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < MBH; ++i) {
+          f32x4 t = KOperand<D>::mma(qh[i], kb, f32x4{0.f, 0.f, 0.f, 0.f});
+          t = KOperand<D>::mma(ql[i], kb, t);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (!RAGGED || i * 16 + 4 * g + r < mvalid) lm = fmaxf(lm, t[r]);
+        }
+        lm = max_over_rows(lm);
+        if (g == 0) sMax[w2][c16] = lm;
+        pair_barrier();
+        sh = -fmaxf(lm, sMax[1 - w2][c16]);
+        pair_barrier();  // both have read sMax before it is written again
+      }
     }
     const f32x4 cinit = {sh, sh, sh, sh};
 

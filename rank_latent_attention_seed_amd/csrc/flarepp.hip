@@ -543,6 +543,10 @@ flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in
           dargs.q_sh = MpD;
           dargs.q_off = g0 * MpD;
           dargs.qnorm = qnorm;
+          if (stage == kRoute) {  // split key norms of the seed encode
+            dargs.knorm = at<float>(ws, p.o_knorm);
+            dargs.Jk = p.J;
+          }
         }
         dargs.zt = zt;
         dargs.K = static_cast<const __bf16*>(K);
