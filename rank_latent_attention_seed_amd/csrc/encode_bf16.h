@@ -78,8 +78,11 @@ struct KOperand<16> {
 
 // ---- tile geometry and the LDS ring.  A slot holds one tile of K or V
 // (TE bf16 = TN tokens x D); the ring has four K slots and four V slots in one
-// kernel-local LDS array.  Eight-wave workgroups (one per CU) use 16 KB
-// slots (128 KB ring); four-wave workgroups use 8 KB slots so two fit per CU.
+// kernel-local LDS array, the V slot of a tile right after its K slot, so
+// that every operand read of a step is a lane base plus an offset that fits
+// the instruction's 16-bit immediate.  Eight-wave workgroups (one per CU) use
+// 16 KB slots (128 KB ring); four-wave workgroups use 8 KB slots so two fit
+// per CU.
 template <int D, int NW>
 struct Ring {
   static constexpr int TE = NW == 8 ? 8192 : 4096;  // elements per slot
@@ -89,11 +92,11 @@ struct Ring {
   static constexpr int kDma = 2 * DI;               // loads per wave and tile
   template <int I>
   __device__ __forceinline__ static __bf16* k(__bf16* ring) {
-    return ring + I * TE;
+    return ring + 2 * I * TE;
   }
   template <int I>
   __device__ __forceinline__ static __bf16* v(__bf16* ring) {
-    return ring + (4 + I) * TE;
+    return ring + (2 * I + 1) * TE;
   }
 };
 
