@@ -123,8 +123,10 @@ def cpu_baseline(p, n_sample: int) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    # the GPU's clocks ramp up over the first tens of milliseconds of
+    # continuous load: 30 warm-up steps (~45 ms) reach the steady state
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="million")
     ap.add_argument("--backward-steps", type=int, default=3,
                     help="timed calls of the float32 backward on the same shapes (0 = skip)")
