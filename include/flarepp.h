@@ -46,7 +46,10 @@
  * call and returns a flarepp_status; no exception crosses the ABI.  A launch
  * failure is reported as FLAREPP_HIP_ERROR.  Faults inside kernels surface at
  * the caller's next synchronisation.  Results are bitwise repeatable for a
- * given descriptor and device (fixed split counts, no atomics).
+ * given descriptor: the split counts and launch shapes are a fixed function
+ * of the descriptor alone (no environment variable, device query or global
+ * state enters them) and no atomics are used.  flarepp_route_tuned lets a
+ * caller override that choice explicitly.
  */
 #ifndef FLAREPP_H
 #define FLAREPP_H
@@ -58,7 +61,7 @@
 extern "C" {
 #endif
 
-#define FLAREPP_ABI_VERSION 1
+#define FLAREPP_ABI_VERSION 2
 
 typedef enum flarepp_status {
     FLAREPP_OK = 0,
@@ -202,6 +205,47 @@ flarepp_status flarepp_route_backward(const flarepp_desc *desc, const void *S, c
 flarepp_status flarepp_spectrum(const flarepp_desc *desc, const void *S, const void *K,
                                 const void *V, float *eig, float *sym_out, void *ws,
                                 size_t ws_bytes, void *stream);
+
+/*
+ * Explicit launch choices, for split-invariance tests and tuning sweeps.  A
+ * zero field keeps the library's own choice, which depends on the descriptor
+ * only.  The result is the same softmax up to rounding for every choice: the
+ * token splits are combined exactly from their (max, sum, accumulator)
+ * statistics, the combination the French technical summary gives for
+ * token-sharded devices ("Contributions Clés", context parallelism).
+ *   splits            token splits per (b, h) in the encodes (rounded so that
+ *                     every split is a whole number of encode tiles; values
+ *                     above the tile count are clamped to it)
+ *   head_group        (b, h) pairs per launch (1 .. 65535; clamped to B*H)
+ *   decode_kernel     1 = the paired two-wave decode (bf16, M > 128 only),
+ *                     2 = the single-wave decode
+ *   decode_wg_per_cu  paired decode: workgroups per compute unit that the
+ *                     token chunking targets
+ * Negative fields are INVALID_ARG.
+ */
+typedef struct flarepp_tuning {
+    int32_t splits;
+    int32_t head_group;
+    int32_t decode_kernel;
+    int32_t decode_wg_per_cu;
+} flarepp_tuning;
+
+/*
+ * flarepp_workspace_size for the launch choices in `tuning` (NULL = the
+ * library's own, identical to flarepp_workspace_size).
+ */
+flarepp_status flarepp_workspace_size_tuned(const flarepp_desc *desc, int32_t op,
+                                            const flarepp_tuning *tuning, size_t *bytes);
+
+/*
+ * flarepp_route with the launch choices in `tuning` (NULL = the library's
+ * own); the workspace must be sized by flarepp_workspace_size_tuned with the
+ * same tuning and FLAREPP_OP_ROUTE.
+ */
+flarepp_status flarepp_route_tuned(const flarepp_desc *desc, const flarepp_tuning *tuning,
+                                   const void *S, const void *K, const void *V, float *Y,
+                                   float *Qd_out, float *Z_out, void *ws, size_t ws_bytes,
+                                   void *stream);
 
 /* Kernel kinds reported by flarepp_route_profiled. */
 typedef enum flarepp_kernel_kind {

@@ -16,7 +16,7 @@
 // (the weights feed the second product without leaving registers; see
 // common.h), and writes Y rows as 16-byte stores (a wave writes 16 whole rows).
 //
-// Shift.  mu_n = c ||K_n|| max_m ||Qd_m|| bounds every logit of token n
+// Shift.  mu_n = |c| ||K_n|| max_m ||Qd_m|| bounds every logit of token n
 // (Cauchy-Schwarz); when 2 mu_n <= 100 for all tokens of a block it enters as
 // the MFMA accumulator input and no per-score max is taken.  Otherwise the
 // block first takes the exact max over m in a logits-only pass.  Either way
@@ -48,7 +48,7 @@ struct DecodeArgs {
   float c;
 };
 
-// One shift for every token of the head: mu_g = c max_n ||K_n|| max_m ||Qd_m||
+// One shift for every token of the head: mu_g = |c| max_n ||K_n|| max_m ||Qd_m||
 // bounds every logit of the head (Cauchy-Schwarz, with a relative margin for
 // the rounding of the hi/lo operand); when 2 mu_g <= kBoundSpan all logits lie
 // in [-2 mu_g, 0] after the shift and no per-token norm is needed.  Needs the
@@ -58,7 +58,7 @@ __device__ __forceinline__ float head_shift(const DecodeArgs& a, int64_t lbh, fl
   float k2 = 0.0f;
   for (int j = lane; j < a.Jk; j += 64) k2 = fmaxf(k2, a.knorm[lbh * a.Jk + j]);
   k2 = wave_max(k2);
-  return a.c * __builtin_sqrtf(k2) * qmax * (1.0f + 1.0f / 4096.0f);
+  return fabsf(a.c) * __builtin_sqrtf(k2) * qmax * (1.0f + 1.0f / 4096.0f);
 }
 
 template <int D, int MB>
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256, 1) void decode_bf16(DecodeArgs a) {
         ss = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss, false);
       }
       ss = sum_over_rows(ss);
-      const float mu = a.c * __builtin_amdgcn_sqrtf(ss) * qmax * (1.0f + 1.0f / 4096.0f);
+      const float mu = fabsf(a.c) * __builtin_amdgcn_sqrtf(ss) * qmax * (1.0f + 1.0f / 4096.0f);
       const bool use_bound = have_bound && !__any(!(2.0f * mu <= kBoundSpan));
       sh = -mu;
       if (!use_bound) {
@@ -325,7 +325,7 @@ __global__ __launch_bounds__(128, 2) void decode_pair_bf16(DecodeArgs a) {
         ss = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss, false);
       }
       ss = sum_over_rows(ss);
-      const float mu = a.c * __builtin_amdgcn_sqrtf(ss) * qmax * (1.0f + 1.0f / 4096.0f);
+      const float mu = fabsf(a.c) * __builtin_amdgcn_sqrtf(ss) * qmax * (1.0f + 1.0f / 4096.0f);
       const bool use_bound = have_bound && __builtin_amdgcn_ballot_w64(!(2.0f * mu <= kBoundSpan)) == 0;
       sh = -mu;
       if (!use_bound) {

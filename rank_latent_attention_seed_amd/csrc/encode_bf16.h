@@ -31,7 +31,7 @@
 // c = s * log2(e) as a bf16 hi/lo pair (two MFMAs per tile, ~16 mantissa
 // bits), and -mu_m enters as the MFMA accumulator input, so the tile is
 // already t = c <Q_m, K_n> - mu_m and a weight is one exp2.  mu_m is either
-//   * a bound: c ||Q_m|| max_n ||K_n|| (Cauchy-Schwarz), supplied by the
+//   * a bound: |c| ||Q_m|| max_n ||K_n|| (Cauchy-Schwarz), supplied by the
 //     caller when it is known and keeps every exponent within [-100, 0]; no
 //     per-score max is taken; or
 //   * online: initialised from the first step's exact column max and raised
@@ -39,8 +39,9 @@
 //     every weight and sum finite), at which point acc and lambda are
 //     rescaled.  Both give the same softmax up to rounding (softmax is
 //     invariant to a common shift).
-// lambda_m sums the same bf16-rounded weights that enter the PV product
-// (computed on the matrix core as a row of ones times P^T).
+// lambda_m sums the same rounded weights that enter the PV product (computed
+// on the matrix core as a row of ones times P^T).  The encodes with a running
+// max form the PV product in fp16, the bound-shifted one in bf16 (see Pv).
 #pragma once
 
 #include "common.h"
@@ -74,6 +75,30 @@ struct KOperand<16> {
   typedef bf16x4 T;
   static constexpr int kLen = 4;
   __device__ __forceinline__ static f32x4 mma(T a, T b, f32x4 c) { return mfma_k16(a, b, c); }
+};
+
+// Number format of the P V product (the weights and the value tile on the
+// matrix core).  bf16 has float32's exponent range and an 8-bit significand.
+// fp16, used by the encodes that take a running max, has an 11-bit
+// significand, so each weight's rounding error is a quarter of bf16's; that
+// error is what limits the seed encode's Qd, and the later stages amplify an
+// error in Qd by about |s| ||K|| (Qd is their query, and the decode's key).
+// fp16's range (largest finite 65504, subnormals down to 2^-24) is kept by
+// the running max: the largest weight of a split is at least 1, so a weight
+// that flushes to zero is below 2^-24 of it (a split of n tokens loses at
+// most n 2^-25 of its sum that way); when every step is checked, weights
+// stay below 2^8.  Under the tile rule (steps unchecked) a score could still
+// exceed the running max by 16 binades; the weight is then infinite, so is
+// the split's sum, and the merge recomputes that (latent, split) record from
+// K and V (merge.h, refit_record).  The value tile is converted from bf16 in
+// LDS by the wave that loaded it.
+template <bool F16>
+struct Pv {
+  typedef bf16x8 T;
+};
+template <>
+struct Pv<true> {
+  typedef f16x8 T;
 };
 
 // ---- tile geometry and the LDS ring.  A slot holds one tile of K or V
@@ -171,7 +196,7 @@ __device__ __forceinline__ void tile_dma(__bf16* ring, const __bf16* Kp, const _
 // Per-wave register state of the encode: query operands, the shift entering
 // each S^T tile as its accumulator input, the softmax statistics, and O^T.
 // acc[DB] is the sum lambda: its tile is ONES^T P^T, whose row 0 carries the
-// column sums of the bf16 weights (so lambda sums exactly the weights that
+// column sums of the rounded weights (so lambda sums exactly the weights that
 // enter O^T).
 template <int D, int MBW>
 struct EncodeState {
@@ -187,13 +212,14 @@ struct EncodeState {
 // runs on the VALU, the matrix core works on the S^T tiles of the next block
 // and on the O^T update of the previous one; those are independent of block
 // i, so the two units overlap within the wave.
-template <int D>
+template <int D, bool F16>
 struct EncodePipe {
   typedef typename KOperand<D>::T kop_t;
+  typedef typename Pv<F16>::T pv_t;
   kop_t k0, k1;           // K operands of the current step (two 16-token halves)
   f32x4 s0, s1;           // S^T tiles of the next (step, block)
-  bf16x8 p;               // weights of the previous block, whose O^T update is pending
-  bf16x8 v[D / 16];       // V^T operands of the previous block's step
+  pv_t p;                 // weights of the previous block, whose O^T update is pending
+  pv_t v[D / 16];         // V^T operands of the previous block's step
 };
 
 // K operands (A of S^T = K Q^T: lane holds token row c16, k-chunk g) of step ks.
@@ -210,16 +236,28 @@ __device__ __forceinline__ void load_kop(const __bf16* sK, int ks, int g, int c1
 // for the eight tokens of its k-slots; one transposing read gives a lane four
 // tokens of its column when the 16 lanes of row g supply the 4-token x
 // 16-column block (lane r: token base + r/4, columns 16 db + 4 (r%4) ..+3).
-template <int D>
-__device__ __forceinline__ void load_vop(const __bf16* sV, int ks, int g, int c16, bf16x8 (&v)[D / 16]) {
+// With F16 the slot holds the fp16 conversion of the tile (same layout).
+template <int D, bool F16>
+__device__ __forceinline__ void load_vop(const __bf16* sV, int ks, int g, int c16,
+                                         typename Pv<F16>::T (&v)[D / 16]) {
   typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  typedef __attribute__((__vector_size__(4 * sizeof(__fp16)))) __fp16 h16x4;
+  typedef __attribute__((address_space(3))) h16x4 lds_h16x4;
   const int vt = ks * 32 + 4 * g + (c16 >> 2);
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) {
     const int ve = 16 * db + 4 * (c16 & 3);
-    const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(sV + slot_off<D>(vt, ve)));
-    const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(sV + slot_off<D>(vt + 16, ve)));
-    v[db] = bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    const __bf16* a0 = sV + slot_off<D>(vt, ve);
+    const __bf16* a1 = sV + slot_off<D>(vt + 16, ve);
+    if constexpr (F16) {
+      const f16x4 v0 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h16x4*)a0));
+      const f16x4 v1 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h16x4*)a1));
+      v[db] = f16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    } else {
+      const bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)a0);
+      const bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)a1);
+      v[db] = bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    }
   }
 }
 
@@ -233,18 +271,27 @@ __device__ __forceinline__ void block_logits(const EncodeState<D, MBW>& st, int 
   s1 = KOperand<D>::mma(k1, st.ql[i], s1);
 }
 
-__device__ __forceinline__ bf16x8 weights(f32x4 s0, f32x4 s1) {
-  const bf16x2 p0 = pack_bf16(fast_exp2(s0[0]), fast_exp2(s0[1]));
-  const bf16x2 p1 = pack_bf16(fast_exp2(s0[2]), fast_exp2(s0[3]));
-  const bf16x2 p2 = pack_bf16(fast_exp2(s1[0]), fast_exp2(s1[1]));
-  const bf16x2 p3 = pack_bf16(fast_exp2(s1[2]), fast_exp2(s1[3]));
-  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+template <bool F16>
+__device__ __forceinline__ typename Pv<F16>::T weights(f32x4 s0, f32x4 s1) {
+  if constexpr (F16) {
+    const f16x2 p0 = pack_f16(fast_exp2(s0[0]), fast_exp2(s0[1]));
+    const f16x2 p1 = pack_f16(fast_exp2(s0[2]), fast_exp2(s0[3]));
+    const f16x2 p2 = pack_f16(fast_exp2(s1[0]), fast_exp2(s1[1]));
+    const f16x2 p3 = pack_f16(fast_exp2(s1[2]), fast_exp2(s1[3]));
+    return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  } else {
+    const bf16x2 p0 = pack_bf16(fast_exp2(s0[0]), fast_exp2(s0[1]));
+    const bf16x2 p1 = pack_bf16(fast_exp2(s0[2]), fast_exp2(s0[3]));
+    const bf16x2 p2 = pack_bf16(fast_exp2(s1[0]), fast_exp2(s1[1]));
+    const bf16x2 p3 = pack_bf16(fast_exp2(s1[2]), fast_exp2(s1[3]));
+    return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  }
 }
 
 // O^T and lambda updates of block i from its weights p and its step's V^T operands.
-template <int D, int MBW>
-__device__ __forceinline__ void block_update(EncodeState<D, MBW>& st, int i, const bf16x8 (&v)[D / 16], bf16x8 p,
-                                             bf16x8 ones) {
+template <int D, int MBW, bool F16>
+__device__ __forceinline__ void block_update(EncodeState<D, MBW>& st, int i, const typename Pv<F16>::T (&v)[D / 16],
+                                             typename Pv<F16>::T p, typename Pv<F16>::T ones) {
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) st.acc[db][i] = mfma_k32(v[db], p, st.acc[db][i]);
   st.acc[D / 16][i] = mfma_k32(ones, p, st.acc[D / 16][i]);
@@ -259,10 +306,10 @@ __device__ __forceinline__ void block_update(EncodeState<D, MBW>& st, int i, con
 // max of the split's first step and raised lazily (only when a value exceeds
 // mu + TAU, so weights and sums stay finite); otherwise the shift is a bound.
 // MASK (the split's ragged last step): tokens at or past n1 weigh zero.
-template <int D, int MBW, bool ONLINE, bool MASK, bool HAS_NEXT>
-__device__ __forceinline__ void encode_step(EncodeState<D, MBW>& st, EncodePipe<D>& pp, const __bf16* sV, int ks,
-                                            const __bf16* sKn, int ksn, int sb, int n1, int g, int c16,
-                                            bf16x8 ones) {
+template <int D, int MBW, bool F16, bool ONLINE, bool MASK, bool HAS_NEXT>
+__device__ __forceinline__ void encode_step(EncodeState<D, MBW>& st, EncodePipe<D, F16>& pp, const __bf16* sV,
+                                            int ks, const __bf16* sKn, int ksn, int sb, int n1, int g, int c16,
+                                            typename Pv<F16>::T ones) {
   constexpr int DB = D / 16;
   constexpr float TAU = 8.0f;
   if (HAS_NEXT && MBW == 1) load_kop<D>(sKn, ksn, g, c16, pp.k0, pp.k1);
@@ -276,8 +323,8 @@ __device__ __forceinline__ void encode_step(EncodeState<D, MBW>& st, EncodePipe<
     } else if (HAS_NEXT) {
       block_logits<D, MBW>(st, 0, pp.k0, pp.k1, pp.s0, pp.s1);
     }
-    block_update<D, MBW>(st, i == 0 ? MBW - 1 : i - 1, pp.v, pp.p, ones);
-    if (i == 0) load_vop<D>(sV, ks, g, c16, pp.v);
+    block_update<D, MBW, F16>(st, i == 0 ? MBW - 1 : i - 1, pp.v, pp.p, ones);
+    if (i == 0) load_vop<D, F16>(sV, ks, g, c16, pp.v);
     // VALU: this block's weights
     if (MASK) {
 #pragma unroll
@@ -286,7 +333,7 @@ __device__ __forceinline__ void encode_step(EncodeState<D, MBW>& st, EncodePipe<
         if (sb + 16 + 4 * g + r >= n1) s1[r] = -INFINITY;
       }
     }
-    bf16x8 p = weights(s0, s1);
+    typename Pv<F16>::T p = weights<F16>(s0, s1);
     // keep the weights ahead of the (rare) rescale branch, in the same
     // scheduling region as the matrix-core work above
     asm volatile("" : "+v"(p));
@@ -305,7 +352,7 @@ __device__ __forceinline__ void encode_step(EncodeState<D, MBW>& st, EncodePipe<
           pp.s1 -= d;
         }
         st.cb[i] = f32x4{-st.mu[i], -st.mu[i], -st.mu[i], -st.mu[i]};
-        p = weights(s0, s1);
+        p = weights<F16>(s0, s1);
       }
     }
     pp.p = p;
@@ -349,23 +396,46 @@ constexpr uint32_t kEncWaitLgkm0 = 0xF | (0x7 << 4) | (0x3 << 14);
 // operands) tile u; the slot refilled there, (u+2) & 3, held tile u-2, which
 // every wave has finished reading.
 //
-// TNORM: the barrier also publishes the largest squared key norm of tile u.
-// Each wave reduces the norms of the chunks it loaded itself (landed after
-// its wait) and stores the result in sKm[u & 1][wave] before the barrier;
-// after it every wave takes the maximum over the NW entries.  Two buffers
-// suffice: the entries of tile u are read right after the barrier that opens
-// it, and rewritten (for tile u + 2) only after the next barrier.
-template <int D, int NW, int I, bool TNORM>
-__device__ __forceinline__ float ring_open(__bf16* ring, float* sKm, const __bf16* Kp, const __bf16* Vp, int u,
-                                           int n0, int n1, int wave, int lane) {
-  constexpr int kWait = Ring<D, NW>::kDma;
-  FLAREPP_WAIT_VM(kWait);
-  float* slot = sKm + (u & 1) * NW;
+// Work a wave does on its own chunks of tile u (slot I) once they have
+// landed, published by the barrier that opens the tile:
+//   TNORM: the largest squared key norm of its rows, stored in
+//     sKm[u & 1][wave]; after the barrier every wave takes the maximum over
+//     the NW entries.  Two buffers suffice: the entries of tile u are read
+//     right after the barrier that opens it, and rewritten (for tile u + 2)
+//     only after the next barrier.
+//   F16: the fp16 conversion of its value chunks, in place.
+// It runs in ring_open, after the wave's wait for its loads of tile u.
+template <int D, int NW, int I, bool TNORM, bool F16>
+__device__ __forceinline__ void tile_prep(__bf16* ring, float* sKm, int u, int wave, int lane) {
+  typedef Ring<D, NW> R;
+  if (F16) {
+#pragma unroll
+    for (int i = 0; i < R::DI; ++i) {
+      __bf16* c = R::template v<I>(ring) + (wave * R::DI + i) * 512 + 8 * lane;
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(c);
+      f16x8 y;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = (_Float16)(float)x[e];
+      *reinterpret_cast<f16x8*>(c) = y;
+    }
+  }
   if (TNORM) {
     const float part = wave_max(own_knorm<D, NW, I>(ring, wave, lane));
-    if (lane == 0) slot[wave] = part;
+    if (lane == 0) sKm[(u & 1) * NW + wave] = part;
+  }
+}
+
+template <int D, int NW, int I, bool TNORM, bool F16>
+__device__ __forceinline__ float ring_open(__bf16* ring, float* sKm, const __bf16* Kp, const __bf16* Vp, int u,
+                                           int n0, int n1, int wave, int lane) {
+  typedef Ring<D, NW> R;
+  constexpr int kWait = R::kDma;
+  FLAREPP_WAIT_VM(kWait);
+  float* slot = sKm + (u & 1) * NW;
+  tile_prep<D, NW, I, TNORM, F16>(ring, sKm, u, wave, lane);
+  if (TNORM || F16) {
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(kEncWaitLgkm0);  // the entry is in LDS before the barrier
+    __builtin_amdgcn_s_waitcnt(kEncWaitLgkm0);  // this wave's writes are in LDS before the barrier
   }
   ring_barrier();
   tile_dma<D, NW, (I + 2) & 3>(ring, Kp, Vp, n0 + (u + 2) * Ring<D, NW>::TN, n1, wave, lane);
@@ -383,11 +453,11 @@ __device__ __forceinline__ float ring_open(__bf16* ring, float* sKm, const __bf1
 // compares its scores with the running max (encode_step's online rule).
 // With TNORM, km2 holds the largest squared key norm of tile t on entry and
 // that of tile t+1 on exit.
-template <int D, int NW, int MBW, bool TNORM, bool CHECK, int I>
-__device__ __forceinline__ void encode_tile_steps(EncodeState<D, MBW>& st, EncodePipe<D>& pp, __bf16* ring,
+template <int D, int NW, int MBW, bool F16, bool TNORM, bool CHECK, int I>
+__device__ __forceinline__ void encode_tile_steps(EncodeState<D, MBW>& st, EncodePipe<D, F16>& pp, __bf16* ring,
                                                   float* sKm, const __bf16* Kp, const __bf16* Vp, int t, int n0,
                                                   int n1, int ntiles, int wave, int lane, bool wave_active, int g,
-                                                  int c16, bf16x8 ones, float& km2) {
+                                                  int c16, typename Pv<F16>::T ones, float& km2) {
   typedef Ring<D, NW> R;
   constexpr int J1 = (I + 1) & 3;
   const int tb = n0 + t * R::TN;
@@ -395,21 +465,21 @@ __device__ __forceinline__ void encode_tile_steps(EncodeState<D, MBW>& st, Encod
 #pragma unroll 1
   for (int ks = 0; ks + 1 < nsteps; ++ks) {
     if (wave_active)
-      encode_step<D, MBW, CHECK, false, true>(st, pp, R::template v<I>(ring), ks, R::template k<I>(ring), ks + 1,
+      encode_step<D, MBW, F16, CHECK, false, true>(st, pp, R::template v<I>(ring), ks, R::template k<I>(ring), ks + 1,
                                               tb + ks * 32, n1, g, c16, ones);
   }
   const int ks = nsteps - 1;
   if (t + 1 < ntiles) {
-    km2 = ring_open<D, NW, J1, TNORM>(ring, sKm, Kp, Vp, t + 1, n0, n1, wave, lane);
+    km2 = ring_open<D, NW, J1, TNORM, F16>(ring, sKm, Kp, Vp, t + 1, n0, n1, wave, lane);
     if (wave_active)
-      encode_step<D, MBW, CHECK, false, true>(st, pp, R::template v<I>(ring), ks, R::template k<J1>(ring), 0,
+      encode_step<D, MBW, F16, CHECK, false, true>(st, pp, R::template v<I>(ring), ks, R::template k<J1>(ring), 0,
                                               tb + ks * 32, n1, g, c16, ones);
   } else if (wave_active) {
     if (tb + (ks + 1) * 32 <= n1)
-      encode_step<D, MBW, CHECK, false, false>(st, pp, R::template v<I>(ring), ks, nullptr, 0, tb + ks * 32, n1, g,
+      encode_step<D, MBW, F16, CHECK, false, false>(st, pp, R::template v<I>(ring), ks, nullptr, 0, tb + ks * 32, n1, g,
                                                c16, ones);
     else
-      encode_step<D, MBW, CHECK, true, false>(st, pp, R::template v<I>(ring), ks, nullptr, 0, tb + ks * 32, n1, g,
+      encode_step<D, MBW, F16, CHECK, true, false>(st, pp, R::template v<I>(ring), ks, nullptr, 0, tb + ks * 32, n1, g,
                                               c16, ones);
   }
 }
@@ -434,24 +504,24 @@ __device__ __forceinline__ bool tile_needs_check(const EncodeState<D, MBW>& st, 
   return __builtin_amdgcn_ballot_w64(bad) != 0;
 }
 
-template <int D, int NW, int MBW, bool KNORM, bool ONLINE, bool SKIP, int I>
-__device__ __forceinline__ void encode_tile(EncodeState<D, MBW>& st, EncodePipe<D>& pp, __bf16* ring, float* sKm,
-                                            const __bf16* Kp, const __bf16* Vp, int t, int n0, int n1, int ntiles,
-                                            int wave, int lane, bool wave_active, int g, int c16, bf16x8 ones,
-                                            float& km2, float& kn2) {
+template <int D, int NW, int MBW, bool F16, bool KNORM, bool ONLINE, bool SKIP, int I>
+__device__ __forceinline__ void encode_tile(EncodeState<D, MBW>& st, EncodePipe<D, F16>& pp, __bf16* ring,
+                                            float* sKm, const __bf16* Kp, const __bf16* Vp, int t, int n0, int n1,
+                                            int ntiles, int wave, int lane, bool wave_active, int g, int c16,
+                                            typename Pv<F16>::T ones, float& km2, float& kn2) {
   constexpr bool TNORM = KNORM || (ONLINE && SKIP);
   if (KNORM) kn2 = fmaxf(kn2, km2);
   if (ONLINE && (!SKIP || tile_needs_check<D, MBW>(st, km2)))
-    encode_tile_steps<D, NW, MBW, TNORM, true, I>(st, pp, ring, sKm, Kp, Vp, t, n0, n1, ntiles, wave, lane,
-                                                  wave_active, g, c16, ones, km2);
+    encode_tile_steps<D, NW, MBW, F16, TNORM, true, I>(st, pp, ring, sKm, Kp, Vp, t, n0, n1, ntiles, wave, lane,
+                                                       wave_active, g, c16, ones, km2);
   else
-    encode_tile_steps<D, NW, MBW, TNORM, false, I>(st, pp, ring, sKm, Kp, Vp, t, n0, n1, ntiles, wave, lane,
-                                                   wave_active, g, c16, ones, km2);
+    encode_tile_steps<D, NW, MBW, F16, TNORM, false, I>(st, pp, ring, sKm, Kp, Vp, t, n0, n1, ntiles, wave, lane,
+                                                        wave_active, g, c16, ones, km2);
 }
 
 // SKIP: the online path applies the tile rule (tile_needs_check); otherwise
 // every step of the online path checks.
-template <int D, int NW, int MBW, bool KNORM, bool ONLINE, bool SKIP>
+template <int D, int NW, int MBW, bool F16, bool KNORM, bool ONLINE, bool SKIP>
 __device__ __forceinline__ void encode_tiles(EncodeState<D, MBW>& st, __bf16* ring, float* sKm, const __bf16* Kp,
                                              const __bf16* Vp, int n0, int n1, int wave, int lane,
                                              bool wave_active, int g, int c16, float& kn2) {
@@ -459,17 +529,19 @@ __device__ __forceinline__ void encode_tiles(EncodeState<D, MBW>& st, __bf16* ri
   constexpr int DB = D / 16;
   constexpr bool TNORM = KNORM || (ONLINE && SKIP);
   const int ntiles = (n1 - n0 + R::TN - 1) / R::TN;
+  typedef typename Pv<F16>::T pv_t;
   // A operand of the lambda tile: row 0 all ones
-  const __bf16 one = c16 == 0 ? (__bf16)1.0f : (__bf16)0.0f;
-  const bf16x8 ones = {one, one, one, one, one, one, one, one};
-  EncodePipe<D> pp;
-  pp.p = bf16x8{};  // no update pending before the first block
+  pv_t ones;
 #pragma unroll
-  for (int db = 0; db < DB; ++db) pp.v[db] = bf16x8{};
+  for (int e = 0; e < 8; ++e) ones[e] = c16 == 0 ? 1.0f : 0.0f;
+  EncodePipe<D, F16> pp;
+  pp.p = pv_t{};  // no update pending before the first block
+#pragma unroll
+  for (int db = 0; db < DB; ++db) pp.v[db] = pv_t{};
 
   tile_dma<D, NW, 0>(ring, Kp, Vp, n0, n1, wave, lane);
   tile_dma<D, NW, 1>(ring, Kp, Vp, n0 + R::TN, n1, wave, lane);
-  float km2 = ring_open<D, NW, 0, TNORM>(ring, sKm, Kp, Vp, 0, n0, n1, wave, lane);
+  float km2 = ring_open<D, NW, 0, TNORM, F16>(ring, sKm, Kp, Vp, 0, n0, n1, wave, lane);
   if (wave_active) {
     load_kop<D>(R::template k<0>(ring), 0, g, c16, pp.k0, pp.k1);
     if (ONLINE) {
@@ -492,28 +564,31 @@ __device__ __forceinline__ void encode_tiles(EncodeState<D, MBW>& st, __bf16* ri
     block_logits<D, MBW>(st, 0, pp.k0, pp.k1, pp.s0, pp.s1);
   }
   for (int t = 0; t < ntiles; t += 4) {
-    encode_tile<D, NW, MBW, KNORM, ONLINE, SKIP, 0>(st, pp, ring, sKm, Kp, Vp, t, n0, n1, ntiles, wave, lane,
+    encode_tile<D, NW, MBW, F16, KNORM, ONLINE, SKIP, 0>(st, pp, ring, sKm, Kp, Vp, t, n0, n1, ntiles, wave, lane,
                                               wave_active, g, c16, ones, km2, kn2);
     if (t + 1 >= ntiles) break;
-    encode_tile<D, NW, MBW, KNORM, ONLINE, SKIP, 1>(st, pp, ring, sKm, Kp, Vp, t + 1, n0, n1, ntiles, wave, lane,
+    encode_tile<D, NW, MBW, F16, KNORM, ONLINE, SKIP, 1>(st, pp, ring, sKm, Kp, Vp, t + 1, n0, n1, ntiles, wave, lane,
                                               wave_active, g, c16, ones, km2, kn2);
     if (t + 2 >= ntiles) break;
-    encode_tile<D, NW, MBW, KNORM, ONLINE, SKIP, 2>(st, pp, ring, sKm, Kp, Vp, t + 2, n0, n1, ntiles, wave, lane,
+    encode_tile<D, NW, MBW, F16, KNORM, ONLINE, SKIP, 2>(st, pp, ring, sKm, Kp, Vp, t + 2, n0, n1, ntiles, wave, lane,
                                               wave_active, g, c16, ones, km2, kn2);
     if (t + 3 >= ntiles) break;
-    encode_tile<D, NW, MBW, KNORM, ONLINE, SKIP, 3>(st, pp, ring, sKm, Kp, Vp, t + 3, n0, n1, ntiles, wave, lane,
+    encode_tile<D, NW, MBW, F16, KNORM, ONLINE, SKIP, 3>(st, pp, ring, sKm, Kp, Vp, t + 3, n0, n1, ntiles, wave, lane,
                                               wave_active, g, c16, ones, km2, kn2);
   }
   // the last block's pending update
-  if (wave_active) block_update<D, MBW>(st, MBW - 1, pp.v, pp.p, ones);
+  if (wave_active) block_update<D, MBW, F16>(st, MBW - 1, pp.v, pp.p, ones);
   // the ring's trailing loads must land before the workgroup's LDS is released
   FLAREPP_WAIT_VM(0);
 }
 
 // BOUNDED: the shift may come from a.bias (the bound path, with the online
-// path as fallback when a bound is unsafe); otherwise always online.
-template <int D, int NW, int MBW, bool KNORM, bool BOUNDED>
+// path as fallback when a bound is unsafe); otherwise always online.  F16: the
+// P V product in fp16 (online encodes only: the bound shift does not keep the
+// weights inside fp16's range).
+template <int D, int NW, int MBW, bool KNORM, bool BOUNDED, bool F16>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void encode_split_bf16(EncodeArgs a) {
+  static_assert(!(F16 && BOUNDED), "fp16 weights need the running max");
   constexpr int DB = D / 16;     // 16-row blocks of O^T
   constexpr int KL = KOperand<D>::kLen;
   typedef typename KOperand<D>::T kop_t;
@@ -576,9 +651,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void encode_split_bf16(EncodeArgs 
   FLAREPP_WAIT_VM(0);
 
   if (!BOUNDED || online)
-    encode_tiles<D, NW, MBW, KNORM, true, !BOUNDED>(st, ring, sKm, Kp, Vp, n0, n1, wave, lane, wave_active, g, c16, kn2);
+    encode_tiles<D, NW, MBW, F16, KNORM, true, !BOUNDED>(st, ring, sKm, Kp, Vp, n0, n1, wave, lane, wave_active, g,
+                                                          c16, kn2);
   else
-    encode_tiles<D, NW, MBW, KNORM, false, false>(st, ring, sKm, Kp, Vp, n0, n1, wave, lane, wave_active, g, c16, kn2);
+    encode_tiles<D, NW, MBW, false, KNORM, false, false>(st, ring, sKm, Kp, Vp, n0, n1, wave, lane, wave_active, g,
+                                                          c16, kn2);
 
   // ---- partial records
   if (wave_active) {

@@ -1,9 +1,9 @@
 // libflarepp host side: argument validation, workspace planning and the
 // launch sequences of the C ABI declared in include/flarepp.h.
 //
-// Launch sequence of the route for the bf16 path, per group of G heads
-// (G is chosen so that one group's K and V stay resident in the MI355X's
-// 256 MB last-level cache between the three passes over them):
+// Launch sequence of the route for the bf16 path, per launch group of G
+// (b, h) pairs (by default all of them: one launch per kernel, whose splits
+// fill the GPU in one round):
 //   prep    seeds -> c*S as a bf16 hi/lo operand (once per call)
 //   encode  split-N seed encode, also records each split's max key norm
 //   merge   -> Qd (caller's copy, bf16 hi/lo operand, row norms, the bound for
@@ -17,7 +17,6 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
-#include <cstdlib>
 
 #include "flarepp.h"
 #include "common.h"
@@ -32,7 +31,11 @@ using namespace flarepp;
 
 namespace {
 
-constexpr int kComputeUnits = 256;                  // MI355X
+// Compute units the launch shapes target: those of the gfx950 products
+// (MI350X, MI355X).  A constant rather than a device query, so that the split
+// counts -- and with them the rounding of every result and the workspace
+// size -- are a function of the descriptor alone, computable without a GPU.
+constexpr int kComputeUnits = 256;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -59,16 +62,6 @@ struct Plan {
   size_t o_shi, o_slo, o_sqn, o_part, o_knorm, o_qhi, o_qlo, o_qnorm, o_bias, o_zt, o_qf, o_zf, total;
 };
 
-bool env_int(const char* name, int* out) {
-  const char* v = std::getenv(name);
-  if (!v || !*v) return false;
-  char* end = nullptr;
-  long x = std::strtol(v, &end, 10);
-  if (*end || x < 1 || x > 1 << 30) return false;
-  *out = (int)x;
-  return true;
-}
-
 // Tokens per decode workgroup at most: the workgroup's rows of Y (D <= 32
 // float32) must fit a buffer resource's 32-bit byte count.
 constexpr int64_t kMaxDecodeChunk = (int64_t(1) << 31) / (32 * 4) / 64 * 64;
@@ -87,7 +80,17 @@ flarepp_status check_desc(const flarepp_desc* d) {
   return FLAREPP_OK;
 }
 
-Plan make_plan(const flarepp_desc* d, int op) {
+flarepp_status check_tuning(const flarepp_tuning* t) {
+  if (!t) return FLAREPP_OK;
+  if (t->splits < 0 || t->head_group < 0 || t->decode_kernel < 0 || t->decode_wg_per_cu < 0)
+    return FLAREPP_INVALID_ARG;
+  if (t->decode_kernel > 2 || t->decode_wg_per_cu > 64) return FLAREPP_INVALID_ARG;
+  return FLAREPP_OK;
+}
+
+// The launch plan and workspace layout of `op` for `d`; fields of `t` that are
+// nonzero replace the library's choices (t may be null).
+Plan make_plan(const flarepp_desc* d, int op, const flarepp_tuning* t = nullptr) {
   Plan p{};
   p.B = (int)d->B;
   p.H = (int)d->H;
@@ -105,8 +108,7 @@ Plan make_plan(const flarepp_desc* d, int op) {
   // tails, and the split partials stay small because the split count per head
   // shrinks with the group (one round of encode workgroups per group).
   int64_t G = p.BH;
-  int env_g;
-  if (env_int("FLAREPP_HEAD_GROUP", &env_g)) G = env_g;
+  if (t && t->head_group > 0) G = t->head_group;
   G = std::min<int64_t>(G, std::min<int64_t>(p.BH, 65535));
   p.G = (int)G;
 
@@ -121,8 +123,7 @@ Plan make_plan(const flarepp_desc* d, int op) {
   // workgroups use 128 KB of LDS, one per CU; four-wave ones fit two)
   const int64_t target = (p.bf16 ? (p.nw == 8 ? 1 : 2) : 4) * int64_t(kComputeUnits);
   int64_t J = std::max<int64_t>(1, cdiv(target, G));
-  int env_j;
-  if (env_int("FLAREPP_SPLITS", &env_j)) J = env_j;
+  if (t && t->splits > 0) J = t->splits;
   J = std::min<int64_t>(J, cdiv(d->N, tile));
   const int64_t chunk = cdiv(cdiv(d->N, J), tile) * tile;
   p.chunk = (int)chunk;
@@ -134,15 +135,12 @@ Plan make_plan(const flarepp_desc* d, int op) {
   // kernel, four 2-wave workgroups per CU); otherwise one 4-wave workgroup
   // per CU pair of SIMDs, 64-token rounds
   p.dpair = nMB > 8;
-  int env_p;
-  // FLAREPP_DECODE_PAIR: 1 = paired kernel, 2 = single-wave kernel
-  if (env_int("FLAREPP_DECODE_PAIR", &env_p)) p.dpair = nMB > 8 && env_p == 1;
+  if (t && t->decode_kernel > 0) p.dpair = nMB > 8 && t->decode_kernel == 1;
   if (p.dpair) {
     // six 2-wave workgroups per CU: three waves per SIMD at <= 168 VGPRs,
     // all resident at once (one round)
     int per_cu = 6;
-    int env_w;
-    if (env_int("FLAREPP_DECODE_WG_PER_CU", &env_w) && env_w > 0) per_cu = env_w;
+    if (t && t->decode_wg_per_cu > 0) per_cu = t->decode_wg_per_cu;
     const int64_t dwg = std::max<int64_t>(1, cdiv(per_cu * int64_t(kComputeUnits), G));
     p.dchunk = (int)std::min<int64_t>(cdiv(cdiv(d->N, dwg), 16) * 16, kMaxDecodeChunk);
   } else {
@@ -298,12 +296,14 @@ flarepp_status run_encode_bf16(const Plan& p, const EncodeArgs& a, int Gc, hipSt
                                int kind) {
   const dim3 grid((unsigned)p.J, (unsigned)Gc, (unsigned)cdiv(p.Mp / 16, p.nw * p.mbw));
   rec.before(kind, st);
+  // the encodes that take a running max form P V in fp16 (see Pv)
+  constexpr bool F16 = !BOUNDED;
   if (p.nw == 8)
-    encode_split_bf16<D, 8, 2, KNORM, BOUNDED><<<grid, dim3(512), 0, st>>>(a);
+    encode_split_bf16<D, 8, 2, KNORM, BOUNDED, F16><<<grid, dim3(512), 0, st>>>(a);
   else if (p.mbw == 2)
-    encode_split_bf16<D, 4, 2, KNORM, BOUNDED><<<grid, dim3(256), 0, st>>>(a);
+    encode_split_bf16<D, 4, 2, KNORM, BOUNDED, F16><<<grid, dim3(256), 0, st>>>(a);
   else
-    encode_split_bf16<D, 4, 1, KNORM, BOUNDED><<<grid, dim3(256), 0, st>>>(a);
+    encode_split_bf16<D, 4, 1, KNORM, BOUNDED, F16><<<grid, dim3(256), 0, st>>>(a);
   rec.after(st);
   return launched();
 }
@@ -412,6 +412,21 @@ MergeArgs merge_args(const Plan& p, void* ws, int64_t g0) {
   return m;
 }
 
+// The merge of an encode with fp16 weights recomputes any record whose sum
+// overflowed (merge.h, refit_record): it needs that encode's operands.
+void refit_from(MergeArgs& m, const EncodeArgs& e) {
+  m.fq_hi = e.q_hi;
+  m.fq_lo = e.q_lo;
+  m.fq_sb = e.q_sb;
+  m.fq_sh = e.q_sh;
+  m.fq_off = e.q_off;
+  m.fK = e.K;
+  m.fV = e.V;
+  m.H = e.H;
+  m.N = e.N;
+  m.chunk = e.chunk;
+}
+
 EncodeArgs encode_args(const Plan& p, void* ws, const void* K, const void* V, int64_t g0) {
   EncodeArgs e{};
   e.K = static_cast<const __bf16*>(K);
@@ -484,6 +499,7 @@ flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in
         else
           FLAREPP_TRY((run_encode_bf16<D, false, false>(p, e, Gc, st, rec, FLAREPP_KERNEL_SEED_ENCODE)));
         MergeArgs m = merge_args(p, ws, g0);
+        refit_from(m, e);  // an encode with fp16 weights (see run_encode_bf16)
         if (stage == kFlare) {
           m.out = Z_out;
           m.op_zt = zt;
@@ -516,6 +532,7 @@ flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in
         else
           FLAREPP_TRY((run_encode_bf16<D, false, false>(p, e, Gc, st, rec, FLAREPP_KERNEL_ENCODE)));
         MergeArgs m = merge_args(p, ws, g0);
+        if (!routed) refit_from(m, e);  // the stand-alone encode has fp16 weights, the routed one bf16
         m.out = stage == kSpectrum ? nullptr : Z_out;  // (Z_out carries the spectrum's matrix output)
         if (stage == kRoute) m.op_zt = zt;
         if (stage == kSpectrum) m.lse = at<float>(ws, p.o_lse2);
@@ -810,15 +827,16 @@ flarepp_status dispatch(const Plan& p, Stage stage, const void* S, const float* 
 // alignment, workspace size and aliasing; all before any HIP call.
 flarepp_status prologue(const flarepp_desc* d, int op, const void* const* in, const size_t* in_bytes, int nin,
                         const void* const* out, const size_t* out_bytes, const bool* out_required, int nout,
-                        void* ws, size_t ws_bytes, Plan* plan) {
+                        void* ws, size_t ws_bytes, Plan* plan, const flarepp_tuning* tuning = nullptr) {
   FLAREPP_TRY(check_desc(d));
+  FLAREPP_TRY(check_tuning(tuning));
   for (int i = 0; i < nin; ++i)
     if (!in[i] || misaligned(in[i])) return FLAREPP_INVALID_ARG;
   for (int i = 0; i < nout; ++i) {
     if (out_required[i] && !out[i]) return FLAREPP_INVALID_ARG;
     if (out[i] && misaligned(out[i])) return FLAREPP_INVALID_ARG;
   }
-  *plan = make_plan(d, op);
+  *plan = make_plan(d, op, tuning);
   if (plan->total > 0) {
     if (!ws || misaligned(ws)) return FLAREPP_INVALID_ARG;
     if (ws_bytes < plan->total) return FLAREPP_WORKSPACE_TOO_SMALL;
@@ -882,6 +900,17 @@ flarepp_status flarepp_workspace_size(const flarepp_desc* desc, int32_t op, size
   return FLAREPP_OK;
 }
 
+flarepp_status flarepp_workspace_size_tuned(const flarepp_desc* desc, int32_t op, const flarepp_tuning* tuning,
+                                            size_t* bytes) {
+  if (!bytes) return FLAREPP_INVALID_ARG;
+  FLAREPP_TRY(check_desc(desc));
+  FLAREPP_TRY(check_tuning(tuning));
+  if (op < FLAREPP_OP_SEED_ENCODE || op > FLAREPP_OP_SPECTRUM) return FLAREPP_INVALID_ARG;
+  if (op == FLAREPP_OP_ROUTE_BACKWARD && desc->dtype != FLAREPP_F32) return FLAREPP_UNSUPPORTED;
+  *bytes = make_plan(desc, op, tuning).total;
+  return FLAREPP_OK;
+}
+
 flarepp_status flarepp_seed_encode(const flarepp_desc* desc, const void* S, const void* K, const void* V,
                                    float* Qd, void* ws, size_t ws_bytes, void* stream) {
   FLAREPP_TRY(check_desc(desc));
@@ -935,6 +964,21 @@ flarepp_status flarepp_route(const flarepp_desc* desc, const void* S, const void
   const bool req[3] = {true, false, false};
   Plan p;
   FLAREPP_TRY(prologue(desc, FLAREPP_OP_ROUTE, in, inb, 3, out, outb, req, 3, ws, ws_bytes, &p));
+  return dispatch(p, kRoute, S, nullptr, nullptr, K, V, Y, Qd_out, Z_out, ws, stream);
+}
+
+flarepp_status flarepp_route_tuned(const flarepp_desc* desc, const flarepp_tuning* tuning, const void* S,
+                                   const void* K, const void* V, float* Y, float* Qd_out, float* Z_out, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  FLAREPP_TRY(check_desc(desc));
+  const Sizes z = sizes(desc);
+  const void* in[3] = {S, K, V};
+  const size_t inb[3] = {z.s, z.kv, z.kv};
+  const void* out[3] = {Y, Qd_out, Z_out};
+  const size_t outb[3] = {z.y, z.md, z.md};
+  const bool req[3] = {true, false, false};
+  Plan p;
+  FLAREPP_TRY(prologue(desc, FLAREPP_OP_ROUTE, in, inb, 3, out, outb, req, 3, ws, ws_bytes, &p, tuning));
   return dispatch(p, kRoute, S, nullptr, nullptr, K, V, Y, Qd_out, Z_out, ws, stream);
 }
 

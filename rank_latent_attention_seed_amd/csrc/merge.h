@@ -21,7 +21,7 @@ namespace flarepp {
 // Buffers marked [G] are indexed by the launch-local head lbh = blockIdx.y;
 // the caller's output by the global (b, h) = bh0 + lbh.
 struct MergeArgs {
-  const float* part;   // [G][Mp][J][D + 4]
+  float* part;         // [G][Mp][J][D + 4] (records recomputed by refit_record are written back)
   int J, Mp, M;
   int64_t bh0;
   float* out;          // [BH][M][D] float32 (the caller's Qd or Z), or null
@@ -32,10 +32,59 @@ struct MergeArgs {
   float* qnorm;        // [G][Mp] ||row||, or null
   const float* knorm;  // [G][Jk] squared key norms per split of a seed encode, or null
   int Jk;
-  float* bias;         // [G][Mp] bound c ||row|| max||K|| for the next encode (+inf if unsafe), or null
+  float* bias;         // [G][Mp] bound |c| ||row|| max||K|| for the next encode (+inf if unsafe), or null
   float c;
   float* lse;          // [G][Mp] log-sum-exp of the row's softmax, log2 units (mu + log2 lambda), or null
+  // The encode whose records are merged, for refit_record (fK null: none is
+  // recomputed): its query operand rows (bf16 hi/lo of c * Q, the rows of
+  // (b, h) at b*fq_sb + h*fq_sh - fq_off), K, V and token splits.
+  const __bf16* fq_hi;
+  const __bf16* fq_lo;
+  int64_t fq_sb, fq_sh, fq_off;
+  const __bf16* fK;
+  const __bf16* fV;
+  int H, N, chunk;
 };
+
+// A record whose sum is not finite comes from an encode whose fp16 weights
+// overflowed in a tile that skipped the running-max check (encode_bf16.h,
+// Pv); it is recomputed here, for one latent m and one split j, with the
+// encode's arithmetic in float32 on the VALU and no rounding of the weights:
+// t_n = <c Q_m, K_n> (log2 units), mu = max t_n, lambda = sum 2^(t_n - mu),
+// acc = sum 2^(t_n - mu) V_n.  Slow (one thread walks the split), and taken
+// only for inputs whose scores jump far past the running max within a tile.
+template <int D>
+__device__ __forceinline__ void refit_record(const MergeArgs& a, int64_t bh, int m, int j, float* rec) {
+  const int b = (int)(bh / a.H), h = (int)(bh - (int64_t)b * a.H);
+  const int64_t qo = (int64_t)b * a.fq_sb + (int64_t)h * a.fq_sh - a.fq_off + (int64_t)m * D;
+  float q[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) q[d] = (float)a.fq_hi[qo + d] + (float)a.fq_lo[qo + d];
+  const int n0 = j * a.chunk, n1 = min(a.N, n0 + a.chunk);
+  const __bf16* Kp = a.fK + bh * (int64_t)a.N * D;
+  const __bf16* Vp = a.fV + bh * (int64_t)a.N * D;
+  auto logit = [&](int n) {
+    float t = 0.0f;
+#pragma unroll
+    for (int d = 0; d < D; ++d) t = fmaf(q[d], (float)Kp[(int64_t)n * D + d], t);
+    return t;
+  };
+  float mu = -INFINITY;
+  for (int n = n0; n < n1; ++n) mu = fmaxf(mu, logit(n));
+  float lam = 0.0f, acc[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) acc[d] = 0.0f;
+  for (int n = n0; n < n1; ++n) {
+    const float w = exp2f(logit(n) - mu);
+    lam += w;
+#pragma unroll
+    for (int d = 0; d < D; ++d) acc[d] = fmaf(w, (float)Vp[(int64_t)n * D + d], acc[d]);
+  }
+#pragma unroll
+  for (int d = 0; d < D; ++d) rec[d] = acc[d];
+  rec[D] = lam;
+  rec[D + 1] = mu;
+}
 
 // Largest exponent span (log2 units) a bound-shifted softmax may cover: with
 // every exponent in [-100, 0] the largest weight is >= 2^-100, far above the
@@ -73,7 +122,10 @@ __global__ __launch_bounds__(256) void merge_partials(MergeArgs a) {
   const int m = blockIdx.x * RPB + r;
   const int64_t lbh = blockIdx.y, bh = a.bh0 + lbh;
   const bool row_ok = m < a.Mp;
-  const float* base = a.part + ((lbh * a.Mp + (row_ok ? m : 0)) * (int64_t)a.J) * PS;
+  float* base = a.part + ((lbh * a.Mp + (row_ok ? m : 0)) * (int64_t)a.J) * PS;
+  if (a.fK && row_ok)
+    for (int jj = q; jj < a.J; jj += T)
+      if (!(base[(int64_t)jj * PS + D] <= 3.0e38f)) refit_record<D>(a, bh, m, jj, base + (int64_t)jj * PS);
 
   float mx = -INFINITY;
 #pragma unroll 8
@@ -144,7 +196,7 @@ __global__ __launch_bounds__(256) void merge_partials(MergeArgs a) {
     if (a.bias) {
       float bnd = INFINITY;
       if (a.knorm) {
-        bnd = a.c * nrm * sqrtf(kmax2) * (1.0f + 1.0f / 4096.0f);
+        bnd = fabsf(a.c) * nrm * sqrtf(kmax2) * (1.0f + 1.0f / 4096.0f);
         if (!(2.0f * bnd <= kBoundSpan)) bnd = INFINITY;
       }
       a.bias[lbh * a.Mp + m] = bnd;
@@ -167,9 +219,14 @@ __global__ __launch_bounds__(256) void merge_rows256(MergeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = blockIdx.x;
   const int64_t lbh = blockIdx.y, bh = a.bh0 + lbh;
-  const float* base = a.part + ((lbh * a.Mp + m) * (int64_t)a.J) * PS;
+  float* base = a.part + ((lbh * a.Mp + m) * (int64_t)a.J) * PS;
 
   const bool h0 = tid < a.J, h1 = tid + 256 < a.J;
+  if (a.fK) {  // records with a non-finite sum: recompute before reading (see refit_record)
+    if (h0 && !(base[(int64_t)tid * PS + D] <= 3.0e38f)) refit_record<D>(a, bh, m, tid, base + (int64_t)tid * PS);
+    if (h1 && !(base[(int64_t)(tid + 256) * PS + D] <= 3.0e38f))
+      refit_record<D>(a, bh, m, tid + 256, base + (int64_t)(tid + 256) * PS);
+  }
   f32x4 r0[NV], r1[NV];
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
@@ -230,7 +287,7 @@ __global__ __launch_bounds__(256) void merge_rows256(MergeArgs a) {
     if (a.bias) {
       float bnd = INFINITY;
       if (a.knorm) {
-        bnd = a.c * nrm * sqrtf(kmax2) * (1.0f + 1.0f / 4096.0f);
+        bnd = fabsf(a.c) * nrm * sqrtf(kmax2) * (1.0f + 1.0f / 4096.0f);
         if (!(2.0f * bnd <= kBoundSpan)) bnd = INFINITY;
       }
       a.bias[lbh * a.Mp + m] = bnd;

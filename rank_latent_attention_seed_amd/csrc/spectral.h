@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void spectral_tokens(SpecTokArgs a) {
     for (int d = 0; d < D; ++d) t = fmaf(k[d], sQ[m * D + d], t);
     return a.c * t;
   };
-  float mu = a.c * sqrtf(kn2) * qmax * (1.0f + 1.0f / 4096.0f);
+  float mu = fabsf(a.c) * sqrtf(kn2) * qmax * (1.0f + 1.0f / 4096.0f);  // bounds |logit| for either sign of c
   if (!(2.0f * mu <= 100.0f)) {
     mu = -INFINITY;
     for (int m = 0; m < a.M; ++m) mu = fmaxf(mu, logit(m));

@@ -21,10 +21,11 @@ F32, BF16 = 0, 1
 OP_SEED_ENCODE, OP_ENCODE, OP_DECODE, OP_ROUTE, OP_FLARE, OP_ROUTE_BACKWARD, OP_SPECTRUM = range(7)
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE_TOO_SMALL", 4: "ALIASING",
           5: "HIP_ERROR"}
-ABI_VERSION = 1
+ABI_VERSION = 2
 SYMBOLS = ("flarepp_abi_version", "flarepp_status_string", "flarepp_workspace_size",
            "flarepp_seed_encode", "flarepp_encode", "flarepp_decode", "flarepp_route",
-           "flarepp_flare", "flarepp_route_backward", "flarepp_spectrum", "flarepp_route_profiled")
+           "flarepp_flare", "flarepp_route_backward", "flarepp_spectrum", "flarepp_route_profiled",
+           "flarepp_workspace_size_tuned", "flarepp_route_tuned")
 KERNEL_KINDS = {0: "prep", 1: "seed_encode", 2: "encode", 3: "merge", 4: "decode"}
 
 
@@ -38,6 +39,16 @@ class FlareppDesc(ctypes.Structure):
         ("dtype", ctypes.c_int32),
         ("scale", ctypes.c_float),
         ("seed_head_stride", ctypes.c_int64),
+    ]
+
+
+class FlareppTuning(ctypes.Structure):
+    """Explicit launch choices (0 = the library's own, a function of the descriptor)."""
+    _fields_ = [
+        ("splits", ctypes.c_int32),
+        ("head_group", ctypes.c_int32),
+        ("decode_kernel", ctypes.c_int32),
+        ("decode_wg_per_cu", ctypes.c_int32),
     ]
 
 
@@ -84,6 +95,11 @@ def _lib():
         lib.flarepp_route_profiled.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                                ctypes.POINTER(vp), ctypes.POINTER(i32), i32,
                                                ctypes.POINTER(i32)]
+        tp = ctypes.POINTER(FlareppTuning)
+        lib.flarepp_workspace_size_tuned.restype = ctypes.c_int
+        lib.flarepp_workspace_size_tuned.argtypes = [dp, i32, tp, ctypes.POINTER(sz)]
+        lib.flarepp_route_tuned.restype = ctypes.c_int
+        lib.flarepp_route_tuned.argtypes = [dp, tp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         if lib.flarepp_abi_version() != ABI_VERSION:
             raise RuntimeError("libflarepp ABI version mismatch")
         _LIB = lib
@@ -120,6 +136,26 @@ def flarepp_workspace_size(desc: FlareppDesc, op: int) -> int:
     _check(_lib().flarepp_workspace_size(ctypes.byref(desc), op, ctypes.byref(n)),
            "flarepp_workspace_size")
     return n.value
+
+
+def _tuning_ref(tuning):
+    return None if tuning is None else ctypes.byref(tuning)
+
+
+def flarepp_workspace_size_tuned(desc: FlareppDesc, op: int, tuning) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib().flarepp_workspace_size_tuned(ctypes.byref(desc), op, _tuning_ref(tuning),
+                                               ctypes.byref(n)), "flarepp_workspace_size_tuned")
+    return n.value
+
+
+def flarepp_route_tuned(desc, tuning, S, K, V, Y, Qd_out, Z_out, ws, ws_bytes, stream) -> int:
+    return _lib().flarepp_route_tuned(ctypes.byref(desc), _tuning_ref(tuning), S, K, V, Y, Qd_out, Z_out,
+                                      ws, ws_bytes, stream)
+
+
+def make_tuning(splits=0, head_group=0, decode_kernel=0, decode_wg_per_cu=0) -> FlareppTuning:
+    return FlareppTuning(int(splits), int(head_group), int(decode_kernel), int(decode_wg_per_cu))
 
 
 def flarepp_seed_encode(desc, S, K, V, Qd, ws, ws_bytes, stream) -> int:
@@ -222,8 +258,9 @@ def _stream(stream):
 
 
 def route(S, K, V, scale, *, with_intermediates=False, workspace: Workspace | None = None, stream=None,
-          out=None):
-    """Y (and optionally Qd, Z) of the full route for GPU tensors S, K, V."""
+          out=None, tuning: FlareppTuning | None = None):
+    """Y (and optionally Qd, Z) of the full route for GPU tensors S, K, V
+    (with explicit launch choices through flarepp_route_tuned if `tuning`)."""
     torch = _torch()
     for t, n in ((S, "S"), (K, "K"), (V, "V")):
         _require(t, n)
@@ -236,9 +273,14 @@ def route(S, K, V, scale, *, with_intermediates=False, workspace: Workspace | No
         Qd = torch.empty((B, H, M, D), dtype=torch.float32, device=K.device)
         Z = torch.empty((B, H, M, D), dtype=torch.float32, device=K.device)
     ws = workspace or Workspace(K.device)
-    buf, nbytes = ws.get(flarepp_workspace_size(desc, OP_ROUTE))
-    _check(flarepp_route(desc, _ptr(S), _ptr(K), _ptr(V), _ptr(Y), _ptr(Qd), _ptr(Z), _ptr(buf),
-                         nbytes, _stream(stream)), "flarepp_route")
+    if tuning is None:
+        buf, nbytes = ws.get(flarepp_workspace_size(desc, OP_ROUTE))
+        _check(flarepp_route(desc, _ptr(S), _ptr(K), _ptr(V), _ptr(Y), _ptr(Qd), _ptr(Z), _ptr(buf),
+                             nbytes, _stream(stream)), "flarepp_route")
+    else:
+        buf, nbytes = ws.get(flarepp_workspace_size_tuned(desc, OP_ROUTE, tuning))
+        _check(flarepp_route_tuned(desc, tuning, _ptr(S), _ptr(K), _ptr(V), _ptr(Y), _ptr(Qd), _ptr(Z),
+                                   _ptr(buf), nbytes, _stream(stream)), "flarepp_route_tuned")
     return (Y, Qd, Z) if with_intermediates else Y
 
 

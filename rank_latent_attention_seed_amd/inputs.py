@@ -313,11 +313,20 @@ def make_problem(name: str) -> Problem:
 
 def random_problem(B: int, H: int, N: int, M: int, D: int, dtype: str = "bf16",
                    scale: float | None = None, seed: int = 0, per_head_seeds: bool = False,
-                   sigma: float = 1.0, sigma_v: float | None = None) -> Problem:
+                   sigma: float = 1.0, sigma_v: float | None = None,
+                   k_ramp: tuple[float, float] | None = None) -> Problem:
     """iid N(0, sigma^2) K, N(0, sigma_v^2) V (sigma_v defaults to sigma), N(0, 1) seeds:
-    for edge shapes (ragged N, small M, ...) and sharpness sweeps."""
+    for edge shapes (ragged N, small M, ...) and sharpness sweeps.
+
+    k_ramp=(lo, hi) multiplies key row n by lo + (hi - lo) * n / (N - 1), so the
+    key norms (and the sharpness of the encode softmaxes) grow along the
+    token axis: the largest scores of a split arrive late."""
     rng = np.random.default_rng(seed)
     K = _noise(rng, (B, H, N, D), sigma)
+    if k_ramp is not None:
+        lo, hi = k_ramp
+        ramp = lo + (hi - lo) * np.arange(N, dtype=np.float64) / max(N - 1, 1)
+        K = (K * ramp[None, None, :, None]).astype(np.float32)
     V = _noise(rng, (B, H, N, D), sigma if sigma_v is None else sigma_v)
     S = rng.standard_normal((H, M, D) if per_head_seeds else (M, D)).astype(np.float32)
     if scale is None:

@@ -61,3 +61,57 @@ def assert_close(name, got, ref, dtype):
     else:
         assert mx <= BF16_MAXABS, f"{name}: max abs error {mx:.3e} > {BF16_MAXABS}"
     return mx, rel
+
+
+def poisoned(shape, dtype=None):
+    """A device tensor filled with NaN bit patterns (every byte 0xFF), so a
+    kernel that reads memory it never wrote, or leaves part of an output
+    unwritten, cannot pass a comparison with the oracle."""
+    import torch
+
+    n = 1
+    for x in shape:
+        n *= int(x)
+    dtype = dtype or torch.float32
+    nbytes = n * torch.empty((), dtype=dtype).element_size()
+    return torch.full((max(nbytes, 1),), 0xFF, dtype=torch.uint8, device="cuda")[:nbytes].view(dtype).view(*shape)
+
+
+def route_poisoned(fp, S, K, V, scale, tuning=None):
+    """Y, Qd, Z of flarepp_route (flarepp_route_tuned when `tuning` is given),
+    with the workspace and all three outputs NaN-poisoned before the call."""
+    import torch
+
+    desc = fp.desc_for(S, K, scale)
+    B, H, N, D = K.shape
+    M = desc.M
+    Y, Qd, Z = poisoned((B, H, N, D)), poisoned((B, H, M, D)), poisoned((B, H, M, D))
+    n = fp.flarepp_workspace_size_tuned(desc, fp.OP_ROUTE, tuning)
+    ws = poisoned((max(n, 1),), torch.uint8)
+    stream = fp._stream(None)
+    if tuning is None:
+        st = fp.flarepp_route(desc, S.data_ptr(), K.data_ptr(), V.data_ptr(), Y.data_ptr(), Qd.data_ptr(),
+                              Z.data_ptr(), ws.data_ptr(), n, stream)
+    else:
+        st = fp.flarepp_route_tuned(desc, tuning, S.data_ptr(), K.data_ptr(), V.data_ptr(), Y.data_ptr(),
+                                    Qd.data_ptr(), Z.data_ptr(), ws.data_ptr(), n, stream)
+    if st != 0:
+        raise fp.FlareppError(st, "flarepp_route")
+    return Y, Qd, Z
+
+
+def compare_route(p, Y, Qd, Z, heads=None, ref=None):
+    """Element-wise comparison of the route's three outputs with the oracle
+    on the listed heads (all by default); returns the oracle results."""
+    import torch
+
+    torch.cuda.synchronize()
+    Y, Qd, Z = Y.cpu().numpy(), Qd.cpu().numpy(), Z.cpu().numpy()
+    heads = heads or all_heads(p.B, p.H)
+    ref = ref or oracle_heads(p.S, p.K, p.V, p.scale, heads)
+    out = {}
+    out["Qd"] = assert_close("Qd", np.stack([Qd[b, h] for b, h in heads]), np.stack([r[0] for r in ref]), p.dtype)
+    out["Z"] = assert_close("Z", np.stack([Z[b, h] for b, h in heads]), np.stack([r[1] for r in ref]), p.dtype)
+    out["Y"] = assert_close("Y", np.stack([Y[b, h] for b, h in heads]), np.stack([r[2] for r in ref]), p.dtype)
+    assert np.isfinite(Y).all()
+    return ref, out

@@ -156,3 +156,48 @@ def test_spectrum_validation():
     assert spec(nbytes=n - 1) == WS_SMALL
     assert spec(eig=addr(1) + 64) == ALIASING        # output inside K
     assert spec(sym=addr(4) + 16) == ALIASING        # outputs overlap
+
+
+def test_tuning_validation_and_sizes():
+    """Explicit launch choices: a null tuning (or all-zero fields) is the
+    library's own plan, split counts change the partial-record workspace, and
+    bad fields are rejected before any HIP call."""
+    d = desc(N=100000, M=256)
+    lib = fp.library()
+    n_default = ws_status(d, fp.OP_ROUTE)[1]
+    assert fp.flarepp_workspace_size_tuned(d, fp.OP_ROUTE, None) == n_default
+    assert fp.flarepp_workspace_size_tuned(d, fp.OP_ROUTE, fp.make_tuning()) == n_default
+    n1 = fp.flarepp_workspace_size_tuned(d, fp.OP_ROUTE, fp.make_tuning(splits=1))
+    n4 = fp.flarepp_workspace_size_tuned(d, fp.OP_ROUTE, fp.make_tuning(splits=4))
+    assert n1 < n4 < n_default
+    # more splits than tiles: clamped (a split is at least one 256-token tile)
+    big = fp.flarepp_workspace_size_tuned(d, fp.OP_ROUTE, fp.make_tuning(splits=1 << 20))
+    assert big == fp.flarepp_workspace_size_tuned(d, fp.OP_ROUTE, fp.make_tuning(splits=391))
+    n = ctypes.c_size_t(0)
+    for bad in (fp.make_tuning(splits=-1), fp.make_tuning(head_group=-2), fp.make_tuning(decode_kernel=3),
+                fp.make_tuning(decode_wg_per_cu=65)):
+        assert lib.flarepp_workspace_size_tuned(ctypes.byref(d), fp.OP_ROUTE, ctypes.byref(bad),
+                                                ctypes.byref(n)) == INVALID_ARG
+        assert fp.flarepp_route_tuned(d, bad, addr(0), addr(1), addr(2), addr(3), None, None, addr(6),
+                                      1 << 30, None) == INVALID_ARG
+    # the tuned route validates like the plain one
+    t = fp.make_tuning(splits=4)
+    assert fp.flarepp_route_tuned(d, t, addr(0), addr(1), addr(2), addr(3), None, None, addr(6), n4 - 1,
+                                  None) == WS_SMALL
+    assert fp.flarepp_route_tuned(d, t, addr(0), addr(1), addr(2), addr(1) + 64, None, None, addr(6), n4,
+                                  None) == ALIASING
+
+
+def test_plan_ignores_the_environment(monkeypatch):
+    """The workspace (and with it the split count) depends on the descriptor
+    only: variables that once tuned the plan have no effect."""
+    d = desc(N=100000, M=256)
+    n = ws_status(d, fp.OP_ROUTE)[1]
+    for var in ("FLAREPP_SPLITS", "FLAREPP_HEAD_GROUP", "FLAREPP_DECODE_PAIR", "FLAREPP_DECODE_WG_PER_CU"):
+        monkeypatch.setenv(var, "3")
+    assert ws_status(d, fp.OP_ROUTE)[1] == n
+
+
+def test_negative_scale_is_accepted():
+    """A negative scale is a valid descriptor (the bounds use |s|)."""
+    assert ws_status(desc(scale=-1.0), fp.OP_ROUTE)[0] == OK

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 from rank_latent_attention_seed_amd import inputs
-from gpu_util import all_heads, assert_close, oracle_heads, to_device
+from gpu_util import all_heads, assert_close, compare_route, oracle_heads, poisoned, route_poisoned, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -25,26 +25,14 @@ def fp():
     return flarepp
 
 
-def run_and_compare(fp, p, heads=None, label=""):
-    import torch
-
+def run_and_compare(fp, p, heads=None, label="", tuning=None):
+    """The route on NaN-poisoned outputs and workspace, compared element by
+    element with the oracle on the listed heads (all by default)."""
     print(f"\n  case {label or p.name}: B{p.B} H{p.H} N{p.N} M{p.M} D{p.D} {p.dtype} s={p.scale:g}",
           flush=True)
     S, K, V = to_device(p.S), to_device(p.K), to_device(p.V)
-    Y, Qd, Z = fp.route(S, K, V, p.scale, with_intermediates=True)
-    torch.cuda.synchronize()
-    Y, Qd, Z = Y.cpu().numpy(), Qd.cpu().numpy(), Z.cpu().numpy()
-    heads = heads or all_heads(p.B, p.H)
-    ref = oracle_heads(p.S, p.K, p.V, p.scale, heads)
-    got_q = np.stack([Qd[b, h] for b, h in heads])
-    got_z = np.stack([Z[b, h] for b, h in heads])
-    got_y = np.stack([Y[b, h] for b, h in heads])
-    out = {}
-    out["Qd"] = assert_close("Qd", got_q, np.stack([r[0] for r in ref]), p.dtype)
-    out["Z"] = assert_close("Z", got_z, np.stack([r[1] for r in ref]), p.dtype)
-    out["Y"] = assert_close("Y", got_y, np.stack([r[2] for r in ref]), p.dtype)
-    assert np.isfinite(Y).all()
-    return out
+    Y, Qd, Z = route_poisoned(fp, S, K, V, p.scale, tuning)
+    return compare_route(p, Y, Qd, Z, heads=heads)[1]
 
 
 @pytest.mark.parametrize("name", ["tiny", "mesh", "cloud", "stress"])
@@ -74,7 +62,8 @@ def test_million_full_size_sampled(fp):
     p = inputs.make_problem("million")
     print(f"\n  case million: B{p.B} H{p.H} N{p.N} M{p.M} D{p.D} {p.dtype}", flush=True)
     S, K, V = to_device(p.S), to_device(p.K), to_device(p.V)
-    Y, Qd, Z = fp.route(S, K, V, p.scale, with_intermediates=True)
+    Y, Qd, Z = route_poisoned(fp, S, K, V, p.scale)
+    assert bool(torch.isfinite(Y).all()), "Y has entries the route did not write"
     rng = np.random.default_rng(11)
     tokens = np.unique(np.concatenate([[0, p.N - 1], rng.choice(p.N, 62, replace=False)]))
     heads = [(0, 0), (0, 5)]
@@ -129,7 +118,7 @@ def test_per_head_seeds(fp, dtype):
     run_and_compare(fp, p, label=f"per-head seeds {dtype}")
 
 
-@pytest.mark.parametrize("scale", [0.0, 1.0, 0.05])
+@pytest.mark.parametrize("scale", [0.0, 1.0, 0.05, -1.0, -0.125])
 def test_scales(fp, scale):
     p = inputs.random_problem(1, 2, 2000, 64, 32, dtype="bf16", scale=scale, seed=9)
     run_and_compare(fp, p, label=f"scale {scale}")
@@ -156,12 +145,27 @@ def test_stages_match_oracle(fp):
     Qd_ref = np.stack([r[0] for r in ref]).reshape(p.B, p.H, p.M, p.D)
     Z_ref = np.stack([r[1] for r in ref]).reshape(p.B, p.H, p.M, p.D)
     Y_ref = np.stack([r[2] for r in ref]).reshape(p.B, p.H, p.N, p.D)
-    Qd = fp.seed_encode(S, K, V, p.scale)
+    d = fp.desc_for(S, K, p.scale)
+    stream = fp._stream(None)
+
+    def ws(op):
+        n = fp.flarepp_workspace_size(d, op)
+        return poisoned((max(n, 1),), torch.uint8), n
+
+    # every stage writes into NaN-poisoned outputs with a NaN-poisoned workspace
+    Qd, Z, Y = poisoned(Qd_ref.shape), poisoned(Z_ref.shape), poisoned(Y_ref.shape)
+    w, n = ws(fp.OP_SEED_ENCODE)
+    assert fp.flarepp_seed_encode(d, S.data_ptr(), K.data_ptr(), V.data_ptr(), Qd.data_ptr(), w.data_ptr(), n,
+                                  stream) == 0
     # the later stages take the oracle's Qd / Z as inputs, so each stage is checked alone
     Qd_o = torch.from_numpy(Qd_ref.astype(np.float32)).cuda()
     Z_o = torch.from_numpy(Z_ref.astype(np.float32)).cuda()
-    Z = fp.encode(Qd_o, K, V, p.scale)
-    Y = fp.decode(Qd_o, Z_o, K, p.scale)
+    w, n = ws(fp.OP_ENCODE)
+    assert fp.flarepp_encode(d, Qd_o.data_ptr(), K.data_ptr(), V.data_ptr(), Z.data_ptr(), w.data_ptr(), n,
+                             stream) == 0
+    w, n = ws(fp.OP_DECODE)
+    assert fp.flarepp_decode(d, Qd_o.data_ptr(), Z_o.data_ptr(), K.data_ptr(), Y.data_ptr(), w.data_ptr(), n,
+                             stream) == 0
     torch.cuda.synchronize()
     assert_close("seed_encode", Qd.cpu().numpy(), Qd_ref, "bf16")
     assert_close("encode", Z.cpu().numpy(), Z_ref, "bf16")
@@ -183,30 +187,26 @@ def test_fixed_query_flare(fp, dtype):
     assert_close("Y", Y.cpu().numpy(), Y_ref, dtype)
 
 
-def test_deterministic_and_split_invariant(fp, monkeypatch):
+def test_deterministic_and_split_invariant(fp):
     import torch
 
     p = inputs.random_problem(1, 2, 20000, 128, 32, dtype="bf16", seed=4)
     print("\n  case determinism / split invariance", flush=True)
     S, K, V = to_device(p.S), to_device(p.K), to_device(p.V)
-    a = fp.route(S, K, V, p.scale, with_intermediates=True)
-    b = fp.route(S, K, V, p.scale, with_intermediates=True)
+    a = route_poisoned(fp, S, K, V, p.scale)
+    b = route_poisoned(fp, S, K, V, p.scale)
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y), "two identical calls differ"
-    monkeypatch.setenv("FLAREPP_SPLITS", "1")
-    c = fp.route(S, K, V, p.scale, with_intermediates=True)
-    monkeypatch.setenv("FLAREPP_SPLITS", "7")
-    d = fp.route(S, K, V, p.scale, with_intermediates=True)
-    torch.cuda.synchronize()
-    for x, y, z in zip(a, c, d):
-        assert float((x - y).abs().max()) <= 1e-2
-        assert float((x - z).abs().max()) <= 1e-2
+    ref = None
+    for splits in (1, 7):
+        c = route_poisoned(fp, S, K, V, p.scale, fp.make_tuning(splits=splits))
+        ref = compare_route(p, *c, ref=ref)[0]  # each split count against the oracle
+        for x, y in zip(a, c):
+            assert float((x - y).abs().max()) <= 1e-2
     # grouping heads into launches does not change any head's arithmetic
-    monkeypatch.setenv("FLAREPP_HEAD_GROUP", "1")
-    e = fp.route(S, K, V, p.scale, with_intermediates=True)
-    monkeypatch.setenv("FLAREPP_HEAD_GROUP", "2")
-    f = fp.route(S, K, V, p.scale, with_intermediates=True)
+    e = route_poisoned(fp, S, K, V, p.scale, fp.make_tuning(splits=8, head_group=1))
+    f = route_poisoned(fp, S, K, V, p.scale, fp.make_tuning(splits=8, head_group=2))
     torch.cuda.synchronize()
     for x, y in zip(e, f):
         assert torch.equal(x, y), "head grouping changed results"
