@@ -20,7 +20,7 @@
 // 16-byte chunks
 // of each token row are XOR-swizzled in LDS (the fetching lane picks the
 // chunk that belongs to its slot) so the matrix-core operand reads are free
-// of bank conflicts.  Per 32-token step a wave computes S^T = K Q^T tiles
+// of bank conflicts (chunk_swz).  Per 32-token step a wave computes S^T = K Q^T tiles
 // (rows = tokens, cols = latents), turns them into softmax weights in
 // registers, and accumulates O^T += V^T P^T; V's operand comes from the
 // token-major tile through transposing LDS reads (ds_read_b64_tr_b16).  The
@@ -126,11 +126,26 @@ struct Ring {
 };
 
 // Swizzle of the 16-byte chunks of token row t (D/8 chunks per row): the
-// chunk holding elements 8u..8u+7 sits at position u ^ swz(t).
+// chunk holding elements 8u..8u+7 sits at position u ^ swz(t).  gfx950's LDS
+// has 64 banks of 4 bytes; for D = 32 (64-byte rows) the K operand read
+// (ds_read_b128: lane (g, c16) reads chunk g of row c16) and the transposing
+// V read (ds_read_b64_tr_b16: 16 lanes read 4 rows x 32 bytes) are both free
+// of bank conflicts with swz(t) = (t >> 1) & 3, measured with
+// SQ_LDS_BANK_CONFLICT on MI355X (4 and 2 cycles per wave instruction; the
+// swizzle (t >> 2) & 3 takes twice as long on both).
 template <int D>
-__device__ __forceinline__ int chunk_swz(int t) {
-  return D == 32 ? ((t >> 2) & 3) : ((t >> 3) & 1);
+__host__ __device__ __forceinline__ constexpr int chunk_swz(int t) {
+  return D == 32 ? ((t >> 1) & 3) : ((t >> 3) & 1);
 }
+// The swizzle of row t equals that of rows t + 16 and t + 32 (EncodePipe's
+// operand offsets rely on it).
+template <int D>
+constexpr bool swz_step_invariant() {
+  for (int t = 0; t < 64; ++t)
+    if (chunk_swz<D>(t) != chunk_swz<D>(t + 16) || chunk_swz<D>(t) != chunk_swz<D>(t + 32)) return false;
+  return true;
+}
+static_assert(swz_step_invariant<32>() && swz_step_invariant<16>(), "chunk swizzle must repeat every 16 rows");
 // Element offset of (token t, element e) inside a tile slot.
 template <int D>
 __device__ __forceinline__ int slot_off(int t, int e) {
@@ -216,20 +231,28 @@ template <int D, bool F16>
 struct EncodePipe {
   typedef typename KOperand<D>::T kop_t;
   typedef typename Pv<F16>::T pv_t;
+  // this lane's operand offsets (elements) within a step of a slot: K row c16
+  // at element KL g, and per 16-column block db the V^T read of row
+  // 4 g + c16 / 4 at element 16 db + 4 (c16 % 4).  The rows 16 further on, and
+  // every later step (32 rows on), add constants: the swizzle of a row depends
+  // on bits of its index that neither changes (chunk_swz), so a step's reads
+  // are these bases plus the step's offset plus immediates.
+  int ko, vo[D / 16];
   kop_t k0, k1;           // K operands of the current step (two 16-token halves)
   f32x4 s0, s1;           // S^T tiles of the next (step, block)
   pv_t p;                 // weights of the previous block, whose O^T update is pending
   pv_t v[D / 16];         // V^T operands of the previous block's step
 };
 
-// K operands (A of S^T = K Q^T: lane holds token row c16, k-chunk g) of step ks.
+// K operands (A of S^T = K Q^T: lane holds token row c16, k-chunk g) of step
+// ks; ko = slot_off(c16, KL g).
 template <int D>
-__device__ __forceinline__ void load_kop(const __bf16* sK, int ks, int g, int c16,
-                                         typename KOperand<D>::T& k0, typename KOperand<D>::T& k1) {
-  constexpr int KL = KOperand<D>::kLen;
+__device__ __forceinline__ void load_kop(const __bf16* sK, int ks, int ko, typename KOperand<D>::T& k0,
+                                         typename KOperand<D>::T& k1) {
   typedef typename KOperand<D>::T kop_t;
-  k0 = *reinterpret_cast<const kop_t*>(sK + slot_off<D>(ks * 32 + c16, KL * g));
-  k1 = *reinterpret_cast<const kop_t*>(sK + slot_off<D>(ks * 32 + 16 + c16, KL * g));
+  const __bf16* b = sK + ks * 32 * D + ko;
+  k0 = *reinterpret_cast<const kop_t*>(b);
+  k1 = *reinterpret_cast<const kop_t*>(b + 16 * D);
 }
 
 // V^T operands of step ks: lane (row d = 16 db + c16, k-row g) needs V[tok][d]
@@ -237,18 +260,17 @@ __device__ __forceinline__ void load_kop(const __bf16* sK, int ks, int g, int c1
 // tokens of its column when the 16 lanes of row g supply the 4-token x
 // 16-column block (lane r: token base + r/4, columns 16 db + 4 (r%4) ..+3).
 // With F16 the slot holds the fp16 conversion of the tile (same layout).
+// vo[db] = slot_off(4 g + c16 / 4, 16 db + 4 (c16 % 4)).
 template <int D, bool F16>
-__device__ __forceinline__ void load_vop(const __bf16* sV, int ks, int g, int c16,
+__device__ __forceinline__ void load_vop(const __bf16* sV, int ks, const int (&vo)[D / 16],
                                          typename Pv<F16>::T (&v)[D / 16]) {
   typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
   typedef __attribute__((__vector_size__(4 * sizeof(__fp16)))) __fp16 h16x4;
   typedef __attribute__((address_space(3))) h16x4 lds_h16x4;
-  const int vt = ks * 32 + 4 * g + (c16 >> 2);
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) {
-    const int ve = 16 * db + 4 * (c16 & 3);
-    const __bf16* a0 = sV + slot_off<D>(vt, ve);
-    const __bf16* a1 = sV + slot_off<D>(vt + 16, ve);
+    const __bf16* a0 = sV + ks * 32 * D + vo[db];
+    const __bf16* a1 = a0 + 16 * D;
     if constexpr (F16) {
       const f16x4 v0 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h16x4*)a0));
       const f16x4 v1 = __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_h16x4*)a1));
@@ -312,19 +334,19 @@ __device__ __forceinline__ void encode_step(EncodeState<D, MBW>& st, EncodePipe<
                                             typename Pv<F16>::T ones) {
   constexpr int DB = D / 16;
   constexpr float TAU = 8.0f;
-  if (HAS_NEXT && MBW == 1) load_kop<D>(sKn, ksn, g, c16, pp.k0, pp.k1);
+  if (HAS_NEXT && MBW == 1) load_kop<D>(sKn, ksn, pp.ko, pp.k0, pp.k1);
 #pragma unroll
   for (int i = 0; i < MBW; ++i) {
     f32x4 s0 = pp.s0, s1 = pp.s1;
     // matrix core: next block's logits, previous block's update
     if (i + 1 < MBW) {
       block_logits<D, MBW>(st, i + 1, pp.k0, pp.k1, pp.s0, pp.s1);
-      if (HAS_NEXT && i + 2 == MBW) load_kop<D>(sKn, ksn, g, c16, pp.k0, pp.k1);
+      if (HAS_NEXT && i + 2 == MBW) load_kop<D>(sKn, ksn, pp.ko, pp.k0, pp.k1);
     } else if (HAS_NEXT) {
       block_logits<D, MBW>(st, 0, pp.k0, pp.k1, pp.s0, pp.s1);
     }
     block_update<D, MBW, F16>(st, i == 0 ? MBW - 1 : i - 1, pp.v, pp.p, ones);
-    if (i == 0) load_vop<D, F16>(sV, ks, g, c16, pp.v);
+    if (i == 0) load_vop<D, F16>(sV, ks, pp.vo, pp.v);
     // VALU: this block's weights
     if (MASK) {
 #pragma unroll
@@ -535,6 +557,9 @@ __device__ __forceinline__ void encode_tiles(EncodeState<D, MBW>& st, __bf16* ri
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = c16 == 0 ? 1.0f : 0.0f;
   EncodePipe<D, F16> pp;
+  pp.ko = slot_off<D>(c16, KOperand<D>::kLen * g);
+#pragma unroll
+  for (int db = 0; db < DB; ++db) pp.vo[db] = slot_off<D>(4 * g + (c16 >> 2), 16 * db + 4 * (c16 & 3));
   pp.p = pv_t{};  // no update pending before the first block
 #pragma unroll
   for (int db = 0; db < DB; ++db) pp.v[db] = pv_t{};
@@ -543,7 +568,7 @@ __device__ __forceinline__ void encode_tiles(EncodeState<D, MBW>& st, __bf16* ri
   tile_dma<D, NW, 1>(ring, Kp, Vp, n0 + R::TN, n1, wave, lane);
   float km2 = ring_open<D, NW, 0, TNORM, F16>(ring, sKm, Kp, Vp, 0, n0, n1, wave, lane);
   if (wave_active) {
-    load_kop<D>(R::template k<0>(ring), 0, g, c16, pp.k0, pp.k1);
+    load_kop<D>(R::template k<0>(ring), 0, pp.ko, pp.k0, pp.k1);
     if (ONLINE) {
       // the running max starts at the exact column max of the first step
       // (the shift is still zero here)

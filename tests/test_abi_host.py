@@ -201,3 +201,4 @@ def test_plan_ignores_the_environment(monkeypatch):
 def test_negative_scale_is_accepted():
     """A negative scale is a valid descriptor (the bounds use |s|)."""
     assert ws_status(desc(scale=-1.0), fp.OP_ROUTE)[0] == OK
+

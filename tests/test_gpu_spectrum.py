@@ -58,6 +58,8 @@ CASES = [
     (1, 2, 1000, 128, 32, "bf16", 1.0, False),
     (1, 1, 50, 1, 32, "f32", 0.7, False),
     (1, 1, 400, 16, 32, "f32", 0.0, False),
+    (1, 2, 600, 40, 32, "f32", -1.0, False),   # s < 0: the bounds use |s|
+    (1, 2, 600, 40, 16, "bf16", -0.5, False),
 ]
 
 
