@@ -69,7 +69,8 @@ typedef enum flarepp_status {
     FLAREPP_UNSUPPORTED = 2,          /* D not 16 or 32, dtype unknown, M or N*D beyond the limits below */
     FLAREPP_WORKSPACE_TOO_SMALL = 3,  /* ws_bytes below flarepp_workspace_size() */
     FLAREPP_ALIASING = 4,             /* an output overlaps an input, another output or the workspace */
-    FLAREPP_HIP_ERROR = 5             /* a kernel launch failed */
+    FLAREPP_HIP_ERROR = 5,            /* a kernel launch failed */
+    FLAREPP_SCRATCH_LIMIT = 6         /* flarepp_route_noalloc: workspace beyond its built-in scratch */
 } flarepp_status;
 
 typedef enum flarepp_dtype {
@@ -246,6 +247,28 @@ flarepp_status flarepp_route_tuned(const flarepp_desc *desc, const flarepp_tunin
                                    const void *S, const void *K, const void *V, float *Y,
                                    float *Qd_out, float *Z_out, void *ws, size_t ws_bytes,
                                    void *stream);
+
+/*
+ * flarepp_route for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The caller passes the inputs and outputs only; the workspace is a device
+ * array built into the library (flarepp_noalloc_scratch_bytes() bytes, 64
+ * MiB; each GPU the library runs on holds its own copy until the process
+ * ends).  The call allocates nothing (no hipMalloc, no allocating library
+ * routine); its first call on a device looks up that device's array address.
+ * Returns FLAREPP_SCRATCH_LIMIT, before any GPU work, when the problem needs
+ * more workspace than the array holds (flarepp_workspace_size with
+ * FLAREPP_OP_ROUTE gives the need).  All calls on one GPU share the array:
+ * calls whose work overlaps in time on one GPU (other streams, other host
+ * threads) race on it and must be serialised by the caller.  Results are
+ * bitwise those of flarepp_route.
+ */
+flarepp_status flarepp_route_noalloc(const flarepp_desc *desc, const void *S, const void *K,
+                                     const void *V, float *Y, float *Qd_out, float *Z_out,
+                                     void *stream);
+
+/* Bytes of the built-in scratch of flarepp_route_noalloc. */
+size_t flarepp_noalloc_scratch_bytes(void);
 
 /* Kernel kinds reported by flarepp_route_profiled. */
 typedef enum flarepp_kernel_kind {

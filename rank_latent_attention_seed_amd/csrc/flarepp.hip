@@ -17,6 +17,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "flarepp.h"
 #include "common.h"
@@ -825,9 +826,11 @@ flarepp_status dispatch(const Plan& p, Stage stage, const void* S, const float* 
 
 // Shared argument checks of the compute calls: descriptor, pointers,
 // alignment, workspace size and aliasing; all before any HIP call.
+// ws_internal: the workspace is the library's own scratch (not checked here).
 flarepp_status prologue(const flarepp_desc* d, int op, const void* const* in, const size_t* in_bytes, int nin,
                         const void* const* out, const size_t* out_bytes, const bool* out_required, int nout,
-                        void* ws, size_t ws_bytes, Plan* plan, const flarepp_tuning* tuning = nullptr) {
+                        void* ws, size_t ws_bytes, Plan* plan, const flarepp_tuning* tuning = nullptr,
+                        bool ws_internal = false) {
   FLAREPP_TRY(check_desc(d));
   FLAREPP_TRY(check_tuning(tuning));
   for (int i = 0; i < nin; ++i)
@@ -837,7 +840,7 @@ flarepp_status prologue(const flarepp_desc* d, int op, const void* const* in, co
     if (out[i] && misaligned(out[i])) return FLAREPP_INVALID_ARG;
   }
   *plan = make_plan(d, op, tuning);
-  if (plan->total > 0) {
+  if (plan->total > 0 && !ws_internal) {
     if (!ws || misaligned(ws)) return FLAREPP_INVALID_ARG;
     if (ws_bytes < plan->total) return FLAREPP_WORKSPACE_TOO_SMALL;
   }
@@ -849,7 +852,7 @@ flarepp_status prologue(const flarepp_desc* d, int op, const void* const* in, co
     ins[ni] = range(in[i], in_bytes[i]);
     inp[ni++] = in[i];
   }
-  if (plan->total > 0) {
+  if (plan->total > 0 && !ws_internal) {
     ins[ni] = range(ws, plan->total);
     inp[ni++] = ws;
   }
@@ -873,6 +876,34 @@ Sizes sizes(const flarepp_desc* d) {
   return z;
 }
 
+// ---- allocation-free route: the workspace is a file-scope device array.
+// Every GPU the library runs on holds its own copy of `scratch` until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current and
+// kept in g_scratch_ptr.  Calls on one GPU share the array, so calls that
+// overlap in time on one GPU (different streams, or several host threads)
+// race on it; nothing in it needs to start at zero (the route writes every
+// workspace word it reads).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+flarepp_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FLAREPP_HIP_ERROR;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FLAREPP_HIP_ERROR;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FLAREPP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -887,6 +918,7 @@ const char* flarepp_status_string(flarepp_status s) {
     case FLAREPP_WORKSPACE_TOO_SMALL: return "workspace too small";
     case FLAREPP_ALIASING: return "an output overlaps another buffer";
     case FLAREPP_HIP_ERROR: return "HIP launch error";
+    case FLAREPP_SCRATCH_LIMIT: return "workspace needed exceeds the library's built-in scratch";
   }
   return "unknown status";
 }
@@ -981,6 +1013,25 @@ flarepp_status flarepp_route_tuned(const flarepp_desc* desc, const flarepp_tunin
   FLAREPP_TRY(prologue(desc, FLAREPP_OP_ROUTE, in, inb, 3, out, outb, req, 3, ws, ws_bytes, &p, tuning));
   return dispatch(p, kRoute, S, nullptr, nullptr, K, V, Y, Qd_out, Z_out, ws, stream);
 }
+
+flarepp_status flarepp_route_noalloc(const flarepp_desc* desc, const void* S, const void* K, const void* V,
+                                     float* Y, float* Qd_out, float* Z_out, void* stream) {
+  FLAREPP_TRY(check_desc(desc));
+  const Sizes z = sizes(desc);
+  const void* in[3] = {S, K, V};
+  const size_t inb[3] = {z.s, z.kv, z.kv};
+  const void* out[3] = {Y, Qd_out, Z_out};
+  const size_t outb[3] = {z.y, z.md, z.md};
+  const bool req[3] = {true, false, false};
+  Plan p;
+  FLAREPP_TRY(prologue(desc, FLAREPP_OP_ROUTE, in, inb, 3, out, outb, req, 3, nullptr, 0, &p, nullptr, true));
+  if (p.total > kScratchBytes) return FLAREPP_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  FLAREPP_TRY(scratch_of_current_device(&ws));
+  return dispatch(p, kRoute, S, nullptr, nullptr, K, V, Y, Qd_out, Z_out, ws, stream);
+}
+
+size_t flarepp_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 flarepp_status flarepp_flare(const flarepp_desc* desc, const void* Q, const void* K, const void* V, float* Y,
                              float* Z_out, void* ws, size_t ws_bytes, void* stream) {

@@ -20,12 +20,13 @@ LIBRARY = os.path.join(_PKG, "libflarepp.so")
 F32, BF16 = 0, 1
 OP_SEED_ENCODE, OP_ENCODE, OP_DECODE, OP_ROUTE, OP_FLARE, OP_ROUTE_BACKWARD, OP_SPECTRUM = range(7)
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE_TOO_SMALL", 4: "ALIASING",
-          5: "HIP_ERROR"}
+          5: "HIP_ERROR", 6: "SCRATCH_LIMIT"}
 ABI_VERSION = 2
 SYMBOLS = ("flarepp_abi_version", "flarepp_status_string", "flarepp_workspace_size",
            "flarepp_seed_encode", "flarepp_encode", "flarepp_decode", "flarepp_route",
            "flarepp_flare", "flarepp_route_backward", "flarepp_spectrum", "flarepp_route_profiled",
-           "flarepp_workspace_size_tuned", "flarepp_route_tuned")
+           "flarepp_workspace_size_tuned", "flarepp_route_tuned", "flarepp_route_noalloc",
+           "flarepp_noalloc_scratch_bytes")
 KERNEL_KINDS = {0: "prep", 1: "seed_encode", 2: "encode", 3: "merge", 4: "decode"}
 
 
@@ -100,6 +101,10 @@ def _lib():
         lib.flarepp_workspace_size_tuned.argtypes = [dp, i32, tp, ctypes.POINTER(sz)]
         lib.flarepp_route_tuned.restype = ctypes.c_int
         lib.flarepp_route_tuned.argtypes = [dp, tp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.flarepp_route_noalloc.restype = ctypes.c_int
+        lib.flarepp_route_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp]
+        lib.flarepp_noalloc_scratch_bytes.restype = sz
+        lib.flarepp_noalloc_scratch_bytes.argtypes = []
         if lib.flarepp_abi_version() != ABI_VERSION:
             raise RuntimeError("libflarepp ABI version mismatch")
         _LIB = lib
@@ -152,6 +157,14 @@ def flarepp_workspace_size_tuned(desc: FlareppDesc, op: int, tuning) -> int:
 def flarepp_route_tuned(desc, tuning, S, K, V, Y, Qd_out, Z_out, ws, ws_bytes, stream) -> int:
     return _lib().flarepp_route_tuned(ctypes.byref(desc), _tuning_ref(tuning), S, K, V, Y, Qd_out, Z_out,
                                       ws, ws_bytes, stream)
+
+
+def flarepp_route_noalloc(desc, S, K, V, Y, Qd_out, Z_out, stream) -> int:
+    return _lib().flarepp_route_noalloc(ctypes.byref(desc), S, K, V, Y, Qd_out, Z_out, stream)
+
+
+def flarepp_noalloc_scratch_bytes() -> int:
+    return _lib().flarepp_noalloc_scratch_bytes()
 
 
 def make_tuning(splits=0, head_group=0, decode_kernel=0, decode_wg_per_cu=0) -> FlareppTuning:
