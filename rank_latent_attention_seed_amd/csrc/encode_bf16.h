@@ -252,6 +252,10 @@ __device__ __forceinline__ void load_kop(const __bf16* sK, int ks, int ko, typen
   typedef typename KOperand<D>::T kop_t;
   const __bf16* b = sK + ks * 32 * D + ko;
   k0 = *reinterpret_cast<const kop_t*>(b);
+  // D = 16: the two 8-byte reads are 512 bytes apart, which the compiler would
+  // fuse into one ds_read2st64_b64 -- measured on MI355X at 16 LDS cycles per
+  // wave instruction where the two ds_read_b64 take 2 each (SQ_LDS_BANK_CONFLICT)
+  if (D == 16) asm volatile("" ::: "memory");
   k1 = *reinterpret_cast<const kop_t*>(b + 16 * D);
 }
 
