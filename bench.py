@@ -26,7 +26,9 @@ Rank 0 prints one JSON line:
   three whose K and V fit in the 256 MB Infinity Cache the median time with
   512 MB written between routes (cache flushed);
 * flare, backward, spectrum = fixed-query FLARE (route/FLARE time ratio), the
-  float32 backward and the mixing-matrix spectrum on the same inputs;
+  backward (bf16 inputs on the matrix cores, and float32 copies on the float32
+  path, each with its time over the forward route's) and the mixing-matrix
+  spectrum on the same inputs;
 * cpu_baseline = the oracle (single-threaded C, fp64) on a bounded sample of
   the same problem, with the host's core count and CPU model.
 
@@ -302,37 +304,45 @@ def cpu_baseline(p, n_sample: int) -> dict:
     return rec
 
 
-def backward_record(fp, torch, r: Route, steps: int) -> dict:
-    """flarepp_route_backward (float32) on float32 copies of the same inputs."""
+def backward_record(fp, torch, r: Route, steps: int, route_ms: float) -> dict:
+    """flarepp_route_backward on the same inputs (bf16, matrix cores) and on
+    float32 copies of them (float32 vector path), with a seeded dY."""
     p = r.p
-    Sf, Kf, Vf = r.S.float(), r.K.float(), r.V.float()
-    dY = torch.randn(Kf.shape, generator=torch.Generator(device="cuda").manual_seed(7), device="cuda")
-    dS, dK, dV = torch.empty_like(Sf), torch.empty_like(Kf), torch.empty_like(Vf)
-    bdesc = fp.desc_for(Sf, Kf, p.scale)
-    bbytes = fp.flarepp_workspace_size(bdesc, fp.OP_ROUTE_BACKWARD)
-    bws = torch.empty(max(bbytes, 1), dtype=torch.uint8, device="cuda")
-    bptr = [t.data_ptr() for t in (Sf, Kf, Vf, dY, dS, dK, dV)]
-
-    def bstep():
-        st = fp.flarepp_route_backward(bdesc, *bptr, bws.data_ptr(), bbytes, r.stream)
-        if st != 0:
-            raise fp.FlareppError(st, "flarepp_route_backward")
-
-    bstep()
-    torch.cuda.synchronize()
-    bms = statistics.median(time_steps(bstep, torch, r.stream, steps))
+    dY = torch.randn(r.K.shape, generator=torch.Generator(device="cuda").manual_seed(7), device="cuda")
     th = p.B * p.H * p.N
-    bflops = 30.0 * p.M * p.D * th  # 3 stages x 10 M D (logits, dP, dV, dQ, dK)
-    btf = bflops / (bms * 1e-3) / 1e12
-    log(f"[bench] backward (float32): {bms:.2f} ms/step, {btf:.2f} TFLOP/s algorithmic")
-    return {
-        "op": "flarepp_route_backward", "dtype": "f32",
-        "workload": f"{p.name} shapes, float32 copies of the inputs, seeded dY",
-        "steps": steps, "ms_per_step": bms, "value": th / (bms * 1e-3), "unit": "token*heads/s",
-        "roofline": {"bound": "alu", "achieved": round(btf, 2), "peak": FP32_VECTOR_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(btf / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": None,
-                     "algorithmic_flops_per_step": bflops},
-    }
+    flops = 30.0 * p.M * p.D * th  # 3 stages x 10 M D (logits, dP, dV, dQ, dK)
+    out = {"op": "flarepp_route_backward", "workload": f"{p.name} shapes, seeded dY", "steps": steps,
+           "algorithmic_flops_per_step": flops}
+    for label, cast in (("bf16", lambda t: t), ("f32", lambda t: t.float())):
+        S, K, V = cast(r.S), cast(r.K), cast(r.V)
+        dS = torch.empty(S.shape, dtype=torch.float32, device="cuda")
+        dK = torch.empty(K.shape, dtype=torch.float32, device="cuda")
+        dV = torch.empty(K.shape, dtype=torch.float32, device="cuda")
+        bdesc = fp.desc_for(S, K, p.scale)
+        bbytes = fp.flarepp_workspace_size(bdesc, fp.OP_ROUTE_BACKWARD)
+        bws = torch.empty(max(bbytes, 1), dtype=torch.uint8, device="cuda")
+        bptr = [t.data_ptr() for t in (S, K, V, dY, dS, dK, dV)]
+
+        def bstep():
+            st = fp.flarepp_route_backward(bdesc, *bptr, bws.data_ptr(), bbytes, r.stream)
+            if st != 0:
+                raise fp.FlareppError(st, "flarepp_route_backward")
+
+        bstep()
+        torch.cuda.synchronize()
+        bms = statistics.median(time_steps(bstep, torch, r.stream, steps))
+        btf = flops / (bms * 1e-3) / 1e12
+        peak = BF16_PEAK_TFLOPS if label == "bf16" else FP32_VECTOR_PEAK_TFLOPS
+        log(f"[bench] backward ({label}): {bms:.2f} ms/step, {btf:.2f} TFLOP/s algorithmic, "
+            f"{bms / route_ms:.2f} x the forward route")
+        out[label] = {
+            "ms_per_step": bms, "value": th / (bms * 1e-3), "unit": "token*heads/s",
+            "over_forward_route": round(bms / route_ms, 3),
+            "roofline": {"bound": "mfma" if label == "bf16" else "alu", "achieved": round(btf, 2), "peak": peak,
+                         "unit": "TFLOP/s", "frac": round(btf / peak, 4), "traffic": None},
+        }
+        del bws, dS, dK, dV
+    return out
 
 
 def spectrum_record(fp, torch, r: Route, steps: int) -> dict:
@@ -475,7 +485,7 @@ def main() -> int:
     for name in names:
         configs[name] = config_record(fp, torch, inputs, name, args.steps, args.warmup)
 
-    bwd = backward_record(fp, torch, r, args.backward_steps) if args.backward_steps > 0 else None
+    bwd = backward_record(fp, torch, r, args.backward_steps, ms) if args.backward_steps > 0 else None
     spec = spectrum_record(fp, torch, r, args.spectrum_steps) if args.spectrum_steps > 0 else None
 
     if args.calibrate_copy > 0:

@@ -176,9 +176,12 @@ flarepp_status flarepp_flare(const flarepp_desc *desc, const void *Q, const void
  * O = softmax(s Q K^T) V with upstream dO: dV = P^T dO, dL = P o (dO V^T -
  * rowsum(dO o O)), dQ = s dL K, dK = s dL^T Q.  The pages measure FLARE++
  * per training step (French technical summary, "Résultats"), i.e. forward
- * and this backward.  FLAREPP_F32 descriptors only (FLAREPP_UNSUPPORTED
- * otherwise); float32 arithmetic.  Workspace: flarepp_workspace_size with
- * FLAREPP_OP_ROUTE_BACKWARD.  Inputs S, K, V, dY; outputs dS, dK, dV must
+ * and this backward.  Both dtypes: S, K, V in the descriptor's dtype, dY and
+ * the gradients fp32.  FLAREPP_F32: float32 vector arithmetic.  FLAREPP_BF16:
+ * matrix-core products with float32 accumulation (logits from a bf16 hi/lo
+ * query, gradient products from bf16 operands and weights) after the
+ * route's own forward stages 1 and 2.  M <= 256.  Workspace:
+ * flarepp_workspace_size with FLAREPP_OP_ROUTE_BACKWARD.  Inputs S, K, V, dY; outputs dS, dK, dV must
  * not overlap them, each other or the workspace.
  */
 flarepp_status flarepp_route_backward(const flarepp_desc *desc, const void *S, const void *K,
@@ -196,9 +199,11 @@ flarepp_status flarepp_route_backward(const flarepp_desc *desc, const void *S, c
  * ранга").  Because both factors are softmaxes of the same logits, W_enc
  * W_dec is similar to the symmetric positive semidefinite G = F F^T with
  * F_mn = sqrt(W_enc[m, n] W_dec[n, m]); its eigenvalues are real, in
- * [0, 1], the largest 1.  The library forms G on the GPU (O(M^2 N)) and finds
- * its eigenvalues by cyclic Jacobi (float32; off-diagonal norm below 1e-6 of
- * the whole, or 30 sweeps).
+ * [0, 1], the largest 1.  The library forms G on the GPU (O(M^2 N); for
+ * bf16 inputs on the matrix cores with F rounded to fp16, for float32 inputs
+ * in float32) and finds its eigenvalues by Householder reduction to
+ * tridiagonal form and bisection (float32; each eigenvalue to about 2 ulp of
+ * the largest).
  *   eig (output): B x H x M fp32, each head's eigenvalues by decreasing value.
  *   sym_out (optional output): B x H x M x M fp32, the matrix G.
  * Both dtypes; workspace: flarepp_workspace_size with FLAREPP_OP_SPECTRUM.

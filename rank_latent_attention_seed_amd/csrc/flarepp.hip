@@ -18,6 +18,7 @@
 #include <cmath>
 #include <cstdint>
 #include <mutex>
+#include <type_traits>
 
 #include "flarepp.h"
 #include "common.h"
@@ -25,6 +26,7 @@
 #include "encode_bf16.h"
 #include "f32_path.h"
 #include "merge.h"
+#include "backward_bf16.h"
 #include "backward_f32.h"
 #include "spectral.h"
 
@@ -54,8 +56,12 @@ struct Plan {
   int tpr;          // threads per latent row in the merge
   int dchunk;       // tokens per decode workgroup (bf16)
   bool dpair;       // paired decode (two waves per token block)
-  // backward (float32) workspace regions
+  // backward workspace regions
   size_t o_lse1, o_lse2, o_tlse, o_tdel, o_dz, o_dq3, o_dq, o_del;
+  // bf16 backward: latent operands as bf16 (rows [G][Mp][D], transposed [.][D][Mt]),
+  // Mt = M rounded up to 32, tokens per token-pass workgroup
+  int Mt, tchunk;
+  size_t o_zh, o_zl, o_zt2, o_qdt, o_dzt, o_dqt, o_st, o_dzr, o_dzl, o_dqr, o_dql;
   // spectrum: Gram partials [G][Jg][M][M] over Jg token splits of gchunk, and the reduced [G][M][M]
   int Jg, gchunk;
   size_t o_gpart, o_mat;
@@ -172,8 +178,46 @@ Plan make_plan(const flarepp_desc* d, int op, const flarepp_tuning* t = nullptr)
   p.o_shi = p.o_slo = p.o_sqn = p.o_part = p.o_knorm = p.o_qhi = p.o_qlo = p.o_qnorm = p.o_bias =
       p.o_zt = p.o_qf = p.o_zf = none;
   p.o_lse1 = p.o_lse2 = p.o_tlse = p.o_tdel = p.o_dz = p.o_dq3 = p.o_dq = p.o_del = none;
+  p.o_zh = p.o_zl = p.o_zt2 = p.o_qdt = p.o_dzt = p.o_dqt = p.o_st = p.o_dzr = p.o_dzl = p.o_dqr = p.o_dql = none;
+  p.Mt = (int)cdiv(d->M, 32) * 32;
+  {
+    // token passes of the bf16 backward: one workgroup per CU over the group
+    const int64_t wgs = std::max<int64_t>(1, cdiv(int64_t(kComputeUnits), G));
+    p.tchunk = (int)(cdiv(cdiv(d->N, wgs), 256) * 256);
+  }
   p.o_gpart = p.o_mat = none;
-  if (bwd) {  // float32 only (checked by the entry point)
+  if (bwd && p.bf16) {
+    const size_t trn = D * (size_t)p.Mt * 2;  // one bf16 [D][Mt] block
+    p.o_shi = take(p.nS * opnd);
+    p.o_slo = take(p.nS * opnd);
+    p.o_part = take(G_ * p.J * Mp * std::max<size_t>(D + 4, 2 * D) * 4);
+    p.o_knorm = take(G_ * p.J * 4);
+    p.o_qhi = take(G_ * opnd);
+    p.o_qlo = take(G_ * opnd);
+    p.o_qnorm = take(G_ * Mp * 4);
+    p.o_bias = take(G_ * Mp * 4);
+    p.o_qf = take(G_ * p.M * D * 4);
+    p.o_zf = take(G_ * p.M * D * 4);
+    p.o_lse1 = take(G_ * Mp * 4);
+    p.o_lse2 = take(G_ * Mp * 4);
+    p.o_tlse = take(G_ * (size_t)p.N * 4);
+    p.o_tdel = take(G_ * (size_t)p.N * 4);
+    p.o_dz = take(G_ * p.M * D * 4);
+    p.o_dq3 = take(G_ * p.M * D * 4);
+    p.o_dq = take(G_ * p.M * D * 4);
+    p.o_del = take(G_ * Mp * 4);
+    p.o_zh = take(G_ * opnd);
+    p.o_zl = take(G_ * opnd);
+    p.o_zt2 = take(G_ * trn);
+    p.o_qdt = take(G_ * trn);
+    p.o_dzt = take(G_ * trn);
+    p.o_dqt = take(G_ * trn);
+    p.o_st = take(p.nS * trn);
+    p.o_dzr = take(G_ * opnd);
+    p.o_dzl = take(G_ * opnd);
+    p.o_dqr = take(G_ * opnd);
+    p.o_dql = take(G_ * opnd);
+  } else if (bwd) {
     p.o_part = take(G_ * p.J * Mp * std::max<size_t>(D + 4, 2 * D) * 4);
     p.o_qf = take(G_ * p.M * D * 4);
     p.o_zf = take(G_ * p.M * D * 4);
@@ -211,7 +255,7 @@ Plan make_plan(const flarepp_desc* d, int op, const flarepp_tuning* t = nullptr)
   if (spec) {
     if (p.o_qf == none) p.o_qf = take(G_ * p.M * D * 4);
     p.o_lse2 = take(G_ * Mp * 4);
-    p.o_tlse = take(G_ * (size_t)p.N * 4);
+    if (!p.bf16) p.o_tlse = take(G_ * (size_t)p.N * 4);  // the bf16 path forms B_n in the Gram pass
     p.o_gpart = take(G_ * p.Jg * (size_t)p.M * p.M * 4);
     p.o_mat = take(G_ * (size_t)p.M * p.M * 4);
   }
@@ -447,25 +491,34 @@ EncodeArgs encode_args(const Plan& p, void* ws, const void* K, const void* V, in
 enum Stage { kSeed, kEncode, kDecode, kRoute, kFlare, kSpectrum };
 
 // Spectrum of one launch group (stages 1 and 2 already ran: Qd rows in the
-// o_qf staging buffer, the encode's log-sum-exp in o_lse2).
+// o_qf staging buffer and, for bf16 inputs, c * Qd as bf16 hi/lo in
+// o_qhi / o_qlo; the encode's log-sum-exp in o_lse2).
 template <int D, typename KT>
 flarepp_status run_spectral(const Plan& p, const void* K, int64_t g0, int Gc, void* ws, float* eig, float* sym_out,
                             hipStream_t st) {
-  float* qf = at<float>(ws, p.o_qf);
-  float* tlse = at<float>(ws, p.o_tlse);
   float* gpart = at<float>(ws, p.o_gpart);
   float* mat = at<float>(ws, p.o_mat);
-  SpecTokArgs t{qf, K, tlse, p.H, p.N, p.M, g0, p.c};
-  spectral_tokens<D, KT><<<dim3((unsigned)cdiv(p.N, 256), (unsigned)Gc), 256, 0, st>>>(t);
-  FLAREPP_TRY(launched());
-  SpecGramArgs g{qf, K, at<float>(ws, p.o_lse2), tlse, gpart, p.H, p.N, p.M, p.Mp, p.Jg, p.gchunk, g0, p.c};
-  spectral_gram<D, KT><<<dim3((unsigned)p.Jg, (unsigned)Gc), 1024, 0, st>>>(g);
-  FLAREPP_TRY(launched());
+  const float* lse = at<float>(ws, p.o_lse2);
+  if constexpr (std::is_same<KT, __bf16>::value) {
+    SpecMfmaArgs g{at<__bf16>(ws, p.o_qhi), at<__bf16>(ws, p.o_qlo), static_cast<const __bf16*>(K), lse, gpart,
+                   p.N, p.M, p.Mp, p.Jg, p.gchunk, g0};
+    spectral_gram_mfma<D><<<dim3((unsigned)p.Jg, (unsigned)Gc), 512, 0, st>>>(g);
+    FLAREPP_TRY(launched());
+  } else {
+    float* qf = at<float>(ws, p.o_qf);
+    float* tlse = at<float>(ws, p.o_tlse);
+    SpecTokArgs t{qf, K, tlse, p.H, p.N, p.M, g0, p.c};
+    spectral_tokens<D, KT><<<dim3((unsigned)cdiv(p.N, 256), (unsigned)Gc), 256, 0, st>>>(t);
+    FLAREPP_TRY(launched());
+    SpecGramArgs g{qf, K, lse, tlse, gpart, p.H, p.N, p.M, p.Mp, p.Jg, p.gchunk, g0, p.c};
+    spectral_gram<D, KT><<<dim3((unsigned)p.Jg, (unsigned)Gc), 1024, 0, st>>>(g);
+    FLAREPP_TRY(launched());
+  }
   SpecReduceArgs r{gpart, mat, sym_out, Gc, p.Jg, p.M, g0};
   spectral_reduce<<<(unsigned)cdiv((int64_t)Gc * p.M * p.M, 256), 256, 0, st>>>(r);
   FLAREPP_TRY(launched());
-  JacobiArgs j{mat, eig, p.M, 30, g0, 1e-6f};
-  jacobi_eigvals<<<(unsigned)Gc, 256, 0, st>>>(j);
+  EigArgs e{mat, eig, p.M, g0};
+  tridiag_eigvals<<<(unsigned)Gc, 1024, 0, st>>>(e);
   return launched();
 }
 
@@ -814,6 +867,181 @@ flarepp_status run_backward(const Plan& p, const float* S, const float* K, const
   return FLAREPP_OK;
 }
 
+// Backward of the route (bf16 inputs, matrix cores): the forward's stages 1
+// and 2 as the route runs them, keeping Qd, Z and the log-sum-exp of both
+// encodes; then per stage in reverse order the token pass (dK, dV), the
+// latent pass (split partials) and their reduction, with the latent
+// operands of each stage converted to bf16 rows and transposes first.
+template <int D>
+flarepp_status run_backward_bf16(const Plan& p, const void* S, const void* K, const void* V, const float* dY,
+                                 float* dS, float* dK, float* dV, void* ws, hipStream_t st) {
+  Recorder rec;
+  const int64_t MD = (int64_t)p.M * D, MpD = (int64_t)p.Mp * D, DMt = (int64_t)D * p.Mt;
+  const int64_t seed_h = p.nS > 1 ? MD : 0;
+  fill_zero<<<(unsigned)cdiv((int64_t)p.nS * MD, 256), 256, 0, st>>>(dS, (int64_t)p.nS * MD);
+  FLAREPP_TRY(launched());
+  __bf16* shi = at<__bf16>(ws, p.o_shi);
+  __bf16* slo = at<__bf16>(ws, p.o_slo);
+  __bf16* qhi = at<__bf16>(ws, p.o_qhi);
+  __bf16* qlo = at<__bf16>(ws, p.o_qlo);
+  float* qf = at<float>(ws, p.o_qf);
+  float* zf = at<float>(ws, p.o_zf);
+  float* part = at<float>(ws, p.o_part);
+  float* dz = at<float>(ws, p.o_dz);
+  float* dq3 = at<float>(ws, p.o_dq3);
+  float* dq = at<float>(ws, p.o_dq);
+  float* del = at<float>(ws, p.o_del);
+  __bf16* zh = at<__bf16>(ws, p.o_zh);
+  __bf16* zl = at<__bf16>(ws, p.o_zl);
+  __bf16* zt = at<__bf16>(ws, p.o_zt2);
+  __bf16* qdt = at<__bf16>(ws, p.o_qdt);
+  __bf16* dzt = at<__bf16>(ws, p.o_dzt);
+  __bf16* dqt = at<__bf16>(ws, p.o_dqt);
+  __bf16* sT = at<__bf16>(ws, p.o_st);
+  __bf16* dzr = at<__bf16>(ws, p.o_dzr);
+  __bf16* dzl = at<__bf16>(ws, p.o_dzl);
+  __bf16* dqr = at<__bf16>(ws, p.o_dqr);
+  __bf16* dql = at<__bf16>(ws, p.o_dql);
+  auto prep = [&](const void* src, bool src_bf16, int64_t src_blk, int nblk, bool center, float alpha, __bf16* hi,
+                  __bf16* lo, __bf16* tr) {
+    BwdPrepArgs a{src, src_bf16 ? 1 : 0, src_blk, p.M, p.Mp, p.Mt, center ? 1 : 0, alpha, hi, lo, tr};
+    bwd_prep_bf16<D><<<(unsigned)nblk, 256, 0, st>>>(a);
+    return launched();
+  };
+  // seed operands (c S as hi/lo for the forward, S^T for stage 1's dK)
+  FLAREPP_TRY(run_prep<D>(p, S, true, 0, seed_h, p.nS, shi, slo, nullptr, nullptr, p.c, st, rec));
+  FLAREPP_TRY(prep(S, true, seed_h, p.nS, false, 1.0f, nullptr, nullptr, sT));
+  for (int64_t g0 = 0; g0 < p.BH; g0 += p.G) {
+    const int Gc = (int)std::min<int64_t>(p.G, p.BH - g0);
+    // ---- forward stages 1 and 2, as in the route
+    {
+      EncodeArgs e = encode_args(p, ws, K, V, g0);
+      e.q_hi = shi;
+      e.q_lo = slo;
+      e.q_sb = 0;
+      e.q_sh = p.nS > 1 ? MpD : 0;
+      e.q_off = 0;
+      e.knorm = at<float>(ws, p.o_knorm);
+      FLAREPP_TRY((run_encode_bf16<D, true, false>(p, e, Gc, st, rec, FLAREPP_KERNEL_SEED_ENCODE)));
+      MergeArgs m = merge_args(p, ws, g0);
+      refit_from(m, e);
+      m.outl = qf;
+      m.op_hi = qhi;
+      m.op_lo = qlo;
+      m.qnorm = at<float>(ws, p.o_qnorm);
+      m.knorm = e.knorm;
+      m.Jk = p.J;
+      m.bias = at<float>(ws, p.o_bias);
+      m.lse = at<float>(ws, p.o_lse1);
+      FLAREPP_TRY(run_merge<D>(p, m, Gc, st, rec));
+      EncodeArgs e2 = encode_args(p, ws, K, V, g0);
+      e2.q_hi = qhi;
+      e2.q_lo = qlo;
+      e2.q_sb = (int64_t)p.H * MpD;
+      e2.q_sh = MpD;
+      e2.q_off = g0 * MpD;
+      e2.bias = at<float>(ws, p.o_bias);
+      FLAREPP_TRY((run_encode_bf16<D, false, true>(p, e2, Gc, st, rec, FLAREPP_KERNEL_ENCODE)));
+      MergeArgs m2 = merge_args(p, ws, g0);
+      m2.outl = zf;
+      m2.lse = at<float>(ws, p.o_lse2);
+      FLAREPP_TRY(run_merge<D>(p, m2, Gc, st, rec));
+    }
+    auto reduce = [&](int R, int field0, const float* add_to, float* out, const float* dot_with, float* delta,
+                      int seed_blocks) {
+      BwdReduceArgs r{part, p.J, R, field0, p.M, p.Mp, Gc, p.H, g0, add_to, out, dot_with, delta, seed_blocks};
+      const int64_t rows = (int64_t)(seed_blocks ? seed_blocks : Gc) * p.M;
+      bwd_reduce<D><<<(unsigned)cdiv(rows * D, 256), 256, 0, st>>>(r);
+      return launched();
+    };
+    const dim3 tok_grid((unsigned)cdiv(p.N, p.tchunk), (unsigned)Gc);
+    const dim3 lat_grid((unsigned)p.J, (unsigned)Gc);
+    // ---- stage 3 (decode)
+    FLAREPP_TRY(prep(zf, false, MD, Gc, true, 1.0f, zh, zl, zt));
+    FLAREPP_TRY(prep(qf, false, MD, Gc, false, 1.0f, nullptr, nullptr, qdt));
+    {
+      BwdDecArgs d{};
+      d.qhi = qhi;
+      d.qlo = qlo;
+      d.qdt = qdt;
+      d.zh = zh;
+      d.zl = zl;
+      d.zt = zt;
+      d.K = static_cast<const __bf16*>(K);
+      d.dY = dY;
+      d.dK = dK;
+      d.tA = at<float>(ws, p.o_tlse);
+      d.tD = at<float>(ws, p.o_tdel);
+      d.part = part;
+      d.J = p.J;
+      d.chunk = p.chunk;
+      d.tchunk = p.tchunk;
+      d.N = p.N;
+      d.M = p.M;
+      d.Mp = p.Mp;
+      d.Mt = p.Mt;
+      d.bh0 = g0;
+      d.s = p.s;
+      bwd_dec_tok_bf16<D><<<tok_grid, 512, 0, st>>>(d);
+      FLAREPP_TRY(launched());
+      bwd_dec_lat_bf16<D><<<lat_grid, 512, 0, st>>>(d);
+      FLAREPP_TRY(launched());
+      FLAREPP_TRY(reduce(2 * D, D, nullptr, dz, zf, del, 0));            // dZ, delta_2 = <dZ, Z>
+      FLAREPP_TRY(reduce(2 * D, 0, nullptr, dq3, nullptr, nullptr, 0));  // dQd from the decode
+    }
+    // ---- stages 2 and 1
+    auto enc_stage = [&](const __bf16* hi, const __bf16* lo, int64_t q_sb, int64_t q_sh, int64_t q_off,
+                         const __bf16* qt, int64_t t_sb, int64_t t_sh, int64_t t_off, const __bf16* dor,
+                         const __bf16* dorl, const __bf16* dot, const float* lse, int acc_dv) {
+      BwdEncArgs e{};
+      e.qhi = hi;
+      e.qlo = lo;
+      e.q_sb = q_sb;
+      e.q_sh = q_sh;
+      e.q_off = q_off;
+      e.qt = qt;
+      e.t_sb = t_sb;
+      e.t_sh = t_sh;
+      e.t_off = t_off;
+      e.dor = dor;
+      e.dorl = dorl;
+      e.dot = dot;
+      e.lse = lse;
+      e.delta = del;
+      e.K = static_cast<const __bf16*>(K);
+      e.V = static_cast<const __bf16*>(V);
+      e.dK = dK;
+      e.dV = dV;
+      e.acc_dk = 1;  // the decode wrote dK first
+      e.acc_dv = acc_dv;
+      e.part = part;
+      e.J = p.J;
+      e.chunk = p.chunk;
+      e.tchunk = p.tchunk;
+      e.H = p.H;
+      e.N = p.N;
+      e.M = p.M;
+      e.Mp = p.Mp;
+      e.Mt = p.Mt;
+      e.bh0 = g0;
+      e.s = p.s;
+      bwd_enc_tok_bf16<D><<<tok_grid, 512, 0, st>>>(e);
+      FLAREPP_TRY(launched());
+      bwd_enc_lat_bf16<D><<<lat_grid, 512, 0, st>>>(e);
+      return launched();
+    };
+    FLAREPP_TRY(prep(dz, false, MD, Gc, false, 1.0f, dzr, dzl, dzt));
+    FLAREPP_TRY(enc_stage(qhi, qlo, (int64_t)p.H * MpD, MpD, g0 * MpD, qdt, (int64_t)p.H * DMt, DMt, g0 * DMt, dzr,
+                          dzl, dzt, at<float>(ws, p.o_lse2), 0));
+    FLAREPP_TRY(reduce(D, 0, dq3, dq, qf, del, 0));  // dQd = encode + decode parts, delta_1 = <dQd, Qd>
+    FLAREPP_TRY(prep(dq, false, MD, Gc, false, 1.0f, dqr, dql, dqt));
+    FLAREPP_TRY(enc_stage(shi, slo, 0, p.nS > 1 ? MpD : 0, 0, sT, 0, p.nS > 1 ? DMt : 0, 0, dqr, dql, dqt,
+                          at<float>(ws, p.o_lse1), 1));
+    FLAREPP_TRY(reduce(D, 0, nullptr, dS, nullptr, nullptr, p.nS));
+  }
+  return FLAREPP_OK;
+}
+
 flarepp_status dispatch(const Plan& p, Stage stage, const void* S, const float* Qd_in, const float* Z_in,
                         const void* K, const void* V, float* Y, float* Qd_out, float* Z_out, void* ws,
                         void* stream, Recorder* recorder = nullptr) {
@@ -927,7 +1155,7 @@ flarepp_status flarepp_workspace_size(const flarepp_desc* desc, int32_t op, size
   if (!bytes) return FLAREPP_INVALID_ARG;
   FLAREPP_TRY(check_desc(desc));
   if (op < FLAREPP_OP_SEED_ENCODE || op > FLAREPP_OP_SPECTRUM) return FLAREPP_INVALID_ARG;
-  if (op == FLAREPP_OP_ROUTE_BACKWARD && desc->dtype != FLAREPP_F32) return FLAREPP_UNSUPPORTED;
+  if (op == FLAREPP_OP_ROUTE_BACKWARD && desc->M > kBwdBf16MaxM) return FLAREPP_UNSUPPORTED;
   *bytes = make_plan(desc, op).total;
   return FLAREPP_OK;
 }
@@ -938,7 +1166,7 @@ flarepp_status flarepp_workspace_size_tuned(const flarepp_desc* desc, int32_t op
   FLAREPP_TRY(check_desc(desc));
   FLAREPP_TRY(check_tuning(tuning));
   if (op < FLAREPP_OP_SEED_ENCODE || op > FLAREPP_OP_SPECTRUM) return FLAREPP_INVALID_ARG;
-  if (op == FLAREPP_OP_ROUTE_BACKWARD && desc->dtype != FLAREPP_F32) return FLAREPP_UNSUPPORTED;
+  if (op == FLAREPP_OP_ROUTE_BACKWARD && desc->M > kBwdBf16MaxM) return FLAREPP_UNSUPPORTED;
   *bytes = make_plan(desc, op, tuning).total;
   return FLAREPP_OK;
 }
@@ -1066,7 +1294,7 @@ flarepp_status flarepp_route_backward(const flarepp_desc* desc, const void* S, c
                                       const float* dY, float* dS, float* dK, float* dV, void* ws, size_t ws_bytes,
                                       void* stream) {
   FLAREPP_TRY(check_desc(desc));
-  if (desc->dtype != FLAREPP_F32) return FLAREPP_UNSUPPORTED;
+  if (desc->M > kBwdBf16MaxM) return FLAREPP_UNSUPPORTED;
   const Sizes z = sizes(desc);
   const void* in[4] = {S, K, V, dY};
   const size_t inb[4] = {z.s, z.kv, z.kv, z.y};
@@ -1076,6 +1304,10 @@ flarepp_status flarepp_route_backward(const flarepp_desc* desc, const void* S, c
   Plan p;
   FLAREPP_TRY(prologue(desc, FLAREPP_OP_ROUTE_BACKWARD, in, inb, 4, out, outb, req, 3, ws, ws_bytes, &p));
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (p.bf16) {
+    if (p.D == 16) return run_backward_bf16<16>(p, S, K, V, dY, dS, dK, dV, ws, st);
+    return run_backward_bf16<32>(p, S, K, V, dY, dS, dK, dV, ws, st);
+  }
   const float *Sf = static_cast<const float*>(S), *Kf = static_cast<const float*>(K),
               *Vf = static_cast<const float*>(V);
   if (p.D == 16) return run_backward<16>(p, Sf, Kf, Vf, dY, dS, dK, dV, ws, st);

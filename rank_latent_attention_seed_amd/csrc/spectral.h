@@ -10,10 +10,14 @@
 // which is similar (by D_A^1/2) to the symmetric positive semidefinite
 //     G = F F^T,   F_mn = 2^(t_mn - (A_m + B_n) / 2),
 // so the spectrum is real, in [0, 1] (C is row-stochastic), and equals the
-// eigenvalues of G.  The kernels form G in O(M^2 N) (split over tokens) and
-// find its eigenvalues with a parallel cyclic Jacobi iteration in O(M^3).
-// Float32 arithmetic throughout.
+// eigenvalues of G.  The kernels form G in O(M^2 N), split over tokens (for
+// bf16 inputs on the matrix cores, with B_n formed in the same pass; for
+// float32 inputs in float32 on the VALU), and find its eigenvalues in
+// O(M^3): Householder reduction to tridiagonal form in LDS, then bisection
+// with Sturm counts.
 #pragma once
+
+#include <float.h>
 
 #include "common.h"
 
@@ -182,119 +186,400 @@ __global__ __launch_bounds__(256) void spectral_reduce(SpecReduceArgs a) {
   if (a.sym_out) a.sym_out[(a.bh0 + lbh) * mm + e] = s;
 }
 
-// Eigenvalues of the symmetric G[lbh] (overwritten) by cyclic Jacobi: in each
-// round the M (rounded up to even) indices form disjoint pairs (round-robin
-// tournament, a "bye" for the padding index); every pair's rotation
-// J = [[c, s], [-s, c]] with t = tan(theta) from
-// tau = (a_qq - a_pp) / (2 a_pq), t = sign(tau) / (|tau| + sqrt(1 + tau^2))
-// zeroes a_pq (Golub & Van Loan, the symmetric Schur decomposition), and
-// A <- J^T A J is applied to all pairs at once, rows first, then columns
-// (disjoint rotations commute).  A sweep is M - 1 rounds (every pair once);
-// sweeps repeat until the off-diagonal Frobenius norm is below tol times the
-// whole norm, at most max_sweeps times.  Output: eigenvalues by decreasing
-// value, eig[(bh0 + lbh) * M ...].
-struct JacobiArgs {
-  float* mat;  // [G][M][M]
-  float* eig;  // [BH][M]
-  int M, max_sweeps;
+// ---- bf16 inputs: B_n and the Gram partials in one pass on the matrix cores.
+//
+// Workgroup (split j, head lbh), eight waves, 32 tokens per step.  Wave w
+// forms the logits of latent blocks 2w, 2w + 1 (16 latents each) as
+// S^T = K (c Qd)^T with the query as a bf16 hi/lo pair (the operands the
+// encode used, so A_m and these logits agree); its C tiles leave each lane
+// one latent and eight tokens, which is exactly a 16x16x32 MFMA operand over
+// the step's 32 tokens (common.h).  The decode log-sum-exp of every token
+// combines a (max, sum) pair per wave through LDS; then
+// F_mn 2^15 = 2^(t_mn - A_m / 2 - B_n / 2 + 15) is rounded to fp16 (F <= 1,
+// so the scaled value stays below fp16's largest finite 65504 and keeps
+// fp16's full 11-bit precision down to F = 2^-29) and written to LDS as
+// operand fragments.  The Gram product G += F F^T then runs as 16x16x32 fp16
+// MFMAs over 16x16 tiles of the upper triangle, grouped into 4x4 super-blocks
+// (four diagonal super-blocks of 10 tiles, six off-diagonal ones of 16) so
+// that each wave reads 8 fragments per step for 16 or 20 MFMAs.  The result
+// is scaled by 2^-30 when written; mirrored tiles complete the symmetric
+// matrix.
+struct SpecMfmaArgs {
+  const __bf16* qhi;  // [G][Mp][D] bf16 hi of c * Qd (log2 units)
+  const __bf16* qlo;  // [G][Mp][D] bf16 lo
+  const __bf16* K;    // B x H x N x D
+  const float* lse;   // encode log-sum-exp A_m, [G][Mp]
+  float* part;        // [G][J][M][M]
+  int N, M, Mp, J, chunk;
   int64_t bh0;
-  float tol;
 };
 
-__global__ __launch_bounds__(256) void jacobi_eigvals(JacobiArgs a) {
-  __shared__ float sc[kSpecMaxM / 2], ss[kSpecMaxM / 2];
-  __shared__ int sp[kSpecMaxM / 2], sq[kSpecMaxM / 2];
-  __shared__ float sred[2][4];
-  __shared__ float sdiag[kSpecMaxM];
+// Super-block jobs by number of 64-latent groups (ng = ceil(Mp / 64)) and
+// wave: a first job (I, J), I == J for a diagonal super-block, and an
+// optional second diagonal one; -1 for none.
+__constant__ const int8_t kSpecJobI[4][8] = {
+    {0, -1, -1, -1, -1, -1, -1, -1}, {0, 0, 1, -1, -1, -1, -1, -1}, {0, 0, 1, 0, 1, 2, -1, -1}, {0, 0, 0, 1, 1, 2, 0, 2}};
+__constant__ const int8_t kSpecJobJ[4][8] = {
+    {0, -1, -1, -1, -1, -1, -1, -1}, {1, 0, 1, -1, -1, -1, -1, -1}, {1, 2, 2, 0, 1, 2, -1, -1}, {1, 2, 3, 2, 3, 3, 0, 2}};
+__constant__ const int8_t kSpecJob2[4][8] = {
+    {-1, -1, -1, -1, -1, -1, -1, -1}, {-1, -1, -1, -1, -1, -1, -1, -1}, {-1, -1, -1, -1, -1, -1, -1, -1},
+    {-1, -1, -1, -1, -1, -1, 1, 3}};
+
+// max / sum over the 16 lanes of a row (lanes sharing l / 16); every lane of
+// the row gets the result
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));
+  x = fmaxf(x, dpp<0x4E>(x));
+  x = fmaxf(x, dpp<0x124>(x));
+  return fmaxf(x, dpp<0x128>(x));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x124>(x);
+  return x + dpp<0x128>(x);
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void spectral_gram_mfma(SpecMfmaArgs a) {
+  static_assert(D == 16 || D == 32, "head dimension 16 or 32");
+  constexpr int kBlocks = kSpecMaxM / 16;
+  __shared__ __attribute__((aligned(16))) _Float16 sF[kBlocks * 64 * 8];  // [block][lane] fragments
+  __shared__ __attribute__((aligned(16))) float sMu[8 * 32], sLam[8 * 32], sCn[8 * 32];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int j = blockIdx.x;
+  const int64_t lbh = blockIdx.y, bh = a.bh0 + lbh;
+  const int n0 = j * a.chunk, n1 = min(a.N, n0 + a.chunk);
+  const int nb = a.Mp / 16, ng = (nb + 3) / 4;
+  for (int e = tid; e < kBlocks * 64; e += 512) reinterpret_cast<f16x8*>(sF)[e] = f16x8{};
+
+  // this wave's two latent blocks: query operands, validity, F exponent offset
+  bf16x8 qh[2], ql[2];
+  bool valid[2];
+  float cm[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int blk = 2 * w + b, m = 16 * blk + l16;
+    valid[b] = m < a.M;
+    cm[b] = valid[b] ? 15.0f - 0.5f * a.lse[lbh * a.Mp + m] : -INFINITY;
+    qh[b] = bf16x8{};
+    ql[b] = bf16x8{};
+    if (blk < nb) {
+      const __bf16* hp = a.qhi + (lbh * a.Mp + m) * D;
+      const __bf16* lp = a.qlo + (lbh * a.Mp + m) * D;
+      if constexpr (D == 32) {
+        qh[b] = *reinterpret_cast<const bf16x8*>(hp + 8 * g);
+        ql[b] = *reinterpret_cast<const bf16x8*>(lp + 8 * g);
+      } else {  // k slots 0..15 take the hi operand, 16..31 the lo one (K is repeated)
+        qh[b] = *reinterpret_cast<const bf16x8*>((g < 2 ? hp : lp) + 8 * (g & 1));
+      }
+    }
+  }
+  // K rows of a step: lane reads token tb + 16 h + l16, elements 8 (g mod D/8) ..
+  // (a resource from the step's first token, so offsets stay small; tokens
+  // past N read as zeros)
+  const __bf16* khead = a.K + bh * (int64_t)a.N * D;
+  const int kcol = D == 32 ? 8 * g : 8 * (g & 1);
+  auto load_k = [&](int tb, int h) {
+    const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(khead + (int64_t)tb * D, (uint32_t)((int64_t)(a.N - tb) * D * 2));
+    return buffer_load<bf16x8>(kr, ((16 * h + l16) * D + kcol) * 2);
+  };
+
+  const int jobI = kSpecJobI[ng - 1][w], jobJ = kSpecJobJ[ng - 1][w], job2 = kSpecJob2[ng - 1][w];
+  f32x4 acc[20];
+#pragma unroll
+  for (int t = 0; t < 20; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  auto frag = [&](int blk) { return *reinterpret_cast<const f16x8*>(sF + (blk * 64 + lane) * 8); };
+
+  bf16x8 kc0 = load_k(n0, 0), kc1 = load_k(n0, 1);
+  __syncthreads();
+  for (int tb = n0; tb < n1; tb += 32) {
+    const bf16x8 k0 = kc0, k1 = kc1;
+    if (tb + 32 < n1) {
+      kc0 = load_k(tb + 32, 0);
+      kc1 = load_k(tb + 32, 1);
+    }
+    // logits: T[b][h][r] = t(latent 16 (2w + b) + l16, token 16 h + 4 g + r)
+    f32x4 T[2][2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+      T[b][0] = mfma_k32(k0, qh[b], z);
+      T[b][1] = mfma_k32(k1, qh[b], z);
+      if constexpr (D == 32) {
+        T[b][0] = mfma_k32(k0, ql[b], T[b][0]);
+        T[b][1] = mfma_k32(k1, ql[b], T[b][1]);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) T[b][h][r] = valid[b] ? T[b][h][r] : -INFINITY;
+    }
+    // per-token (max, sum) over this wave's latents
+    f32x4 mu[2], lam[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float m = row16_max(fmaxf(T[0][h][r], T[1][h][r]));
+        const float sh = m == -INFINITY ? 0.0f : m;
+        mu[h][r] = m;
+        lam[h][r] = row16_sum(fast_exp2(T[0][h][r] - sh) + fast_exp2(T[1][h][r] - sh));
+      }
+    if (l16 == 0) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        *reinterpret_cast<f32x4*>(sMu + w * 32 + 16 * h + 4 * g) = mu[h];
+        *reinterpret_cast<f32x4*>(sLam + w * 32 + 16 * h + 4 * g) = lam[h];
+      }
+    }
+    __syncthreads();
+    // B_n of token tb + (lane mod 32), then -B_n / 2 (or -inf past the split)
+    {
+      const int t = lane & 31;
+      float m = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 8; ++v) m = fmaxf(m, sMu[v * 32 + t]);
+      float sum = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const float mv = sMu[v * 32 + t];
+        sum += mv == -INFINITY ? 0.0f : sLam[v * 32 + t] * fast_exp2(mv - m);
+      }
+      const float cn = tb + t < n1 ? -0.5f * (m + log2f(sum)) : -INFINITY;
+      if (lane < 32) sCn[w * 32 + t] = cn;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const f32x4 cn0 = *reinterpret_cast<const f32x4*>(sCn + w * 32 + 4 * g);
+    const f32x4 cn1 = *reinterpret_cast<const f32x4*>(sCn + w * 32 + 16 + 4 * g);
+    // F fragments of the wave's blocks
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      if (2 * w + b < nb) {
+        const f16x2 p0 = pack_f16(fast_exp2(T[b][0][0] + cn0[0] + cm[b]), fast_exp2(T[b][0][1] + cn0[1] + cm[b]));
+        const f16x2 p1 = pack_f16(fast_exp2(T[b][0][2] + cn0[2] + cm[b]), fast_exp2(T[b][0][3] + cn0[3] + cm[b]));
+        const f16x2 p2 = pack_f16(fast_exp2(T[b][1][0] + cn1[0] + cm[b]), fast_exp2(T[b][1][1] + cn1[1] + cm[b]));
+        const f16x2 p3 = pack_f16(fast_exp2(T[b][1][2] + cn1[2] + cm[b]), fast_exp2(T[b][1][3] + cn1[3] + cm[b]));
+        *reinterpret_cast<f16x8*>(sF + ((2 * w + b) * 64 + lane) * 8) =
+            f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+      }
+    }
+    __syncthreads();
+    // Gram tiles of this wave's super-blocks
+    if (jobI >= 0) {
+      if (jobI != jobJ) {
+        f16x8 fa[4], fb[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          fa[u] = frag(4 * jobI + u);
+          fb[u] = frag(4 * jobJ + u);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[4 * u + v] = mfma_k32(fa[u], fb[v], acc[4 * u + v]);
+      } else {
+        f16x8 fa[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) fa[u] = frag(4 * jobI + u);
+        int t = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int v = u; v < 4; ++v, ++t) acc[t] = mfma_k32(fa[u], fa[v], acc[t]);
+        if (job2 >= 0) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) fa[u] = frag(4 * job2 + u);
+          t = 10;
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int v = u; v < 4; ++v, ++t) acc[t] = mfma_k32(fa[u], fa[v], acc[t]);
+        }
+      }
+    }
+  }
+  // G partial: c[r] = G[16 bi + 4 g + r][16 bj + l16] (times 2^30)
+  float* out = a.part + (lbh * a.J + j) * (int64_t)a.M * a.M;
+  auto put = [&](int bi, int bj, f32x4 c) {
+    const int col = 16 * bj + l16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * bi + 4 * g + r;
+      if (row < a.M && col < a.M) {
+        const float x = c[r] * 0x1p-30f;
+        out[(int64_t)row * a.M + col] = x;
+        if (bi != bj) out[(int64_t)col * a.M + row] = x;
+      }
+    }
+  };
+  if (jobI >= 0) {
+    if (jobI != jobJ) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) put(4 * jobI + u, 4 * jobJ + v, acc[4 * u + v]);
+    } else {
+      int t = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = u; v < 4; ++v, ++t) put(4 * jobI + u, 4 * jobI + v, acc[t]);
+      if (job2 >= 0) {
+        t = 10;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int v = u; v < 4; ++v, ++t) put(4 * job2 + u, 4 * job2 + v, acc[t]);
+      }
+    }
+  }
+}
+
+// Eigenvalues of the symmetric G[lbh] (its lower triangle), one workgroup per
+// head.  The lower triangle is held packed in LDS (at most 256 * 257 / 2
+// floats, 131.6 KB).  Householder reduction to tridiagonal form (Golub & Van
+// Loan, "Householder tridiagonalization"): for k = 0 .. M - 3 the reflector
+// H = I - beta v v^T with v = x - alpha e_1, alpha = -sign(x_1) ||x||, maps
+// the column x = A[k+1:, k] to alpha e_1; the trailing block becomes
+// H A' H = A' - v w^T - w v^T with p = beta A' v, w = p - (beta v^T p / 2) v.
+// Then every eigenvalue of the tridiagonal (d, e) by bisection on its
+// Gershgorin interval: the number of eigenvalues below x is the number of
+// negative terms of the Sturm sequence q_0 = d_0 - x,
+// q_i = d_i - x - e_{i-1}^2 / q_{i-1} (tiny pivots replaced by -pivmin, as in
+// LAPACK's bisection), one eigenvalue per thread, halving until the interval
+// is below 2 ulp of the spectrum's scale.  Output by decreasing value,
+// eig[(bh0 + lbh) * M ...].
+struct EigArgs {
+  const float* mat;  // [G][M][M]
+  float* eig;        // [BH][M]
+  int M;
+  int64_t bh0;
+};
+
+__device__ __forceinline__ int tri_at(int i, int j) { return i * (i + 1) / 2 + j; }  // j <= i
+
+__global__ __launch_bounds__(1024) void tridiag_eigvals(EigArgs a) {
+  __shared__ float sA[kSpecMaxM * (kSpecMaxM + 1) / 2];
+  __shared__ float sv[kSpecMaxM], sp[kSpecMaxM], sd[kSpecMaxM], se[kSpecMaxM];
+  __shared__ float sred[16];
+  __shared__ float sbeta;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int M = a.M;
-  const int64_t lbh = blockIdx.x;
-  float* A = a.mat + lbh * (int64_t)M * M;
-  const int n = (M + 1) & ~1;
-  const int npairs = n / 2;
-  for (int sweep = 0; sweep < a.max_sweeps; ++sweep) {
-    // convergence test on the current matrix
-    float off = 0.0f, all = 0.0f;
-    for (int e = tid; e < M * M; e += 256) {
-      const float x = A[e];
-      all += x * x;
-      if (e / M != e % M) off += x * x;
-    }
-    off = wave_sum(off);
-    all = wave_sum(all);
-    if (lane == 0) {
-      sred[0][wave] = off;
-      sred[1][wave] = all;
+  const float* A = a.mat + blockIdx.x * (int64_t)M * M;
+  for (int e = tid; e < M * M; e += 1024) {
+    const int i = e / M, j = e - i * M;
+    if (j <= i) sA[tri_at(i, j)] = A[e];
+  }
+  __syncthreads();
+  for (int k = 0; k + 2 < M; ++k) {
+    const int n = M - 1 - k, r0 = k + 1;  // trailing block: rows and columns r0 .. M - 1
+    if (wave == 0) {
+      float x[4], s = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = lane + 64 * q;
+        x[q] = i < n ? sA[tri_at(r0 + i, k)] : 0.0f;
+        if (i >= 1) s = fmaf(x[q], x[q], s);
+      }
+      s = wave_sum(s);
+      const float x0 = sA[tri_at(r0, k)];
+      float alpha = x0, beta = 0.0f, v0 = 0.0f;
+      if (s > 0.0f) {
+        alpha = -copysignf(sqrtf(fmaf(x0, x0, s)), x0);
+        v0 = x0 - alpha;
+        beta = -1.0f / (alpha * v0);  // 2 / v^T v, since v^T v = -2 alpha v0
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = lane + 64 * q;
+        if (i < n) sv[i] = i == 0 ? v0 : x[q];
+      }
+      if (lane == 0) {
+        sbeta = beta;
+        sd[k] = sA[tri_at(k, k)];
+        se[k] = alpha;
+      }
     }
     __syncthreads();
-    const float offt = sred[0][0] + sred[0][1] + sred[0][2] + sred[0][3];
-    const float allt = sred[1][0] + sred[1][1] + sred[1][2] + sred[1][3];
-    __syncthreads();
-    if (!(offt > a.tol * a.tol * allt)) break;
-    for (int r = 0; r < n - 1; ++r) {
-      if (tid < npairs) {
-        int p, q;
-        if (tid == 0) {
-          p = r;
-          q = n - 1;
-        } else {
-          p = (r + tid) % (n - 1);
-          q = (r - tid + n - 1) % (n - 1);
-        }
-        if (p > q) {
-          const int t = p;
-          p = q;
-          q = t;
-        }
-        float c = 1.0f, s = 0.0f;
-        if (q < M) {
-          const float apq = A[(int64_t)p * M + q];
-          if (apq != 0.0f) {
-            const float tau = (A[(int64_t)q * M + q] - A[(int64_t)p * M + p]) / (2.0f * apq);
-            const float t = (tau >= 0.0f ? 1.0f : -1.0f) / (fabsf(tau) + sqrtf(1.0f + tau * tau));
-            c = 1.0f / sqrtf(1.0f + t * t);
-            s = t * c;
+    const float beta = sbeta;
+    if (beta != 0.0f) {
+      // p = beta A' v, rows i = wave, wave + 16, ...; and this wave's part of v^T p
+      float vp = 0.0f;
+      for (int i = wave; i < n; i += 16) {
+        const int gi = r0 + i;
+        float acc = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int jj = lane + 64 * q;
+          if (jj < n) {
+            const int gj = r0 + jj;
+            acc = fmaf(sA[gi >= gj ? tri_at(gi, gj) : tri_at(gj, gi)], sv[jj], acc);
           }
         }
-        sp[tid] = p;
-        sq[tid] = q;
-        sc[tid] = c;
-        ss[tid] = s;
+        acc = beta * wave_sum(acc);
+        if (lane == 0) sp[i] = acc;
+        vp = fmaf(acc, sv[i], vp);
       }
-      __syncthreads();
-      // rows p, q of every pair: A <- J^T A
-      for (int e = tid; e < npairs * M; e += 256) {
-        const int k = e / M, col = e % M;
-        const int p = sp[k], q = sq[k];
-        if (q >= M) continue;
-        const float c = sc[k], s = ss[k];
-        const float ap = A[(int64_t)p * M + col], aq = A[(int64_t)q * M + col];
-        A[(int64_t)p * M + col] = c * ap - s * aq;
-        A[(int64_t)q * M + col] = s * ap + c * aq;
-      }
-      __syncthreads();
-      // columns p, q of every pair: A <- A J
-      for (int e = tid; e < npairs * M; e += 256) {
-        const int k = e / M, row = e % M;
-        const int p = sp[k], q = sq[k];
-        if (q >= M) continue;
-        const float c = sc[k], s = ss[k];
-        const float ap = A[(int64_t)row * M + p], aq = A[(int64_t)row * M + q];
-        A[(int64_t)row * M + p] = c * ap - s * aq;
-        A[(int64_t)row * M + q] = s * ap + c * aq;
-      }
-      __syncthreads();
+      if (lane == 0) sred[wave] = vp;
     }
+    __syncthreads();
+    if (beta != 0.0f) {
+      float vtp = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) vtp += sred[v];
+      const float kc = 0.5f * beta * vtp;
+      for (int i = wave; i < n; i += 16) {
+        const float vi = sv[i], wi = sp[i] - kc * vi;
+        float* row = sA + tri_at(r0 + i, r0);
+        for (int jj = lane; jj <= i; jj += 64) {
+          const float vj = sv[jj], wj = sp[jj] - kc * vj;
+          row[jj] -= fmaf(vi, wj, wi * vj);
+        }
+      }
+    }
+    __syncthreads();
   }
-  // eigenvalues = diagonal, by decreasing value (rank by counting; ties by index)
-  for (int i = tid; i < M; i += 256) sdiag[i] = A[(int64_t)i * M + i];
+  if (tid == 0) {
+    if (M >= 2) {
+      sd[M - 2] = sA[tri_at(M - 2, M - 2)];
+      se[M - 2] = sA[tri_at(M - 1, M - 2)];
+    }
+    sd[M - 1] = sA[tri_at(M - 1, M - 1)];
+  }
   __syncthreads();
-  for (int i = tid; i < M; i += 256) {
-    const float d = sdiag[i];
-    int rank = 0;
-    for (int k = 0; k < M; ++k) rank += (sdiag[k] > d) || (sdiag[k] == d && k < i);
-    a.eig[(a.bh0 + lbh) * M + rank] = d;
+  // bisection, thread t finds the t-th smallest eigenvalue
+  const int t = tid;
+  if (t >= M) return;
+  float glo = INFINITY, ghi = -INFINITY, e2max = 0.0f;
+  for (int i = 0; i < M; ++i) {
+    const float r = (i > 0 ? fabsf(se[i - 1]) : 0.0f) + (i + 1 < M ? fabsf(se[i]) : 0.0f);
+    glo = fminf(glo, sd[i] - r);
+    ghi = fmaxf(ghi, sd[i] + r);
+    if (i + 1 < M) e2max = fmaxf(e2max, se[i] * se[i]);
   }
+  const float scale = fmaxf(fabsf(glo), fabsf(ghi));
+  const float pivmin = FLT_MIN * fmaxf(1.0f, e2max);
+  const float tol = 2.0f * FLT_EPSILON * scale + FLT_MIN;
+  float lo = glo - tol, hi = ghi + tol;
+  for (int it = 0; it < 100 && hi - lo > tol; ++it) {
+    const float x = 0.5f * (lo + hi);
+    int cnt = 0;
+    float q = sd[0] - x;
+    for (int i = 0;; ++i) {
+      if (fabsf(q) < pivmin) q = -pivmin;
+      cnt += q < 0.0f;
+      if (i + 1 == M) break;
+      q = (sd[i + 1] - x) - se[i] * se[i] / q;
+    }
+    if (cnt > t)
+      hi = x;
+    else
+      lo = x;
+  }
+  a.eig[(a.bh0 + blockIdx.x) * M + (M - 1 - t)] = 0.5f * (lo + hi);
 }
 
 }  // namespace flarepp

@@ -298,10 +298,13 @@ def route(S, K, V, scale, *, with_intermediates=False, workspace: Workspace | No
 
 
 def route_backward(S, K, V, scale, dY, *, workspace: Workspace | None = None, stream=None):
-    """(dS, dK, dV): gradients of <dY, route(S, K, V)> for float32 GPU tensors."""
+    """(dS, dK, dV): float32 gradients of <dY, route(S, K, V)>; S, K, V float32 or
+    bfloat16 GPU tensors, dY float32."""
     torch = _torch()
     for t, n in ((S, "S"), (K, "K"), (V, "V"), (dY, "dY")):
         _require(t, n)
+    if dY.dtype != torch.float32:
+        raise TypeError("dY must be float32")
     desc = desc_for(S, K, scale)
     dS = torch.empty_like(S, dtype=torch.float32)
     dK = torch.empty(K.shape, dtype=torch.float32, device=K.device)

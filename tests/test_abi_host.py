@@ -49,7 +49,7 @@ def ws_status(d, op):
 
 
 @pytest.mark.parametrize("op", range(5))
-def test_workspace_sizes(op):  # forward ops (the backward is float32 only: test_backward_validation)
+def test_workspace_sizes(op):  # forward ops (the backward: test_backward_validation)
     st, n_bf16 = ws_status(desc(), op)
     assert st == OK
     st, n_f32 = ws_status(desc(dtype=fp.F32), op)
@@ -119,18 +119,19 @@ def test_stage_validation():
                                       1 << 30, None) == INVALID_ARG
 
 
-def test_backward_validation():
-    d = desc(dtype=fp.F32)
+@pytest.mark.parametrize("dt", [fp.F32, fp.BF16])
+def test_backward_validation(dt):
+    d = desc(dtype=dt)
     st, n = ws_status(d, fp.OP_ROUTE_BACKWARD)
     assert st == OK and n > 0
-    assert ws_status(desc(), fp.OP_ROUTE_BACKWARD)[0] == UNSUPPORTED  # float32 only
+    assert ws_status(desc(dtype=dt, M=257), fp.OP_ROUTE_BACKWARD)[0] == UNSUPPORTED
 
     def bwd(dd=d, S=addr(0), K=addr(1), V=addr(2), dY=addr(3), dS=addr(4), dK=addr(5), dV=addr(7),
             ws=addr(6), nbytes=n):
         return fp.flarepp_route_backward(dd, S, K, V, dY, dS, dK, dV, ws, nbytes, None)
 
     # every case fails validation on the host, before any HIP call
-    assert bwd(dd=desc()) == UNSUPPORTED
+    assert bwd(dd=desc(dtype=dt, D=24)) == UNSUPPORTED
     assert bwd(dS=None) == INVALID_ARG
     assert bwd(dY=None) == INVALID_ARG
     assert bwd(dV=addr(7) + 4) == INVALID_ARG      # misaligned
