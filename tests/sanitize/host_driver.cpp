@@ -33,8 +33,7 @@ int main() {
       for (int64_t N : Ns)
         for (int64_t M : Ms) {
           flarepp_desc d = {1, 8, N, M, 32, dt, 0.2f, 0};
-          const flarepp_status want = (op == FLAREPP_OP_ROUTE_BACKWARD && dt == FLAREPP_BF16) ? FLAREPP_UNSUPPORTED
-                                                                                          : FLAREPP_OK;
+          const flarepp_status want = FLAREPP_OK;
           EXPECT(flarepp_workspace_size(&d, op, &n), want);
           for (int32_t sp : {1, 3, 1000000}) {
             flarepp_tuning t = {sp, 2, 0, 0};
@@ -87,9 +86,9 @@ int main() {
          FLAREPP_INVALID_ARG);
   EXPECT(flarepp_spectrum(&good, addr(0), addr(1), addr(2), faddr(1), nullptr, addr(6), size_t(1) << 40, nullptr),
          FLAREPP_ALIASING);
-  EXPECT(flarepp_route_backward(&good, addr(0), addr(1), addr(2), faddr(3), faddr(4), faddr(5), faddr(7), addr(6),
+  EXPECT(flarepp_route_backward(&good, addr(0), addr(1), addr(2), faddr(3), faddr(1), faddr(5), faddr(7), addr(6),
                                 size_t(1) << 40, nullptr),
-         FLAREPP_UNSUPPORTED);
+         FLAREPP_ALIASING);  // dS inside K
   flarepp_desc big = {64, 64, 4096, 256, 32, FLAREPP_BF16, 0.2f, 0};
   EXPECT(flarepp_route_noalloc(&big, addr(0), addr(1), addr(2), faddr(3), nullptr, nullptr, nullptr),
          FLAREPP_SCRATCH_LIMIT);
