@@ -167,23 +167,17 @@ __device__ __forceinline__ typename KOperand<D>::T tok_operand(const __bf16* bas
   const __amdgpu_buffer_rsrc_t r = buffer_rsrc(base + n * D, (uint32_t)(cnt * D * 2));
   return buffer_load<typename KOperand<D>::T>(r, (l16 * D + KL * g) * 2);
 }
-// dY rows (float32) of 16 tokens as a bf16 hi/lo pair, same lane layout
+// bf16 hi/lo pair of KL float32 elements (x0, then x1 when KL = 8)
 template <int D>
-__device__ __forceinline__ void tok_operand_f32(const float* base, int64_t n, int64_t nend, int l16, int g,
-                                                typename KOperand<D>::T& hi, typename KOperand<D>::T& lo) {
-  constexpr int KL = KOperand<D>::kLen;
-  const int64_t cnt = nend > n ? nend - n : 0;
-  const __amdgpu_buffer_rsrc_t r = buffer_rsrc(base + n * D, (uint32_t)(cnt * D * 4));
-  const int off = (l16 * D + KL * g) * 4;
-  const f32x4 x0 = buffer_load<f32x4>(r, off);
-  f32x4 r0;
+__device__ __forceinline__ void split_hilo(f32x4 x0, f32x4 x1, typename KOperand<D>::T& hi,
+                                           typename KOperand<D>::T& lo) {
+  f32x4 r0, r1;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) r0[e] = x0[e] - (float)(__bf16)x0[e];
-  if constexpr (KL == 8) {
-    const f32x4 x1 = buffer_load<f32x4>(r, off + 16);
-    f32x4 r1;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) r1[e] = x1[e] - (float)(__bf16)x1[e];
+  for (int e = 0; e < 4; ++e) {
+    r0[e] = x0[e] - (float)(__bf16)x0[e];
+    r1[e] = x1[e] - (float)(__bf16)x1[e];
+  }
+  if constexpr (KOperand<D>::kLen == 8) {
     hi = pack_tiles(x0, x1);
     lo = pack_tiles(r0, r1);
   } else {
@@ -193,6 +187,28 @@ __device__ __forceinline__ void tok_operand_f32(const float* base, int64_t n, in
     lo = bf16x4{q0[0], q0[1], q1[0], q1[1]};
   }
 }
+
+// Raw float32 dY of 16 tokens from token n: the KL elements of the lane's
+// operand slots (x0, x1) and, for the C-tile layout, elements 16 db + 4 g ..
+// (y[db]).  Tokens past nend read as zeros.
+template <int D>
+struct DyRaw {
+  f32x4 x0, x1, y[D / 16];
+  __device__ __forceinline__ void load(const float* base, int64_t n, int64_t nend, int l16, int g) {
+    constexpr int KL = KOperand<D>::kLen;
+    const int64_t cnt = nend > n ? nend - n : 0;
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(base + n * D, (uint32_t)(cnt * D * 4));
+    const int off = (l16 * D + KL * g) * 4;
+    x0 = buffer_load<f32x4>(r, off);
+    x1 = KL == 8 ? buffer_load<f32x4>(r, off + 16) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (D == 16) {
+      y[0] = x0;  // elements 4 g .. 4 g + 3 either way
+    } else {
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) y[db] = buffer_load<f32x4>(r, (l16 * D + 16 * db + 4 * g) * 4);
+    }
+  }
+};
 
 // ---- encode-stage token pass: dV_n and dK_n of the workgroup's tokens.
 // Wave w takes 32-token blocks tb = n0 + 32 w + 256 i; per 32-latent block
@@ -232,13 +248,24 @@ __global__ __launch_bounds__(512) void bwd_enc_tok_bf16(BwdEncArgs a) {
   const int64_t n0 = (int64_t)blockIdx.x * a.tchunk, n1 = min((int64_t)a.N, n0 + a.tchunk);
   const __bf16* Kh = a.K + bh * (int64_t)a.N * D;
   const __bf16* Vh = a.V + bh * (int64_t)a.N * D;
+  // K and V of the next 32-token block are loaded while this one computes
+  kop_t kn[2], vn[2];
+  auto load_kv = [&](int64_t tb) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      kn[u] = tok_operand<D>(Kh, tb + 16 * u, n1, l16, g);
+      vn[u] = tok_operand<D>(Vh, tb + 16 * u, n1, l16, g);
+    }
+  };
+  if (n0 + 32 * w < n1) load_kv(n0 + 32 * w);
   for (int64_t tb = n0 + 32 * w; tb < n1; tb += 256) {
     kop_t kb_op[2], vb_op[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      kb_op[u] = tok_operand<D>(Kh, tb + 16 * u, n1, l16, g);
-      vb_op[u] = tok_operand<D>(Vh, tb + 16 * u, n1, l16, g);
+      kb_op[u] = kn[u];
+      vb_op[u] = vn[u];
     }
+    if (tb + 256 < n1) load_kv(tb + 256);
     f32x4 dvt[2][DB], dkt[2][DB];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -347,14 +374,25 @@ __global__ __launch_bounds__(512) void bwd_enc_lat_bf16(BwdEncArgs a) {
 
   const __bf16* Kh = a.K + bh * (int64_t)a.N * D;
   const __bf16* Vh = a.V + bh * (int64_t)a.N * D;
+  // the next step's K and V are loaded while this one computes
+  kop_t kn[2], vn[2];
+  auto load_kv = [&](int64_t tb) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      kn[hh] = tok_operand<D>(Kh, tb + 16 * hh, n1, l16, g);
+      vn[hh] = tok_operand<D>(Vh, tb + 16 * hh, n1, l16, g);
+    }
+  };
+  if (n0 < n1) load_kv(n0);
   int buf = 0;
   for (int64_t tb = n0; tb < n1; tb += 32, buf ^= 1) {
     kop_t ka[2], va[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      ka[hh] = tok_operand<D>(Kh, tb + 16 * hh, n1, l16, g);
-      va[hh] = tok_operand<D>(Vh, tb + 16 * hh, n1, l16, g);
+      ka[hh] = kn[hh];
+      va[hh] = vn[hh];
     }
+    if (tb + 32 < n1) load_kv(tb + 32);
     if (w == 0) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
@@ -408,8 +446,9 @@ struct BwdDecArgs {
   const __bf16* K;    // B x H x N x D
   const float* dY;    // B x H x N x D
   float* dK;          // token pass: written
-  float* tA;          // [G][N] decode log-sum-exp A_n (token pass writes, latent pass reads)
-  float* tD;          // [G][N] <dY_n, Y'_n>
+  float* tA;          // [G][tstride] decode log-sum-exp A_n (token pass writes, latent pass reads)
+  float* tD;          // [G][tstride] <dY_n, Y'_n>
+  int64_t tstride;    // N rounded up to a multiple of 4
   float* part;        // latent pass: [G][Mp][J][2 D], dQd at 0, dZ at D
   int J, chunk, tchunk;
   int N, M, Mp, Mt;
@@ -446,18 +485,28 @@ __global__ __launch_bounds__(512) void bwd_dec_tok_bf16(BwdDecArgs a) {
   const int64_t n0 = (int64_t)blockIdx.x * a.tchunk, n1 = min((int64_t)a.N, n0 + a.tchunk);
   const __bf16* Kh = a.K + bh * (int64_t)a.N * D;
   const float* Gh = a.dY + bh * (int64_t)a.N * D;
+  // K and dY of the next 32-token block are loaded while this one computes
+  kop_t kn[2];
+  DyRaw<D> yn[2];
+  auto load_blk = [&](int64_t tb) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      kn[u] = tok_operand<D>(Kh, tb + 16 * u, n1, l16, g);
+      yn[u].load(Gh, tb + 16 * u, n1, l16, g);
+    }
+  };
+  if (n0 + 32 * w < n1) load_blk(n0 + 32 * w);
   for (int64_t tb = n0 + 32 * w; tb < n1; tb += 256) {
     kop_t kb_op[2], gb_op[2], gl_op[2];
     f32x4 gy[2][DB];  // dY_n elements 16 db + 4 g .. + 3, n = tb + 16 u + l16
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      kb_op[u] = tok_operand<D>(Kh, tb + 16 * u, n1, l16, g);
-      tok_operand_f32<D>(Gh, tb + 16 * u, n1, l16, g, gb_op[u], gl_op[u]);
-      const int64_t cnt = n1 > tb + 16 * u ? n1 - (tb + 16 * u) : 0;
-      const __amdgpu_buffer_rsrc_t r = buffer_rsrc(Gh + (tb + 16 * u) * D, (uint32_t)(cnt * D * 4));
+      kb_op[u] = kn[u];
+      split_hilo<D>(yn[u].x0, yn[u].x1, gb_op[u], gl_op[u]);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) gy[u][db] = buffer_load<f32x4>(r, (l16 * D + 16 * db + 4 * g) * 4);
+      for (int db = 0; db < DB; ++db) gy[u][db] = yn[u].y[db];
     }
+    if (tb + 256 < n1) load_blk(tb + 256);
     // pass 1: running max, weight sums and Y'^T
     float mrun[2] = {-INFINITY, -INFINITY}, lam[2] = {0.0f, 0.0f};
     f32x4 yt[2][DB];
@@ -517,8 +566,8 @@ __global__ __launch_bounds__(512) void bwd_dec_tok_bf16(BwdDecArgs a) {
       nDl[u] = -dd;
       const int64_t n = tb + 16 * u + l16;
       if (g == 0 && n < n1) {
-        a.tA[lbh * (int64_t)a.N + n] = -nA[u];
-        a.tD[lbh * (int64_t)a.N + n] = dd;
+        a.tA[lbh * a.tstride + n] = -nA[u];
+        a.tD[lbh * a.tstride + n] = dd;
       }
     }
     // pass 2: dL and dK^T += Qd^T dL
@@ -607,24 +656,40 @@ __global__ __launch_bounds__(512) void bwd_dec_lat_bf16(BwdDecArgs a) {
 
   const __bf16* Kh = a.K + bh * (int64_t)a.N * D;
   const float* Gh = a.dY + bh * (int64_t)a.N * D;
-  const float* tA = a.tA + lbh * (int64_t)a.N;
-  const float* tD = a.tD + lbh * (int64_t)a.N;
+  // per-token statistics of the head: rows of a.tstride floats (a multiple
+  // of 4, so a lane's four tokens are one aligned 16-byte load)
+  const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(a.tA + lbh * a.tstride, (uint32_t)(a.tstride * 4));
+  const __amdgpu_buffer_rsrc_t rD = buffer_rsrc(a.tD + lbh * a.tstride, (uint32_t)(a.tstride * 4));
+  // the next step's K, dY and statistics are loaded while this one computes
+  kop_t kn[2];
+  DyRaw<D> yn[2];
+  f32x4 an[2], dn[2];
+  auto load_step = [&](int64_t tb) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      kn[hh] = tok_operand<D>(Kh, tb + 16 * hh, n1, l16, g);
+      yn[hh].load(Gh, tb + 16 * hh, n1, l16, g);
+      an[hh] = buffer_load<f32x4>(rA, (int)(tb + 16 * hh + 4 * g) * 4);
+      dn[hh] = buffer_load<f32x4>(rD, (int)(tb + 16 * hh + 4 * g) * 4);
+    }
+  };
+  if (n0 < n1) load_step(n0);
   int buf = 0;
   for (int64_t tb = n0; tb < n1; tb += 32, buf ^= 1) {
     kop_t ka[2], ga[2], gl[2];
     f32x4 na[2], nd[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      ka[hh] = tok_operand<D>(Kh, tb + 16 * hh, n1, l16, g);
-      tok_operand_f32<D>(Gh, tb + 16 * hh, n1, l16, g, ga[hh], gl[hh]);
+      ka[hh] = kn[hh];
+      split_hilo<D>(yn[hh].x0, yn[hh].x1, ga[hh], gl[hh]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t n = tb + 16 * hh + 4 * g + r;
-        const bool live = n < n1;
-        na[hh][r] = live ? -tA[n] : -INFINITY;
-        nd[hh][r] = live ? -tD[n] : 0.0f;
+        const bool live = tb + 16 * hh + 4 * g + r < n1;
+        na[hh][r] = live ? -an[hh][r] : -INFINITY;
+        nd[hh][r] = live ? -dn[hh][r] : 0.0f;
       }
     }
+    if (tb + 32 < n1) load_step(tb + 32);
     if (w == 0) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)

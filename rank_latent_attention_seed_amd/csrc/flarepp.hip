@@ -200,8 +200,8 @@ Plan make_plan(const flarepp_desc* d, int op, const flarepp_tuning* t = nullptr)
     p.o_zf = take(G_ * p.M * D * 4);
     p.o_lse1 = take(G_ * Mp * 4);
     p.o_lse2 = take(G_ * Mp * 4);
-    p.o_tlse = take(G_ * (size_t)p.N * 4);
-    p.o_tdel = take(G_ * (size_t)p.N * 4);
+    p.o_tlse = take(G_ * (size_t)cdiv(p.N, 4) * 16);
+    p.o_tdel = take(G_ * (size_t)cdiv(p.N, 4) * 16);
     p.o_dz = take(G_ * p.M * D * 4);
     p.o_dq3 = take(G_ * p.M * D * 4);
     p.o_dq = take(G_ * p.M * D * 4);
@@ -972,6 +972,7 @@ flarepp_status run_backward_bf16(const Plan& p, const void* S, const void* K, co
       d.dK = dK;
       d.tA = at<float>(ws, p.o_tlse);
       d.tD = at<float>(ws, p.o_tdel);
+      d.tstride = cdiv(p.N, 4) * 4;
       d.part = part;
       d.J = p.J;
       d.chunk = p.chunk;
