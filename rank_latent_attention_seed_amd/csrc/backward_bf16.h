@@ -7,10 +7,13 @@
 // taken through the decode (queries = tokens, keys = Qd, values = Z), the
 // encode and the seed encode (FLARE summary, "Основной механизм FLARE").
 //
-// Each stage has a token pass (a workgroup owns tokens and walks all
-// latents, whose operands it stages in LDS once) and a latent pass (a
-// workgroup owns one split of the tokens and all latents, wave w latents
-// 32 w .. 32 w + 31, and writes split partials that bwd_reduce sums).  Every
+// Each stage has a latent pass (a workgroup owns one split of the tokens and
+// all latents, wave w latents 32 w .. 32 w + 31, and writes split partials
+// that bwd_reduce sums) and token-side work (a workgroup owns tokens and
+// walks all latents, whose operands it stages in LDS once): the decode's in
+// one pass that also forms the per-token statistics the decode's latent pass
+// needs, both encode stages' in one final pass, so dK and dV (float32, the
+// largest arrays of the call) are read and written once there.  Every
 // contraction is a 16x16 MFMA tile with float32 accumulation:
 //   * logits t = c <q, k> (log2 units, c = s log2 e) take the query as a
 //     bf16 hi/lo pair (K is exact in bf16), so their error is that of
@@ -27,8 +30,11 @@
 //     weights and bf16 operands: 2^-9 relative rounding per term.
 // The C tile of a logit product leaves each lane one column and four rows;
 // two such tiles are the eight k slots of the next product's operand in
-// registers (common.h).  Transposed operands are read from LDS copies laid
-// out [d][m] (latents) or [d][token].
+// registers (common.h).  Latent operands are staged in LDS as rows with
+// XOR-swizzled 16-byte chunks (the route's encode tile layout, slot_off), so
+// both the row operand and the transposed one (ds_read_b64_tr_b16) read
+// without bank conflicts; the K tile of a latent-pass step is transposed
+// into LDS by one wave.
 #pragma once
 
 #include "common.h"
@@ -37,10 +43,6 @@
 namespace flarepp {
 
 constexpr int kBwdBf16MaxM = 256;
-// LDS row stride (elements) of a transposed latent operand [D][m]: a read
-// of 8 bytes by lane (row d = l mod 16, column 32 kb + 4 g) then starts 4
-// banks apart per row and 2 per g, two wave passes as for a contiguous read.
-constexpr int kBwdTS = kBwdBf16MaxM + 8;
 // LDS row stride (elements) of a transposed 32-token tile [D][token]
 constexpr int kBwdTT = 32 + 8;
 
@@ -90,30 +92,23 @@ __global__ __launch_bounds__(256) void bwd_prep_bf16(BwdPrepArgs a) {
   }
 }
 
-// Arguments of the encode-stage passes (stages 1 and 2): queries Q
-// (c Q as bf16 hi/lo rows and Q^T; (b, h)'s block at b * sb + h * sh - off,
-// which also covers the seed blocks of stage 1), dO (bf16 rows and dO^T),
-// the forward's per-latent log-sum-exp A_m and delta_m = <dO_m, O_m>.
+// Arguments of the encode-stage latent pass (stages 1 and 2): queries Q
+// (c Q as bf16 hi/lo rows; (b, h)'s block at b * sb + h * sh - off, which
+// also covers the seed blocks of stage 1), dO (bf16 hi/lo rows), the
+// forward's per-latent log-sum-exp A_m and delta_m = <dO_m, O_m>.
 struct BwdEncArgs {
   const __bf16* qhi;
   const __bf16* qlo;
   int64_t q_sb, q_sh, q_off;  // in [.][Mp][D] blocks
-  const __bf16* qt;
-  int64_t t_sb, t_sh, t_off;  // in [.][D][Mt] blocks
   const __bf16* dor;          // [G][Mp][D] dO as bf16 hi
   const __bf16* dorl;         // [G][Mp][D] bf16 lo (dO - hi)
-  const __bf16* dot;          // [G][D][Mt]
   const float* lse;           // [G][Mp]
   const float* delta;         // [G][Mp]
   const __bf16* K;            // B x H x N x D
   const __bf16* V;
-  float* dK;                  // token pass: B x H x N x D
-  float* dV;
-  int acc_dk, acc_dv;         // add into dK / dV (else overwrite)
-  float* part;                // latent pass: [G][Mp][J][D]
-  int J, chunk;               // latent pass: token splits
-  int tchunk;                 // token pass: tokens per workgroup (multiple of 256)
-  int H, N, M, Mp, Mt;
+  float* part;                // [G][Mp][J][D]
+  int J, chunk;               // token splits
+  int H, N, M, Mp;
   int64_t bh0;
   float s;
 };
@@ -136,24 +131,35 @@ __device__ __forceinline__ bf16x8 pack_tiles(f32x4 x0, f32x4 x1) {
 
 __device__ __forceinline__ f32x4 splat4(float x) { return f32x4{x, x, x, x}; }
 
-// Row-major [Mp][D] bf16 block -> LDS rows 0 .. Mt - 1 (zero past Mp).
+// Row-major [Mp][D] bf16 block -> LDS rows 0 .. Mt - 1 (zero past Mp), the
+// 16-byte chunks of row m swizzled as in the encode's tiles (slot_off).
 template <int D>
 __device__ __forceinline__ void stage_rows(__bf16* dst, const __bf16* src, int Mp, int Mt, int tid, int nthr) {
-  for (int e = tid; e < Mt * D / 8; e += nthr) {
+  constexpr int CH = D / 8;
+  for (int e = tid; e < Mt * CH; e += nthr) {
+    const int m = e / CH, c = e - m * CH;
     bf16x8 v = bf16x8{};
-    if (e < Mp * D / 8) v = reinterpret_cast<const bf16x8*>(src)[e];
-    reinterpret_cast<bf16x8*>(dst)[e] = v;
+    if (m < Mp) v = reinterpret_cast<const bf16x8*>(src)[e];
+    *reinterpret_cast<bf16x8*>(dst + m * D + ((c ^ chunk_swz<D>(m)) << 3)) = v;
   }
 }
-// Transposed [D][Mt] bf16 block -> LDS [D][kBwdTS].
+// Row operand of latent rows m0 .. m0 + 15 (lane: row m0 + l16, elements KL g ..)
 template <int D>
-__device__ __forceinline__ void stage_tr(__bf16* dst, const __bf16* src, int Mt, int tid, int nthr) {
-  const int per = Mt / 8;
-  for (int e = tid; e < D * per; e += nthr) {
-    const int d = e / per, c = e - d * per;
-    *reinterpret_cast<bf16x8*>(dst + d * kBwdTS + 8 * c) =
-        *reinterpret_cast<const bf16x8*>(src + (int64_t)d * Mt + 8 * c);
-  }
+__device__ __forceinline__ typename KOperand<D>::T row_operand(const __bf16* sX, int m0, int l16, int g) {
+  return *reinterpret_cast<const typename KOperand<D>::T*>(sX + slot_off<D>(m0 + l16, KOperand<D>::kLen * g));
+}
+// Transposed operand of latents 32 kb .. 32 kb + 31, elements 16 db .. 16 db + 15
+// (lane: row element 16 db + l16, k slots latents 32 kb + 4 g .. + 3 and
+// 32 kb + 16 + 4 g .. + 3): two transposing reads, each giving four latents
+// of one element when the 16 lanes of a row group supply a 4-latent x
+// 16-element block (lane r: latent + r / 4, elements + 4 (r % 4) .. + 3).
+template <int D>
+__device__ __forceinline__ bf16x8 tr_rows(const __bf16* sX, int kb, int db, int l16, int g) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  const __bf16* a0 = sX + slot_off<D>(32 * kb + 4 * g + (l16 >> 2), 16 * db + 4 * (l16 & 3));
+  const bf16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)a0);
+  const bf16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0 + 16 * D));
+  return bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
 }
 
 // K rows of 16 tokens as the B operand of a logit tile (lane: token
@@ -167,81 +173,82 @@ __device__ __forceinline__ typename KOperand<D>::T tok_operand(const __bf16* bas
   const __amdgpu_buffer_rsrc_t r = buffer_rsrc(base + n * D, (uint32_t)(cnt * D * 2));
   return buffer_load<typename KOperand<D>::T>(r, (l16 * D + KL * g) * 2);
 }
-// bf16 hi/lo pair of KL float32 elements (x0, then x1 when KL = 8)
-template <int D>
-__device__ __forceinline__ void split_hilo(f32x4 x0, f32x4 x1, typename KOperand<D>::T& hi,
-                                           typename KOperand<D>::T& lo) {
-  f32x4 r0, r1;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    r0[e] = x0[e] - (float)(__bf16)x0[e];
-    r1[e] = x1[e] - (float)(__bf16)x1[e];
-  }
-  if constexpr (KOperand<D>::kLen == 8) {
-    hi = pack_tiles(x0, x1);
-    lo = pack_tiles(r0, r1);
-  } else {
-    const bf16x2 p0 = pack_bf16(x0[0], x0[1]), p1 = pack_bf16(x0[2], x0[3]);
-    const bf16x2 q0 = pack_bf16(r0[0], r0[1]), q1 = pack_bf16(r0[2], r0[3]);
-    hi = bf16x4{p0[0], p0[1], p1[0], p1[1]};
-    lo = bf16x4{q0[0], q0[1], q1[0], q1[1]};
-  }
-}
-
-// Raw float32 dY of 16 tokens from token n: the KL elements of the lane's
-// operand slots (x0, x1) and, for the C-tile layout, elements 16 db + 4 g ..
-// (y[db]).  Tokens past nend read as zeros.
-template <int D>
-struct DyRaw {
-  f32x4 x0, x1, y[D / 16];
-  __device__ __forceinline__ void load(const float* base, int64_t n, int64_t nend, int l16, int g) {
-    constexpr int KL = KOperand<D>::kLen;
-    const int64_t cnt = nend > n ? nend - n : 0;
-    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(base + n * D, (uint32_t)(cnt * D * 4));
-    const int off = (l16 * D + KL * g) * 4;
-    x0 = buffer_load<f32x4>(r, off);
-    x1 = KL == 8 ? buffer_load<f32x4>(r, off + 16) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    if constexpr (D == 16) {
-      y[0] = x0;  // elements 4 g .. 4 g + 3 either way
-    } else {
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) y[db] = buffer_load<f32x4>(r, (l16 * D + 16 * db + 4 * g) * 4);
-    }
-  }
+// dY of the launch's heads as a bf16 hi/lo pair ([G][N][D] each), once per
+// call, for both decode passes.
+struct BwdDySplitArgs {
+  const float* dY;  // the launch's first head
+  __bf16* hi;
+  __bf16* lo;
+  int64_t n;        // elements, a multiple of 4
 };
 
-// ---- encode-stage token pass: dV_n and dK_n of the workgroup's tokens.
-// Wave w takes 32-token blocks tb = n0 + 32 w + 256 i; per 32-latent block
-// kb: L = (c Q) K^T - A (rows latents, cols tokens), dP = dO V^T - delta,
-// P = 2^L, dL = P dP, then dV^T += dO^T P and dK^T += Q^T dL.
+__global__ __launch_bounds__(256) void bwd_dy_split(BwdDySplitArgs a) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= a.n) return;
+  const f32x4 x = *reinterpret_cast<const f32x4*>(a.dY + i);
+  const bf16x2 h0 = pack_bf16(x[0], x[1]), h1 = pack_bf16(x[2], x[3]);
+  const bf16x2 l0 = pack_bf16(x[0] - (float)h0[0], x[1] - (float)h0[1]);
+  const bf16x2 l1 = pack_bf16(x[2] - (float)h1[0], x[3] - (float)h1[1]);
+  *reinterpret_cast<bf16x4*>(a.hi + i) = bf16x4{h0[0], h0[1], h1[0], h1[1]};
+  *reinterpret_cast<bf16x4*>(a.lo + i) = bf16x4{l0[0], l0[1], l1[0], l1[1]};
+}
+
+// ---- encode-stage token pass, both encode stages at once: dV_n and dK_n
+// of the workgroup's tokens (dK added to the decode's part).  Wave w takes
+// 32-token blocks tb = n0 + 32 w + 256 i; per stage and 32-latent block kb:
+// L = (c Q) K^T - A (rows latents, cols tokens), dP = dO V^T - delta,
+// P = 2^L, dL = P dP, then dV^T += dO^T P and dK^T += (c Q)^T dL, the
+// transposed operands read from the same LDS rows; dK is scaled by s / c.
+struct BwdStageOps {
+  const __bf16* qhi;  // c Q as bf16 hi/lo rows; (b, h)'s block at b * q_sb + h * q_sh - q_off
+  const __bf16* qlo;
+  int64_t q_sb, q_sh, q_off;
+  const __bf16* dor;   // [G][Mp][D] dO as bf16 hi
+  const __bf16* dorl;  // [G][Mp][D] bf16 lo
+  const float* lse;    // [G][Mp] A_m
+  const float* delta;  // [G][Mp] <dO_m, O_m>
+};
+
+struct BwdEncTokArgs {
+  BwdStageOps st[2];  // the encode (queries Qd) and the seed encode (queries S)
+  const __bf16* K;
+  const __bf16* V;
+  float* dK;          // B x H x N x D, holds the decode's part
+  float* dV;          // B x H x N x D, written
+  int tchunk;         // tokens per workgroup (multiple of 256)
+  int H, N, M, Mp, Mt;
+  int64_t bh0;
+  float kscale;       // s / c (0 when s = 0)
+};
+
 template <int D>
-__global__ __launch_bounds__(512) void bwd_enc_tok_bf16(BwdEncArgs a) {
-  constexpr int KL = KOperand<D>::kLen;
+__global__ __launch_bounds__(512) void bwd_enc_tok_bf16(BwdEncTokArgs a) {
   constexpr int DB = D / 16;
   typedef typename KOperand<D>::T kop_t;
-  __shared__ __attribute__((aligned(16))) __bf16 sQh[kBwdBf16MaxM * D];
-  __shared__ __attribute__((aligned(16))) __bf16 sQl[kBwdBf16MaxM * D];
-  __shared__ __attribute__((aligned(16))) __bf16 sDo[kBwdBf16MaxM * D];
-  __shared__ __attribute__((aligned(16))) __bf16 sDol[kBwdBf16MaxM * D];
-  __shared__ __attribute__((aligned(16))) __bf16 sQt[D * kBwdTS];
-  __shared__ __attribute__((aligned(16))) __bf16 sDot[D * kBwdTS];
-  __shared__ __attribute__((aligned(16))) float sNA[kBwdBf16MaxM];
-  __shared__ __attribute__((aligned(16))) float sND[kBwdBf16MaxM];
+  __shared__ __attribute__((aligned(16))) __bf16 sQh[2][kBwdBf16MaxM * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sQl[2][kBwdBf16MaxM * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sDo[2][kBwdBf16MaxM * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sDol[2][kBwdBf16MaxM * D];
+  __shared__ __attribute__((aligned(16))) float sNA[2][kBwdBf16MaxM];
+  __shared__ __attribute__((aligned(16))) float sND[2][kBwdBf16MaxM];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int64_t lbh = blockIdx.y, bh = a.bh0 + lbh;
   const int b = (int)(bh / a.H), h = (int)(bh - (int64_t)b * a.H);
   const int Mt = a.Mt, nkb = Mt / 32;
-  stage_rows<D>(sQh, a.qhi + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh - a.q_off, a.Mp, Mt, tid, 512);
-  stage_rows<D>(sQl, a.qlo + (int64_t)b * a.q_sb + (int64_t)h * a.q_sh - a.q_off, a.Mp, Mt, tid, 512);
-  stage_rows<D>(sDo, a.dor + lbh * a.Mp * D, a.Mp, Mt, tid, 512);
-  stage_rows<D>(sDol, a.dorl + lbh * a.Mp * D, a.Mp, Mt, tid, 512);
-  stage_tr<D>(sQt, a.qt + (int64_t)b * a.t_sb + (int64_t)h * a.t_sh - a.t_off, Mt, tid, 512);
-  stage_tr<D>(sDot, a.dot + lbh * (int64_t)D * Mt, Mt, tid, 512);
-  for (int m = tid; m < Mt; m += 512) {
-    const bool real = m < a.M;
-    sNA[m] = real ? -a.lse[lbh * a.Mp + m] : -INFINITY;
-    sND[m] = real ? -a.delta[lbh * a.Mp + m] : 0.0f;
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const BwdStageOps& o = a.st[x];
+    const int64_t qo = (int64_t)b * o.q_sb + (int64_t)h * o.q_sh - o.q_off;
+    stage_rows<D>(sQh[x], o.qhi + qo, a.Mp, Mt, tid, 512);
+    stage_rows<D>(sQl[x], o.qlo + qo, a.Mp, Mt, tid, 512);
+    stage_rows<D>(sDo[x], o.dor + lbh * a.Mp * D, a.Mp, Mt, tid, 512);
+    stage_rows<D>(sDol[x], o.dorl + lbh * a.Mp * D, a.Mp, Mt, tid, 512);
+    for (int m = tid; m < Mt; m += 512) {
+      const bool real = m < a.M;
+      sNA[x][m] = real ? -o.lse[lbh * a.Mp + m] : -INFINITY;
+      sND[x][m] = real ? -o.delta[lbh * a.Mp + m] : 0.0f;
+    }
   }
   __syncthreads();
 
@@ -271,44 +278,50 @@ __global__ __launch_bounds__(512) void bwd_enc_tok_bf16(BwdEncArgs a) {
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int db = 0; db < DB; ++db) dvt[u][db] = dkt[u][db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int kb = 0; kb < nkb; ++kb) {
-      f32x4 P[2][2], dL[2][2];
+    for (int x = 0; x < 2; ++x) {
+      const __bf16* qh_s = sQh[x];
+      const __bf16* ql_s = sQl[x];
+      const __bf16* do_s = sDo[x];
+      const __bf16* dl_s = sDol[x];
+      for (int kb = 0; kb < nkb; ++kb) {
+        f32x4 P[2][2], dL[2][2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int m0 = 32 * kb + 16 * t;
-        const kop_t qh = *reinterpret_cast<const kop_t*>(sQh + (m0 + l16) * D + KL * g);
-        const kop_t ql = *reinterpret_cast<const kop_t*>(sQl + (m0 + l16) * D + KL * g);
-        const kop_t dov = *reinterpret_cast<const kop_t*>(sDo + (m0 + l16) * D + KL * g);
-        const kop_t dol = *reinterpret_cast<const kop_t*>(sDol + (m0 + l16) * D + KL * g);
-        const f32x4 na = *reinterpret_cast<const f32x4*>(sNA + m0 + 4 * g);
-        const f32x4 nd = *reinterpret_cast<const f32x4*>(sND + m0 + 4 * g);
+        for (int t = 0; t < 2; ++t) {
+          const int m0 = 32 * kb + 16 * t;
+          const kop_t qh = row_operand<D>(qh_s, m0, l16, g);
+          const kop_t ql = row_operand<D>(ql_s, m0, l16, g);
+          const kop_t dov = row_operand<D>(do_s, m0, l16, g);
+          const kop_t dol = row_operand<D>(dl_s, m0, l16, g);
+          const f32x4 na = *reinterpret_cast<const f32x4*>(&sNA[x][m0 + 4 * g]);
+          const f32x4 nd = *reinterpret_cast<const f32x4*>(&sND[x][m0 + 4 * g]);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          f32x4 L = KOperand<D>::mma(qh, kb_op[u], na);
-          L = KOperand<D>::mma(ql, kb_op[u], L);
-          f32x4 dp = KOperand<D>::mma(dov, vb_op[u], nd);
-          dp = KOperand<D>::mma(dol, vb_op[u], dp);
+          for (int u = 0; u < 2; ++u) {
+            f32x4 L = KOperand<D>::mma(qh, kb_op[u], na);
+            L = KOperand<D>::mma(ql, kb_op[u], L);
+            f32x4 dp = KOperand<D>::mma(dov, vb_op[u], nd);
+            dp = KOperand<D>::mma(dol, vb_op[u], dp);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            P[t][u][r] = fast_exp2(L[r]);
-            dL[t][u][r] = P[t][u][r] * dp[r];
+            for (int r = 0; r < 4; ++r) {
+              P[t][u][r] = fast_exp2(L[r]);
+              dL[t][u][r] = P[t][u][r] * dp[r];
+            }
           }
         }
-      }
-      bf16x8 pb[2], lb[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        pb[u] = pack_tiles(P[0][u], P[1][u]);
-        lb[u] = pack_tiles(dL[0][u], dL[1][u]);
-      }
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const bf16x8 dot = tr_operand(sDot + (16 * db + l16) * kBwdTS, 32 * kb, g);
-        const bf16x8 qt = tr_operand(sQt + (16 * db + l16) * kBwdTS, 32 * kb, g);
+        bf16x8 pb[2], lb[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          dvt[u][db] = mfma_k32(dot, pb[u], dvt[u][db]);
-          dkt[u][db] = mfma_k32(qt, lb[u], dkt[u][db]);
+          pb[u] = pack_tiles(P[0][u], P[1][u]);
+          lb[u] = pack_tiles(dL[0][u], dL[1][u]);
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 dot = tr_rows<D>(do_s, kb, db, l16, g);
+          const bf16x8 qt = tr_rows<D>(qh_s, kb, db, l16, g);
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            dvt[u][db] = mfma_k32(dot, pb[u], dvt[u][db]);
+            dkt[u][db] = mfma_k32(qt, lb[u], dkt[u][db]);
+          }
         }
       }
     }
@@ -319,11 +332,8 @@ __global__ __launch_bounds__(512) void bwd_enc_tok_bf16(BwdEncArgs a) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const int64_t o = (bh * (int64_t)a.N + n) * D + 16 * db + 4 * g;
-          f32x4 kv = dkt[u][db] * a.s, vv = dvt[u][db];
-          if (a.acc_dk) kv += *reinterpret_cast<const f32x4*>(a.dK + o);
-          if (a.acc_dv) vv += *reinterpret_cast<const f32x4*>(a.dV + o);
-          *reinterpret_cast<f32x4*>(a.dK + o) = kv;
-          *reinterpret_cast<f32x4*>(a.dV + o) = vv;
+          *reinterpret_cast<f32x4*>(a.dK + o) = *reinterpret_cast<const f32x4*>(a.dK + o) + dkt[u][db] * a.kscale;
+          *reinterpret_cast<f32x4*>(a.dV + o) = dvt[u][db];
         }
       }
     }
@@ -413,10 +423,15 @@ __global__ __launch_bounds__(512) void bwd_enc_lat_bf16(BwdEncArgs a) {
         L = KOperand<D>::mma(ka[hh], ql[t], L);
         f32x4 dp = KOperand<D>::mma(va[hh], dov[t], splat4(nd[t]));
         dp = KOperand<D>::mma(va[hh], dol[t], dp);
+        if (tb + 32 <= n1) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool live = tb + 16 * hh + 4 * g + r < n1;
-          dl[hh][r] = live ? fast_exp2(L[r]) * dp[r] : 0.0f;
+          for (int r = 0; r < 4; ++r) dl[hh][r] = fast_exp2(L[r]) * dp[r];
+        } else {  // the split's last, partial step
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool live = tb + 16 * hh + 4 * g + r < n1;
+            dl[hh][r] = live ? fast_exp2(L[r]) * dp[r] : 0.0f;
+          }
         }
       }
       const bf16x8 lb = pack_tiles(dl[0], dl[1]);
@@ -434,17 +449,18 @@ __global__ __launch_bounds__(512) void bwd_enc_lat_bf16(BwdEncArgs a) {
   }
 }
 
-// Arguments of the decode passes (stage 3): keys Qd (c Qd hi/lo rows, Qd^T),
-// values Z through Z' = Z - mean Z (hi/lo rows, Z'^T), upstream dY.
+// Arguments of the decode passes (stage 3): keys Qd (c Qd hi/lo rows),
+// values Z through Z' = Z - mean Z (hi/lo rows), upstream dY.
 struct BwdDecArgs {
-  const __bf16* qhi;  // [G][Mp][D]
+  const __bf16* qhi;  // [G][Mp][D] c Qd as bf16 hi/lo
   const __bf16* qlo;
-  const __bf16* qdt;  // [G][D][Mt]
-  const __bf16* zh;   // [G][Mp][D]
+  const __bf16* zh;   // [G][Mp][D] Z' as bf16 hi/lo
   const __bf16* zl;
-  const __bf16* zt;   // [G][D][Mt]
   const __bf16* K;    // B x H x N x D
-  const float* dY;    // B x H x N x D
+  const __bf16* dyh;  // [G][N][D] dY as bf16 hi
+  const __bf16* dyl;  // [G][N][D] bf16 lo
+  const float* qnorm; // [G][Mp] ||Qd_m||
+  float c;            // s log2 e
   float* dK;          // token pass: written
   float* tA;          // [G][tstride] decode log-sum-exp A_n (token pass writes, latent pass reads)
   float* tD;          // [G][tstride] <dY_n, Y'_n>
@@ -454,11 +470,16 @@ struct BwdDecArgs {
   int N, M, Mp, Mt;
   int64_t bh0;
   float s;
+  float kscale;       // s / c (0 when s = 0)
 };
 
-// ---- decode token pass: per 32-token block, first A_n and Y'_n with an
-// online max over the latent blocks (L = (c Qd) K^T, rows latents), then
-// dL = 2^(L - A_n) (Z' dY^T - <dY_n, Y'_n>) and dK^T += Qd^T dL.
+// ---- decode token pass: per 32-token block, first A_n and Y'_n over the
+// latent blocks (L = (c Qd) K^T, rows latents), then
+// dL = 2^(L - A_n) (Z' dY^T - <dY_n, Y'_n>) and dK^T += (c Qd)^T dL (scaled
+// by s / c; the transposed operands read from the LDS rows).  The shift
+// of the first pass is the bound mu_n = |c| ||K_n|| max ||Qd_m|| when
+// 2 mu_n <= 100 for every token of the wave's block (no max, no rescaling),
+// else a running max over the latent blocks.
 template <int D>
 __global__ __launch_bounds__(512) void bwd_dec_tok_bf16(BwdDecArgs a) {
   constexpr int KL = KOperand<D>::kLen;
@@ -468,8 +489,6 @@ __global__ __launch_bounds__(512) void bwd_dec_tok_bf16(BwdDecArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 sQl[kBwdBf16MaxM * D];
   __shared__ __attribute__((aligned(16))) __bf16 sZh[kBwdBf16MaxM * D];
   __shared__ __attribute__((aligned(16))) __bf16 sZl[kBwdBf16MaxM * D];
-  __shared__ __attribute__((aligned(16))) __bf16 sQt[D * kBwdTS];
-  __shared__ __attribute__((aligned(16))) __bf16 sZt[D * kBwdTS];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int64_t lbh = blockIdx.y, bh = a.bh0 + lbh;
@@ -478,78 +497,130 @@ __global__ __launch_bounds__(512) void bwd_dec_tok_bf16(BwdDecArgs a) {
   stage_rows<D>(sQl, a.qlo + lbh * a.Mp * D, a.Mp, Mt, tid, 512);
   stage_rows<D>(sZh, a.zh + lbh * a.Mp * D, a.Mp, Mt, tid, 512);
   stage_rows<D>(sZl, a.zl + lbh * a.Mp * D, a.Mp, Mt, tid, 512);
-  stage_tr<D>(sQt, a.qdt + lbh * (int64_t)D * Mt, Mt, tid, 512);
-  stage_tr<D>(sZt, a.zt + lbh * (int64_t)D * Mt, Mt, tid, 512);
+  float qmax = 0.0f;
+  for (int m = lane; m < a.Mp; m += 64) qmax = fmaxf(qmax, a.qnorm[lbh * a.Mp + m]);
+  qmax = wave_max(qmax);
   __syncthreads();
+  const bool ragged = a.M < Mt;  // the last latent block has padding rows
+  // pad rows of latent block kb: rows m0 + 4 g + r >= M take -inf logits
+  auto mask_pad = [&](f32x4& L, int m0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) L[r] = m0 + 4 * g + r < a.M ? L[r] : -INFINITY;
+  };
 
   const int64_t n0 = (int64_t)blockIdx.x * a.tchunk, n1 = min((int64_t)a.N, n0 + a.tchunk);
   const __bf16* Kh = a.K + bh * (int64_t)a.N * D;
-  const float* Gh = a.dY + bh * (int64_t)a.N * D;
-  // K and dY of the next 32-token block are loaded while this one computes
-  kop_t kn[2];
-  DyRaw<D> yn[2];
+  const __bf16* Gh = a.dyh + lbh * (int64_t)a.N * D;
+  const __bf16* Gl = a.dyl + lbh * (int64_t)a.N * D;
+  // K and dY of the next 32-token block are loaded while this one computes;
+  // dY both as the lane's operand slots and as the C-tile elements 16 db + 4 g ..
+  kop_t kn[2], hn[2], ln[2];
+  bf16x4 yhn[2][DB], yln[2][DB];
   auto load_blk = [&](int64_t tb) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      kn[u] = tok_operand<D>(Kh, tb + 16 * u, n1, l16, g);
-      yn[u].load(Gh, tb + 16 * u, n1, l16, g);
+      const int64_t n = tb + 16 * u;
+      kn[u] = tok_operand<D>(Kh, n, n1, l16, g);
+      hn[u] = tok_operand<D>(Gh, n, n1, l16, g);
+      ln[u] = tok_operand<D>(Gl, n, n1, l16, g);
+      if constexpr (D == 32) {
+        const int64_t cnt = n1 > n ? n1 - n : 0;
+        const __amdgpu_buffer_rsrc_t rh = buffer_rsrc(Gh + n * D, (uint32_t)(cnt * D * 2));
+        const __amdgpu_buffer_rsrc_t rl = buffer_rsrc(Gl + n * D, (uint32_t)(cnt * D * 2));
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          yhn[u][db] = buffer_load<bf16x4>(rh, (l16 * D + 16 * db + 4 * g) * 2);
+          yln[u][db] = buffer_load<bf16x4>(rl, (l16 * D + 16 * db + 4 * g) * 2);
+        }
+      }
     }
   };
   if (n0 + 32 * w < n1) load_blk(n0 + 32 * w);
   for (int64_t tb = n0 + 32 * w; tb < n1; tb += 256) {
     kop_t kb_op[2], gb_op[2], gl_op[2];
     f32x4 gy[2][DB];  // dY_n elements 16 db + 4 g .. + 3, n = tb + 16 u + l16
+    float mu[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       kb_op[u] = kn[u];
-      split_hilo<D>(yn[u].x0, yn[u].x1, gb_op[u], gl_op[u]);
+      gb_op[u] = hn[u];
+      gl_op[u] = ln[u];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) gy[u][db] = yn[u].y[db];
+      for (int db = 0; db < DB; ++db) {
+        bf16x4 yh, yl;
+        if constexpr (D == 32) {
+          yh = yhn[u][db];
+          yl = yln[u][db];
+        } else {
+          yh = hn[u];
+          yl = ln[u];
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) gy[u][db][r] = (float)yh[r] + (float)yl[r];
+      }
+      float k2 = 0.0f;
+#pragma unroll
+      for (int e = 0; e < KL; ++e) k2 = fmaf((float)kb_op[u][e], (float)kb_op[u][e], k2);
+      mu[u] = fabsf(a.c) * __builtin_sqrtf(sum_over_rows(k2)) * qmax * (1.0f + 1.0f / 4096.0f);
     }
     if (tb + 256 < n1) load_blk(tb + 256);
-    // pass 1: running max, weight sums and Y'^T
-    float mrun[2] = {-INFINITY, -INFINITY}, lam[2] = {0.0f, 0.0f};
+    const bool bounded = __all(2.0f * fmaxf(mu[0], mu[1]) <= 100.0f);
+
+    // pass 1: weight sums and Y'^T
+    float mrun[2], lam[2] = {0.0f, 0.0f};
     f32x4 yt[2][DB];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < 2; ++u) {
+      mrun[u] = bounded ? mu[u] : -INFINITY;
 #pragma unroll
       for (int db = 0; db < DB; ++db) yt[u][db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
     for (int kb = 0; kb < nkb; ++kb) {
       f32x4 L[2][2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int m0 = 32 * kb + 16 * t;
-        const kop_t qh = *reinterpret_cast<const kop_t*>(sQh + (m0 + l16) * D + KL * g);
-        const kop_t ql = *reinterpret_cast<const kop_t*>(sQl + (m0 + l16) * D + KL * g);
+        const kop_t qh = row_operand<D>(sQh, m0, l16, g);
+        const kop_t ql = row_operand<D>(sQl, m0, l16, g);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
-          L[t][u] = KOperand<D>::mma(qh, kb_op[u], z);
+          L[t][u] = KOperand<D>::mma(qh, kb_op[u], splat4(bounded ? -mu[u] : 0.0f));
           L[t][u] = KOperand<D>::mma(ql, kb_op[u], L[t][u]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) L[t][u][r] = m0 + 4 * g + r < a.M ? L[t][u][r] : -INFINITY;
+          if (ragged && kb == nkb - 1) mask_pad(L[t][u], m0);
         }
       }
       bf16x8 zt[DB];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) zt[db] = tr_operand(sZt + (16 * db + l16) * kBwdTS, 32 * kb, g);
+      for (int db = 0; db < DB; ++db) zt[db] = tr_rows<D>(sZh, kb, db, l16, g);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        float mx = fmaxf(max3(L[0][u][0], L[0][u][1], L[0][u][2]), max3(L[0][u][3], L[1][u][0], L[1][u][1]));
-        mx = max_over_rows(fmaxf(mx, fmaxf(L[1][u][2], L[1][u][3])));
-        const float mnew = fmaxf(mrun[u], mx);
-        const float sc = fast_exp2(mrun[u] - mnew);
-        mrun[u] = mnew;
         f32x4 P0, P1;
+        if (bounded) {  // logits already shifted by mu
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          P0[r] = fast_exp2(L[0][u][r] - mnew);
-          P1[r] = fast_exp2(L[1][u][r] - mnew);
+          for (int r = 0; r < 4; ++r) {
+            P0[r] = fast_exp2(L[0][u][r]);
+            P1[r] = fast_exp2(L[1][u][r]);
+          }
+          lam[u] += ((P0[0] + P0[1]) + (P0[2] + P0[3])) + ((P1[0] + P1[1]) + (P1[2] + P1[3]));
+          const bf16x8 pb = pack_tiles(P0, P1);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) yt[u][db] = mfma_k32(zt[db], pb, yt[u][db]);
+        } else {  // running max
+          float mx = fmaxf(max3(L[0][u][0], L[0][u][1], L[0][u][2]), max3(L[0][u][3], L[1][u][0], L[1][u][1]));
+          mx = max_over_rows(fmaxf(mx, fmaxf(L[1][u][2], L[1][u][3])));
+          const float mnew = fmaxf(mrun[u], mx);
+          const float sc = fast_exp2(mrun[u] - mnew);
+          mrun[u] = mnew;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            P0[r] = fast_exp2(L[0][u][r] - mnew);
+            P1[r] = fast_exp2(L[1][u][r] - mnew);
+          }
+          lam[u] = lam[u] * sc + ((P0[0] + P0[1]) + (P0[2] + P0[3])) + ((P1[0] + P1[1]) + (P1[2] + P1[3]));
+          const bf16x8 pb = pack_tiles(P0, P1);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) yt[u][db] = mfma_k32(zt[db], pb, yt[u][db] * sc);
         }
-        lam[u] = lam[u] * sc + ((P0[0] + P0[1]) + (P0[2] + P0[3])) + ((P1[0] + P1[1]) + (P1[2] + P1[3]));
-        const bf16x8 pb = pack_tiles(P0, P1);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) yt[u][db] = mfma_k32(zt[db], pb, yt[u][db] * sc);
       }
     }
     float nA[2], nDl[2];
@@ -581,24 +652,25 @@ __global__ __launch_bounds__(512) void bwd_dec_tok_bf16(BwdDecArgs a) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int m0 = 32 * kb + 16 * t;
-        const kop_t qh = *reinterpret_cast<const kop_t*>(sQh + (m0 + l16) * D + KL * g);
-        const kop_t ql = *reinterpret_cast<const kop_t*>(sQl + (m0 + l16) * D + KL * g);
-        const kop_t zh = *reinterpret_cast<const kop_t*>(sZh + (m0 + l16) * D + KL * g);
-        const kop_t zl = *reinterpret_cast<const kop_t*>(sZl + (m0 + l16) * D + KL * g);
+        const kop_t qh = row_operand<D>(sQh, m0, l16, g);
+        const kop_t ql = row_operand<D>(sQl, m0, l16, g);
+        const kop_t zh = row_operand<D>(sZh, m0, l16, g);
+        const kop_t zl = row_operand<D>(sZl, m0, l16, g);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           f32x4 L = KOperand<D>::mma(qh, kb_op[u], splat4(nA[u]));
           L = KOperand<D>::mma(ql, kb_op[u], L);
+          if (ragged && kb == nkb - 1) mask_pad(L, m0);
           f32x4 dp = KOperand<D>::mma(zh, gb_op[u], splat4(nDl[u]));
           dp = KOperand<D>::mma(zl, gb_op[u], dp);
           dp = KOperand<D>::mma(zh, gl_op[u], dp);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) dL[t][u][r] = m0 + 4 * g + r < a.M ? fast_exp2(L[r]) * dp[r] : 0.0f;
+          for (int r = 0; r < 4; ++r) dL[t][u][r] = fast_exp2(L[r]) * dp[r];
         }
       }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const bf16x8 qt = tr_operand(sQt + (16 * db + l16) * kBwdTS, 32 * kb, g);
+        const bf16x8 qt = tr_rows<D>(sQh, kb, db, l16, g);
 #pragma unroll
         for (int u = 0; u < 2; ++u) dkt[u][db] = mfma_k32(qt, pack_tiles(dL[0][u], dL[1][u]), dkt[u][db]);
       }
@@ -609,7 +681,7 @@ __global__ __launch_bounds__(512) void bwd_dec_tok_bf16(BwdDecArgs a) {
       if (n < n1) {
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          *reinterpret_cast<f32x4*>(a.dK + (bh * (int64_t)a.N + n) * D + 16 * db + 4 * g) = dkt[u][db] * a.s;
+          *reinterpret_cast<f32x4*>(a.dK + (bh * (int64_t)a.N + n) * D + 16 * db + 4 * g) = dkt[u][db] * a.kscale;
       }
     }
   }
@@ -655,20 +727,21 @@ __global__ __launch_bounds__(512) void bwd_dec_lat_bf16(BwdDecArgs a) {
     for (int db = 0; db < DB; ++db) dzt[t][db] = dqt[t][db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   const __bf16* Kh = a.K + bh * (int64_t)a.N * D;
-  const float* Gh = a.dY + bh * (int64_t)a.N * D;
+  const __bf16* Gh = a.dyh + lbh * (int64_t)a.N * D;
+  const __bf16* Gl = a.dyl + lbh * (int64_t)a.N * D;
   // per-token statistics of the head: rows of a.tstride floats (a multiple
   // of 4, so a lane's four tokens are one aligned 16-byte load)
   const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(a.tA + lbh * a.tstride, (uint32_t)(a.tstride * 4));
   const __amdgpu_buffer_rsrc_t rD = buffer_rsrc(a.tD + lbh * a.tstride, (uint32_t)(a.tstride * 4));
   // the next step's K, dY and statistics are loaded while this one computes
-  kop_t kn[2];
-  DyRaw<D> yn[2];
+  kop_t kn[2], hn[2], ln[2];
   f32x4 an[2], dn[2];
   auto load_step = [&](int64_t tb) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       kn[hh] = tok_operand<D>(Kh, tb + 16 * hh, n1, l16, g);
-      yn[hh].load(Gh, tb + 16 * hh, n1, l16, g);
+      hn[hh] = tok_operand<D>(Gh, tb + 16 * hh, n1, l16, g);
+      ln[hh] = tok_operand<D>(Gl, tb + 16 * hh, n1, l16, g);
       an[hh] = buffer_load<f32x4>(rA, (int)(tb + 16 * hh + 4 * g) * 4);
       dn[hh] = buffer_load<f32x4>(rD, (int)(tb + 16 * hh + 4 * g) * 4);
     }
@@ -681,12 +754,18 @@ __global__ __launch_bounds__(512) void bwd_dec_lat_bf16(BwdDecArgs a) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       ka[hh] = kn[hh];
-      split_hilo<D>(yn[hh].x0, yn[hh].x1, ga[hh], gl[hh]);
+      ga[hh] = hn[hh];
+      gl[hh] = ln[hh];
+      if (tb + 32 <= n1) {
+        na[hh] = -an[hh];
+        nd[hh] = -dn[hh];
+      } else {  // the split's last, partial step
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool live = tb + 16 * hh + 4 * g + r < n1;
-        na[hh][r] = live ? -an[hh][r] : -INFINITY;
-        nd[hh][r] = live ? -dn[hh][r] : 0.0f;
+        for (int r = 0; r < 4; ++r) {
+          const bool live = tb + 16 * hh + 4 * g + r < n1;
+          na[hh][r] = live ? -an[hh][r] : -INFINITY;
+          nd[hh][r] = live ? -dn[hh][r] : 0.0f;
+        }
       }
     }
     if (tb + 32 < n1) load_step(tb + 32);

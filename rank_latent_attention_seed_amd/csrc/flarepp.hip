@@ -61,7 +61,7 @@ struct Plan {
   // bf16 backward: latent operands as bf16 (rows [G][Mp][D], transposed [.][D][Mt]),
   // Mt = M rounded up to 32, tokens per token-pass workgroup
   int Mt, tchunk;
-  size_t o_zh, o_zl, o_zt2, o_qdt, o_dzt, o_dqt, o_st, o_dzr, o_dzl, o_dqr, o_dql;
+  size_t o_zh, o_zl, o_dzr, o_dzl, o_dqr, o_dql, o_dyh, o_dyl, o_del1;
   // spectrum: Gram partials [G][Jg][M][M] over Jg token splits of gchunk, and the reduced [G][M][M]
   int Jg, gchunk;
   size_t o_gpart, o_mat;
@@ -178,7 +178,7 @@ Plan make_plan(const flarepp_desc* d, int op, const flarepp_tuning* t = nullptr)
   p.o_shi = p.o_slo = p.o_sqn = p.o_part = p.o_knorm = p.o_qhi = p.o_qlo = p.o_qnorm = p.o_bias =
       p.o_zt = p.o_qf = p.o_zf = none;
   p.o_lse1 = p.o_lse2 = p.o_tlse = p.o_tdel = p.o_dz = p.o_dq3 = p.o_dq = p.o_del = none;
-  p.o_zh = p.o_zl = p.o_zt2 = p.o_qdt = p.o_dzt = p.o_dqt = p.o_st = p.o_dzr = p.o_dzl = p.o_dqr = p.o_dql = none;
+  p.o_zh = p.o_zl = p.o_dzr = p.o_dzl = p.o_dqr = p.o_dql = p.o_dyh = p.o_dyl = p.o_del1 = none;
   p.Mt = (int)cdiv(d->M, 32) * 32;
   {
     // token passes of the bf16 backward: one workgroup per CU over the group
@@ -187,7 +187,6 @@ Plan make_plan(const flarepp_desc* d, int op, const flarepp_tuning* t = nullptr)
   }
   p.o_gpart = p.o_mat = none;
   if (bwd && p.bf16) {
-    const size_t trn = D * (size_t)p.Mt * 2;  // one bf16 [D][Mt] block
     p.o_shi = take(p.nS * opnd);
     p.o_slo = take(p.nS * opnd);
     p.o_part = take(G_ * p.J * Mp * std::max<size_t>(D + 4, 2 * D) * 4);
@@ -208,15 +207,13 @@ Plan make_plan(const flarepp_desc* d, int op, const flarepp_tuning* t = nullptr)
     p.o_del = take(G_ * Mp * 4);
     p.o_zh = take(G_ * opnd);
     p.o_zl = take(G_ * opnd);
-    p.o_zt2 = take(G_ * trn);
-    p.o_qdt = take(G_ * trn);
-    p.o_dzt = take(G_ * trn);
-    p.o_dqt = take(G_ * trn);
-    p.o_st = take(p.nS * trn);
+    p.o_del1 = take(G_ * Mp * 4);
     p.o_dzr = take(G_ * opnd);
     p.o_dzl = take(G_ * opnd);
     p.o_dqr = take(G_ * opnd);
     p.o_dql = take(G_ * opnd);
+    p.o_dyh = take(G_ * (size_t)p.N * D * 2);
+    p.o_dyl = take(G_ * (size_t)p.N * D * 2);
   } else if (bwd) {
     p.o_part = take(G_ * p.J * Mp * std::max<size_t>(D + 4, 2 * D) * 4);
     p.o_qf = take(G_ * p.M * D * 4);
@@ -876,7 +873,7 @@ template <int D>
 flarepp_status run_backward_bf16(const Plan& p, const void* S, const void* K, const void* V, const float* dY,
                                  float* dS, float* dK, float* dV, void* ws, hipStream_t st) {
   Recorder rec;
-  const int64_t MD = (int64_t)p.M * D, MpD = (int64_t)p.Mp * D, DMt = (int64_t)D * p.Mt;
+  const int64_t MD = (int64_t)p.M * D, MpD = (int64_t)p.Mp * D;
   const int64_t seed_h = p.nS > 1 ? MD : 0;
   fill_zero<<<(unsigned)cdiv((int64_t)p.nS * MD, 256), 256, 0, st>>>(dS, (int64_t)p.nS * MD);
   FLAREPP_TRY(launched());
@@ -893,11 +890,6 @@ flarepp_status run_backward_bf16(const Plan& p, const void* S, const void* K, co
   float* del = at<float>(ws, p.o_del);
   __bf16* zh = at<__bf16>(ws, p.o_zh);
   __bf16* zl = at<__bf16>(ws, p.o_zl);
-  __bf16* zt = at<__bf16>(ws, p.o_zt2);
-  __bf16* qdt = at<__bf16>(ws, p.o_qdt);
-  __bf16* dzt = at<__bf16>(ws, p.o_dzt);
-  __bf16* dqt = at<__bf16>(ws, p.o_dqt);
-  __bf16* sT = at<__bf16>(ws, p.o_st);
   __bf16* dzr = at<__bf16>(ws, p.o_dzr);
   __bf16* dzl = at<__bf16>(ws, p.o_dzl);
   __bf16* dqr = at<__bf16>(ws, p.o_dqr);
@@ -910,7 +902,6 @@ flarepp_status run_backward_bf16(const Plan& p, const void* S, const void* K, co
   };
   // seed operands (c S as hi/lo for the forward, S^T for stage 1's dK)
   FLAREPP_TRY(run_prep<D>(p, S, true, 0, seed_h, p.nS, shi, slo, nullptr, nullptr, p.c, st, rec));
-  FLAREPP_TRY(prep(S, true, seed_h, p.nS, false, 1.0f, nullptr, nullptr, sT));
   for (int64_t g0 = 0; g0 < p.BH; g0 += p.G) {
     const int Gc = (int)std::min<int64_t>(p.G, p.BH - g0);
     // ---- forward stages 1 and 2, as in the route
@@ -956,19 +947,20 @@ flarepp_status run_backward_bf16(const Plan& p, const void* S, const void* K, co
     };
     const dim3 tok_grid((unsigned)cdiv(p.N, p.tchunk), (unsigned)Gc);
     const dim3 lat_grid((unsigned)p.J, (unsigned)Gc);
-    // ---- stage 3 (decode)
-    FLAREPP_TRY(prep(zf, false, MD, Gc, true, 1.0f, zh, zl, zt));
-    FLAREPP_TRY(prep(qf, false, MD, Gc, false, 1.0f, nullptr, nullptr, qdt));
+    // ---- stage 3 (decode): token pass (its dK part, per-token statistics), latent pass
+    FLAREPP_TRY(prep(zf, false, MD, Gc, true, 1.0f, zh, zl, nullptr));
+    const float kscale = p.c != 0.0f ? p.s / p.c : 0.0f;
     {
       BwdDecArgs d{};
       d.qhi = qhi;
       d.qlo = qlo;
-      d.qdt = qdt;
       d.zh = zh;
       d.zl = zl;
-      d.zt = zt;
       d.K = static_cast<const __bf16*>(K);
-      d.dY = dY;
+      d.dyh = at<__bf16>(ws, p.o_dyh);
+      d.dyl = at<__bf16>(ws, p.o_dyl);
+      d.qnorm = at<float>(ws, p.o_qnorm);
+      d.c = p.c;
       d.dK = dK;
       d.tA = at<float>(ws, p.o_tlse);
       d.tD = at<float>(ws, p.o_tdel);
@@ -983,6 +975,11 @@ flarepp_status run_backward_bf16(const Plan& p, const void* S, const void* K, co
       d.Mt = p.Mt;
       d.bh0 = g0;
       d.s = p.s;
+      d.kscale = kscale;
+      BwdDySplitArgs ys{dY + g0 * (int64_t)p.N * D, at<__bf16>(ws, p.o_dyh), at<__bf16>(ws, p.o_dyl),
+                        (int64_t)Gc * p.N * D};
+      bwd_dy_split<<<(unsigned)cdiv(ys.n / 4, 256), 256, 0, st>>>(ys);
+      FLAREPP_TRY(launched());
       bwd_dec_tok_bf16<D><<<tok_grid, 512, 0, st>>>(d);
       FLAREPP_TRY(launched());
       bwd_dec_lat_bf16<D><<<lat_grid, 512, 0, st>>>(d);
@@ -990,55 +987,62 @@ flarepp_status run_backward_bf16(const Plan& p, const void* S, const void* K, co
       FLAREPP_TRY(reduce(2 * D, D, nullptr, dz, zf, del, 0));            // dZ, delta_2 = <dZ, Z>
       FLAREPP_TRY(reduce(2 * D, 0, nullptr, dq3, nullptr, nullptr, 0));  // dQd from the decode
     }
-    // ---- stages 2 and 1
-    auto enc_stage = [&](const __bf16* hi, const __bf16* lo, int64_t q_sb, int64_t q_sh, int64_t q_off,
-                         const __bf16* qt, int64_t t_sb, int64_t t_sh, int64_t t_off, const __bf16* dor,
-                         const __bf16* dorl, const __bf16* dot, const float* lse, int acc_dv) {
+    // ---- stages 2 and 1: latent passes, then one token pass for both
+    BwdStageOps ops[2];
+    ops[0] = BwdStageOps{qhi, qlo, (int64_t)p.H * MpD, MpD, g0 * MpD, dzr, dzl, at<float>(ws, p.o_lse2), nullptr};
+    ops[1] = BwdStageOps{shi, slo, 0, p.nS > 1 ? MpD : 0, 0, dqr, dql, at<float>(ws, p.o_lse1), nullptr};
+    auto enc_latent = [&](const BwdStageOps& o, const float* delta) {
       BwdEncArgs e{};
-      e.qhi = hi;
-      e.qlo = lo;
-      e.q_sb = q_sb;
-      e.q_sh = q_sh;
-      e.q_off = q_off;
-      e.qt = qt;
-      e.t_sb = t_sb;
-      e.t_sh = t_sh;
-      e.t_off = t_off;
-      e.dor = dor;
-      e.dorl = dorl;
-      e.dot = dot;
-      e.lse = lse;
-      e.delta = del;
+      e.qhi = o.qhi;
+      e.qlo = o.qlo;
+      e.q_sb = o.q_sb;
+      e.q_sh = o.q_sh;
+      e.q_off = o.q_off;
+      e.dor = o.dor;
+      e.dorl = o.dorl;
+      e.lse = o.lse;
+      e.delta = delta;
       e.K = static_cast<const __bf16*>(K);
       e.V = static_cast<const __bf16*>(V);
-      e.dK = dK;
-      e.dV = dV;
-      e.acc_dk = 1;  // the decode wrote dK first
-      e.acc_dv = acc_dv;
       e.part = part;
       e.J = p.J;
       e.chunk = p.chunk;
-      e.tchunk = p.tchunk;
       e.H = p.H;
       e.N = p.N;
       e.M = p.M;
       e.Mp = p.Mp;
-      e.Mt = p.Mt;
       e.bh0 = g0;
       e.s = p.s;
-      bwd_enc_tok_bf16<D><<<tok_grid, 512, 0, st>>>(e);
-      FLAREPP_TRY(launched());
       bwd_enc_lat_bf16<D><<<lat_grid, 512, 0, st>>>(e);
       return launched();
     };
-    FLAREPP_TRY(prep(dz, false, MD, Gc, false, 1.0f, dzr, dzl, dzt));
-    FLAREPP_TRY(enc_stage(qhi, qlo, (int64_t)p.H * MpD, MpD, g0 * MpD, qdt, (int64_t)p.H * DMt, DMt, g0 * DMt, dzr,
-                          dzl, dzt, at<float>(ws, p.o_lse2), 0));
-    FLAREPP_TRY(reduce(D, 0, dq3, dq, qf, del, 0));  // dQd = encode + decode parts, delta_1 = <dQd, Qd>
-    FLAREPP_TRY(prep(dq, false, MD, Gc, false, 1.0f, dqr, dql, dqt));
-    FLAREPP_TRY(enc_stage(shi, slo, 0, p.nS > 1 ? MpD : 0, 0, sT, 0, p.nS > 1 ? DMt : 0, 0, dqr, dql, dqt,
-                          at<float>(ws, p.o_lse1), 1));
+    float* del2 = del;
+    float* del1 = at<float>(ws, p.o_del1);
+    FLAREPP_TRY(prep(dz, false, MD, Gc, false, 1.0f, dzr, dzl, nullptr));
+    FLAREPP_TRY(enc_latent(ops[0], del2));
+    FLAREPP_TRY(reduce(D, 0, dq3, dq, qf, del1, 0));  // dQd = encode + decode parts, delta_1 = <dQd, Qd>
+    FLAREPP_TRY(prep(dq, false, MD, Gc, false, 1.0f, dqr, dql, nullptr));
+    FLAREPP_TRY(enc_latent(ops[1], del1));
     FLAREPP_TRY(reduce(D, 0, nullptr, dS, nullptr, nullptr, p.nS));
+    ops[0].delta = del2;
+    ops[1].delta = del1;
+    BwdEncTokArgs t{};
+    t.st[0] = ops[0];
+    t.st[1] = ops[1];
+    t.K = static_cast<const __bf16*>(K);
+    t.V = static_cast<const __bf16*>(V);
+    t.dK = dK;
+    t.dV = dV;
+    t.tchunk = p.tchunk;
+    t.H = p.H;
+    t.N = p.N;
+    t.M = p.M;
+    t.Mp = p.Mp;
+    t.Mt = p.Mt;
+    t.bh0 = g0;
+    t.kscale = kscale;
+    bwd_enc_tok_bf16<D><<<tok_grid, 512, 0, st>>>(t);
+    FLAREPP_TRY(launched());
   }
   return FLAREPP_OK;
 }
