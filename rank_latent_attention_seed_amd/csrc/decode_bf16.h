@@ -300,6 +300,13 @@ __global__ __launch_bounds__(128, 2) void decode_pair_bf16(DecodeArgs a) {
   // latent rows of this wave at or past M (the padding of the last block and
   // whole blocks past the end) get weight zero
   const int mvalid = a.M - mb0 * 16;
+  // ragged: block ipart holds the first row at or past M (rows 4 g + r of it
+  // with 4 g + r >= rem take padb = -inf); later blocks are all padding.
+  // Additive per-lane biases keep the masks out of scalar registers.
+  const int ipart = mvalid >> 4, rem = mvalid & 15;
+  f32x4 padb;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) padb[r] = 4 * g + r < rem ? 0.0f : -INFINITY;
 
   // K and Y of this workgroup's tokens as buffer resources: tokens past n1
   // read as zeros and their stores are dropped
@@ -333,11 +340,12 @@ __global__ __launch_bounds__(128, 2) void decode_pair_bf16(DecodeArgs a) {
         float lm = -INFINITY;
 #pragma unroll
         for (int i = 0; i < MBH; ++i) {
+          if (RAGGED && i > ipart) continue;
           f32x4 t = KOperand<D>::mma(qh[i], kb, f32x4{0.f, 0.f, 0.f, 0.f});
           t = KOperand<D>::mma(ql[i], kb, t);
+          if (RAGGED && i == ipart) t += padb;
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (!RAGGED || i * 16 + 4 * g + r < mvalid) lm = fmaxf(lm, t[r]);
+          for (int r = 0; r < 4; ++r) lm = fmaxf(lm, t[r]);
         }
         lm = max_over_rows(lm);
         if (g == 0) sMax[w2][c16] = lm;
@@ -362,9 +370,10 @@ __global__ __launch_bounds__(128, 2) void decode_pair_bf16(DecodeArgs a) {
           L[u] = KOperand<D>::mma(qh[i], kb, cinit);
           L[u] = KOperand<D>::mma(ql[i], kb, L[u]);
           if (RAGGED) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (i * 16 + 4 * g + r >= mvalid) L[u][r] = -INFINITY;
+            if (i == ipart)
+              L[u] += padb;
+            else if (i > ipart)
+              L[u] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
           }
         } else {
           L[u] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};

@@ -99,6 +99,8 @@ EDGE = [
     (1, 1, 1000, 256, 32, "bf16"),
     (2, 2, 4097, 33, 32, "bf16"),
     (1, 3, 300, 48, 16, "bf16"),
+    (1, 2, 3000, 200, 32, "bf16"),   # paired decode with padding rows (M not a multiple of 32)
+    (1, 1, 1500, 143, 16, "bf16"),
     (1, 1, 1, 1, 32, "f32"),
     (1, 2, 77, 19, 16, "f32"),
     (2, 1, 1000, 256, 32, "f32"),
@@ -132,6 +134,14 @@ def test_large_logits_take_the_online_path(fp):
     p = inputs.random_problem(1, 1, 3000, 32, 16, dtype="bf16", scale=0.5, seed=3, sigma=4.0,
                               sigma_v=1.0)
     run_and_compare(fp, p, label="large logits")
+
+
+def test_large_logits_ragged_paired_decode(fp):
+    # the decode's exact-max fallback with padding rows in a wave's latent
+    # blocks (M = 200: 13 blocks over the two waves of a token block)
+    p = inputs.random_problem(1, 1, 2000, 200, 16, dtype="bf16", scale=0.5, seed=4, sigma=4.0,
+                              sigma_v=1.0)
+    run_and_compare(fp, p, label="large logits, ragged paired decode")
 
 
 def test_stages_match_oracle(fp):
