@@ -53,6 +53,12 @@ struct EncodeArgs {
   const __bf16* q_lo;  // low part of the same
   int64_t q_sb, q_sh;  // element strides of the operand between batches / heads
   int64_t q_off;       // the operand rows of (b, h) start at b*q_sb + h*q_sh - q_off
+  // Alternatively (q_seed non-null) the unscaled bf16 query rows [.][M][D],
+  // with the same (b, h) addressing; the operands are then formed here as
+  // hi = bf16(qc * row), lo = bf16(qc * row - hi), rows at or past M zero.
+  const __bf16* q_seed;
+  float qc;
+  int M;
   const __bf16* K;     // B x H x N x D
   const __bf16* V;     // B x H x N x D
   float* part;         // [G][Mp][J][D + 4] partial records (G = heads of this launch)
@@ -649,8 +655,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void encode_split_bf16(EncodeArgs 
       const int mblk = mb0 + i;
       if (mblk < nMB) {
         const int m = mblk * 16 + c16;
-        st.qh[i] = *reinterpret_cast<const kop_t*>(a.q_hi + qo + (int64_t)m * D + KL * g);
-        st.ql[i] = *reinterpret_cast<const kop_t*>(a.q_lo + qo + (int64_t)m * D + KL * g);
+        if (a.q_seed) {
+          kop_t x = kop_t{};
+          if (m < a.M) x = *reinterpret_cast<const kop_t*>(a.q_seed + qo + (int64_t)m * D + KL * g);
+#pragma unroll
+          for (int e = 0; e < KL; ++e) {
+            const float xs = a.qc * (float)x[e];
+            const __bf16 hi = (__bf16)xs;
+            st.qh[i][e] = hi;
+            st.ql[i][e] = (__bf16)(xs - (float)hi);
+          }
+        } else {
+          st.qh[i] = *reinterpret_cast<const kop_t*>(a.q_hi + qo + (int64_t)m * D + KL * g);
+          st.ql[i] = *reinterpret_cast<const kop_t*>(a.q_lo + qo + (int64_t)m * D + KL * g);
+        }
         st.mu[i] = (BOUNDED && a.bias) ? a.bias[lbh * a.Mp + m] : 0.0f;
       } else {
         st.qh[i] = kop_t{};

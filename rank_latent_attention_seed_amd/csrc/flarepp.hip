@@ -158,7 +158,7 @@ Plan make_plan(const flarepp_desc* d, int op, const flarepp_tuning* t = nullptr)
   // workspace layout
   const size_t G_ = (size_t)p.G, Mp = (size_t)p.Mp, D = (size_t)p.D;
   const size_t opnd = Mp * D * 2;  // one bf16 Mp x D block
-  const bool route = op == FLAREPP_OP_ROUTE, seed = op == FLAREPP_OP_SEED_ENCODE;
+  const bool route = op == FLAREPP_OP_ROUTE;
   const bool enc = op == FLAREPP_OP_ENCODE, dec = op == FLAREPP_OP_DECODE, flare = op == FLAREPP_OP_FLARE;
   const bool bwd = op == FLAREPP_OP_ROUTE_BACKWARD;
   const bool spec = op == FLAREPP_OP_SPECTRUM;
@@ -227,10 +227,10 @@ Plan make_plan(const flarepp_desc* d, int op, const flarepp_tuning* t = nullptr)
     p.o_dq = take(G_ * p.M * D * 4);
     p.o_del = take(G_ * Mp * 4);
   } else if (p.bf16) {
-    if (route || seed || flare || spec) {
+    if (flare) {
       p.o_shi = take(p.nS * opnd);
       p.o_slo = take(p.nS * opnd);
-      if (flare) p.o_sqn = take(p.nS * Mp * 4);
+      p.o_sqn = take(p.nS * Mp * 4);
     }
     if (!dec) p.o_part = take(G_ * p.J * Mp * (D + 4) * 4);
     if (route || spec) p.o_knorm = take(G_ * p.J * 4);
@@ -459,6 +459,8 @@ MergeArgs merge_args(const Plan& p, void* ws, int64_t g0) {
 void refit_from(MergeArgs& m, const EncodeArgs& e) {
   m.fq_hi = e.q_hi;
   m.fq_lo = e.q_lo;
+  m.fq_seed = e.q_seed;
+  m.fq_c = e.qc;
   m.fq_sb = e.q_sb;
   m.fq_sh = e.q_sh;
   m.fq_off = e.q_off;
@@ -528,7 +530,9 @@ flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in
   if (p.bf16) {
     __bf16* shi = at<__bf16>(ws, p.o_shi);
     __bf16* slo = at<__bf16>(ws, p.o_slo);
-    if (stage == kSeed || stage == kRoute || stage == kFlare || stage == kSpectrum)
+    // FLARE's decode takes c S as its key operand; the other stages form the
+    // seed encode's query operands from S inside the encode
+    if (stage == kFlare)
       FLAREPP_TRY(run_prep<D>(p, S, true, 0, seed_h, p.nS, shi, slo, nullptr, at<float>(ws, p.o_sqn), p.c, st, rec));
     for (int64_t g0 = 0; g0 < p.BH; g0 += p.G) {
       const int Gc = (int)std::min<int64_t>(p.G, p.BH - g0);
@@ -539,11 +543,18 @@ flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in
       const bool routed = stage == kRoute || stage == kSpectrum;  // stages 1 and 2 as in the route
       if (stage == kSeed || routed || stage == kFlare) {
         EncodeArgs e = encode_args(p, ws, K, V, g0);
-        e.q_hi = shi;
-        e.q_lo = slo;
         e.q_sb = 0;
-        e.q_sh = p.nS > 1 ? MpD : 0;
         e.q_off = 0;
+        if (stage == kFlare) {  // the prepared c S operands
+          e.q_hi = shi;
+          e.q_lo = slo;
+          e.q_sh = p.nS > 1 ? MpD : 0;
+        } else {  // formed from S in the encode
+          e.q_seed = static_cast<const __bf16*>(S);
+          e.qc = p.c;
+          e.M = p.M;
+          e.q_sh = seed_h;
+        }
         e.knorm = at<float>(ws, p.o_knorm);
         if (routed)
           FLAREPP_TRY((run_encode_bf16<D, true, false>(p, e, Gc, st, rec, FLAREPP_KERNEL_SEED_ENCODE)));

@@ -40,6 +40,8 @@ struct MergeArgs {
   // (b, h) at b*fq_sb + h*fq_sh - fq_off), K, V and token splits.
   const __bf16* fq_hi;
   const __bf16* fq_lo;
+  const __bf16* fq_seed;  // or the unscaled rows [.][M][D] the encode formed them from (EncodeArgs::q_seed)
+  float fq_c;
   int64_t fq_sb, fq_sh, fq_off;
   const __bf16* fK;
   const __bf16* fV;
@@ -59,7 +61,15 @@ __device__ __forceinline__ void refit_record(const MergeArgs& a, int64_t bh, int
   const int64_t qo = (int64_t)b * a.fq_sb + (int64_t)h * a.fq_sh - a.fq_off + (int64_t)m * D;
   float q[D];
 #pragma unroll
-  for (int d = 0; d < D; ++d) q[d] = (float)a.fq_hi[qo + d] + (float)a.fq_lo[qo + d];
+  for (int d = 0; d < D; ++d) {
+    if (a.fq_seed) {  // the encode's own rounding of c * row into hi + lo
+      const float xs = a.fq_c * (float)a.fq_seed[qo + d];
+      const __bf16 hi = (__bf16)xs;
+      q[d] = (float)hi + (float)(__bf16)(xs - (float)hi);
+    } else {
+      q[d] = (float)a.fq_hi[qo + d] + (float)a.fq_lo[qo + d];
+    }
+  }
   const int n0 = j * a.chunk, n1 = min(a.N, n0 + a.chunk);
   const __bf16* Kp = a.fK + bh * (int64_t)a.N * D;
   const __bf16* Vp = a.fV + bh * (int64_t)a.N * D;
