@@ -4,8 +4,9 @@
 // Launch sequence of the route for the bf16 path, per launch group of G
 // (b, h) pairs (by default all of them: one launch per kernel, whose splits
 // fill the GPU in one round):
-//   prep    seeds -> c*S as a bf16 hi/lo operand (once per call)
-//   encode  split-N seed encode, also records each split's max key norm
+//   encode  split-N seed encode (its query operands, c*S as bf16 hi/lo,
+//           formed from S as it loads them), also records each split's max
+//           key norm
 //   merge   -> Qd (caller's copy, bf16 hi/lo operand, row norms, the bound for
 //              the next encode)
 //   encode  split-N encode with Qd
