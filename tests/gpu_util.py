@@ -100,6 +100,41 @@ def route_poisoned(fp, S, K, V, scale, tuning=None):
     return Y, Qd, Z
 
 
+def backward_poisoned(fp, S, K, V, scale, dY):
+    """dS, dK, dV of flarepp_route_backward with the workspace and the three
+    gradient outputs NaN-poisoned before the call."""
+    import torch
+
+    desc = fp.desc_for(S, K, scale)
+    dS = poisoned(tuple(S.shape))
+    dK, dV = poisoned(tuple(K.shape)), poisoned(tuple(K.shape))
+    n = fp.flarepp_workspace_size(desc, fp.OP_ROUTE_BACKWARD)
+    ws = poisoned((max(n, 1),), torch.uint8)
+    st = fp.flarepp_route_backward(desc, S.data_ptr(), K.data_ptr(), V.data_ptr(), dY.data_ptr(), dS.data_ptr(),
+                                   dK.data_ptr(), dV.data_ptr(), ws.data_ptr(), n, fp._stream(None))
+    if st != 0:
+        raise fp.FlareppError(st, "flarepp_route_backward")
+    return dS, dK, dV
+
+
+def spectrum_poisoned(fp, S, K, V, scale):
+    """Eigenvalues and G of flarepp_spectrum with the workspace and both
+    outputs NaN-poisoned before the call."""
+    import torch
+
+    desc = fp.desc_for(S, K, scale)
+    B, H, N, D = K.shape
+    M = desc.M
+    eig, G = poisoned((B, H, M)), poisoned((B, H, M, M))
+    n = fp.flarepp_workspace_size(desc, fp.OP_SPECTRUM)
+    ws = poisoned((max(n, 1),), torch.uint8)
+    st = fp.flarepp_spectrum(desc, S.data_ptr(), K.data_ptr(), V.data_ptr(), eig.data_ptr(), G.data_ptr(),
+                             ws.data_ptr(), n, fp._stream(None))
+    if st != 0:
+        raise fp.FlareppError(st, "flarepp_spectrum")
+    return eig, G
+
+
 def compare_route(p, Y, Qd, Z, heads=None, ref=None):
     """Element-wise comparison of the route's three outputs with the oracle
     on the listed heads (all by default); returns the oracle results."""

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 from rank_latent_attention_seed_amd import inputs
-from gpu_util import to_device
+from gpu_util import backward_poisoned, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +35,8 @@ def run_and_compare(fp, p, label, seed=0):
     rng = np.random.default_rng(seed + 100)
     dY = rng.standard_normal((p.B, p.H, p.N, p.D)).astype(np.float32)
     S, K, V, G = to_device(p.S), to_device(p.K), to_device(p.V), to_device(dY)
-    dS, dK, dV = fp.route_backward(S, K, V, p.scale, G)
+    # workspace and gradients NaN-poisoned: every element must be written
+    dS, dK, dV = backward_poisoned(fp, S, K, V, p.scale, G)
     torch.cuda.synchronize()
     rS, rK, rV = oracle.route_backward(p.S, p.K, p.V, p.scale, dY.astype(np.float64))
     # normwise per gradient tensor: max|err| / max|ref| of that tensor.  A

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 from rank_latent_attention_seed_amd import inputs
-from gpu_util import to_device
+from gpu_util import spectrum_poisoned, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +31,8 @@ def run_and_compare(fp, p, label):
 
     print(f"\n  case {label}: B{p.B} H{p.H} N{p.N} M{p.M} D{p.D} {p.dtype} s={p.scale:g}", flush=True)
     S, K, V = to_device(p.S), to_device(p.K), to_device(p.V)
-    eig, G = fp.spectrum(S, K, V, p.scale, with_matrix=True)
+    # workspace and outputs NaN-poisoned: every element must be written
+    eig, G = spectrum_poisoned(fp, S, K, V, p.scale)
     torch.cuda.synchronize()
     eig, G = eig.cpu().numpy().astype(np.float64), G.cpu().numpy().astype(np.float64)
     ref = spectral.spectrum(p.S, p.K, p.V, p.scale)
