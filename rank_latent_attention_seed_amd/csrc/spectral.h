@@ -449,9 +449,11 @@ __global__ __launch_bounds__(512) void spectral_gram_mfma(SpecMfmaArgs a) {
 // Gershgorin interval: the number of eigenvalues below x is the number of
 // negative terms of the Sturm sequence q_0 = d_0 - x,
 // q_i = d_i - x - e_{i-1}^2 / q_{i-1} (tiny pivots replaced by -pivmin, as in
-// LAPACK's bisection), one eigenvalue per thread, halving until the interval
-// is below 2 ulp of the spectrum's scale.  Output by decreasing value,
-// eig[(bh0 + lbh) * M ...].
+// LAPACK's bisection; the division by the hardware reciprocal, 1 ulp, so the
+// count is that of a tridiagonal within a few ulp of (d, e)), four threads per
+// eigenvalue counting at four points that cut its interval into fifths,
+// until the interval is below 2 ulp of the spectrum's scale.  Output by
+// decreasing value, eig[(bh0 + lbh) * M ...].
 struct EigArgs {
   const float* mat;  // [G][M][M]
   float* eig;        // [BH][M]
@@ -463,7 +465,7 @@ __device__ __forceinline__ int tri_at(int i, int j) { return i * (i + 1) / 2 + j
 
 __global__ __launch_bounds__(1024) void tridiag_eigvals(EigArgs a) {
   __shared__ float sA[kSpecMaxM * (kSpecMaxM + 1) / 2];
-  __shared__ float sv[kSpecMaxM], sp[kSpecMaxM], sd[kSpecMaxM], se[kSpecMaxM];
+  __shared__ float sv[kSpecMaxM], sp[kSpecMaxM], sd[kSpecMaxM], se[kSpecMaxM], se2[kSpecMaxM];
   __shared__ float sred[16];
   __shared__ float sbeta;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -506,23 +508,55 @@ __global__ __launch_bounds__(1024) void tridiag_eigvals(EigArgs a) {
     __syncthreads();
     const float beta = sbeta;
     if (beta != 0.0f) {
-      // p = beta A' v, rows i = wave, wave + 16, ...; and this wave's part of v^T p
-      float vp = 0.0f;
-      for (int i = wave; i < n; i += 16) {
+      // p = beta A' v: four threads per row (thread 4 i + q takes the columns
+      // q, q + 4, ...), a two-step reduction within the quad; then each
+      // wave's part of v^T p
+      const int i = tid >> 2, q = tid & 3;
+      float acc = 0.0f;
+      if (i < n) {
         const int gi = r0 + i;
-        float acc = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int jj = lane + 64 * q;
-          if (jj < n) {
-            const int gj = r0 + jj;
-            acc = fmaf(sA[gi >= gj ? tri_at(gi, gj) : tri_at(gj, gi)], sv[jj], acc);
+        // columns j <= i: row gi of the packed triangle, contiguous (four
+        // independent sums so the LDS reads of four columns overlap)
+        const float* row = sA + tri_at(gi, r0);
+        float a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+        int jj = q;
+        for (; jj + 12 <= i; jj += 16) {
+          acc = fmaf(row[jj], sv[jj], acc);
+          a1 = fmaf(row[jj + 4], sv[jj + 4], a1);
+          a2 = fmaf(row[jj + 8], sv[jj + 8], a2);
+          a3 = fmaf(row[jj + 12], sv[jj + 12], a3);
+        }
+        for (; jj <= i; jj += 4) acc = fmaf(row[jj], sv[jj], acc);
+        // columns j > i: entry (r0 + j, gi); offsets advance by
+        // tri(x + 4) - tri(x) = 4 x + 10 between the thread's columns
+        if (jj < n) {
+          int off = tri_at(r0 + jj, gi);
+          for (; jj + 12 < n; jj += 16) {
+            const int o1 = off + 4 * (r0 + jj) + 10;
+            const int o2 = o1 + 4 * (r0 + jj + 4) + 10;
+            const int o3 = o2 + 4 * (r0 + jj + 8) + 10;
+            acc = fmaf(sA[off], sv[jj], acc);
+            a1 = fmaf(sA[o1], sv[jj + 4], a1);
+            a2 = fmaf(sA[o2], sv[jj + 8], a2);
+            a3 = fmaf(sA[o3], sv[jj + 12], a3);
+            off = o3 + 4 * (r0 + jj + 12) + 10;
+          }
+          for (; jj < n; jj += 4) {
+            acc = fmaf(sA[off], sv[jj], acc);
+            off += 4 * (r0 + jj) + 10;
           }
         }
-        acc = beta * wave_sum(acc);
-        if (lane == 0) sp[i] = acc;
-        vp = fmaf(acc, sv[i], vp);
+        acc = (acc + a1) + (a2 + a3);
       }
+      acc += dpp<0xB1>(acc);  // quad_perm [1,0,3,2]
+      acc += dpp<0x4E>(acc);  // quad_perm [2,3,0,1]
+      acc *= beta;
+      float vp = 0.0f;
+      if (i < n && q == 0) {
+        sp[i] = acc;
+        vp = acc * sv[i];
+      }
+      vp = wave_sum(vp);
       if (lane == 0) sred[wave] = vp;
     }
     __syncthreads();
@@ -531,12 +565,40 @@ __global__ __launch_bounds__(1024) void tridiag_eigvals(EigArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) vtp += sred[v];
       const float kc = 0.5f * beta * vtp;
-      for (int i = wave; i < n; i += 16) {
-        const float vi = sv[i], wi = sp[i] - kc * vi;
-        float* row = sA + tri_at(r0 + i, r0);
-        for (int jj = lane; jj <= i; jj += 64) {
-          const float vj = sv[jj], wj = sp[jj] - kc * vj;
-          row[jj] -= fmaf(vi, wj, wi * vj);
+      // w_j = p_j - kc v_j for this lane's columns (lane + 64 c), once per step
+      float vl[4], wl[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int jj = lane + 64 * c;
+        vl[c] = jj < n ? sv[jj] : 0.0f;
+        wl[c] = jj < n ? sp[jj] - kc * vl[c] : 0.0f;
+      }
+      // rows i = wave, wave + 16, ...: A'_ij -= v_i w_j + w_i v_j for j <= i,
+      // four rows per pass, every load of a pass issued before its stores
+      for (int i0 = wave; i0 < n; i0 += 64) {
+        float x[4][4], vr[4], wr[4];
+        float* rows[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + 16 * u;
+          const bool live = i < n;
+          vr[u] = live ? sv[i] : 0.0f;
+          wr[u] = live ? sp[i] - kc * vr[u] : 0.0f;
+          rows[u] = sA + tri_at(r0 + (live ? i : i0), r0);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int jj = lane + 64 * c;
+            x[u][c] = live && jj <= i ? rows[u][jj] : 0.0f;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = i0 + 16 * u;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int jj = lane + 64 * c;
+            if (i < n && jj <= i) rows[u][jj] = x[u][c] - fmaf(vr[u], wl[c], wr[u] * vl[c]);
+          }
         }
       }
     }
@@ -550,36 +612,47 @@ __global__ __launch_bounds__(1024) void tridiag_eigvals(EigArgs a) {
     sd[M - 1] = sA[tri_at(M - 1, M - 1)];
   }
   __syncthreads();
-  // bisection, thread t finds the t-th smallest eigenvalue
-  const int t = tid;
-  if (t >= M) return;
+  for (int i = tid; i < M; i += 1024) se2[i] = se[i] * se[i];
+  __syncthreads();
+  // multisection: the four threads of a quad share eigenvalue e = tid / 4 and
+  // count at four interior points of its interval, which then shrinks five-fold
+  const int e = tid >> 2, sub = tid & 3;
+  if (e >= M) return;  // whole quads leave together
   float glo = INFINITY, ghi = -INFINITY, e2max = 0.0f;
   for (int i = 0; i < M; ++i) {
     const float r = (i > 0 ? fabsf(se[i - 1]) : 0.0f) + (i + 1 < M ? fabsf(se[i]) : 0.0f);
     glo = fminf(glo, sd[i] - r);
     ghi = fmaxf(ghi, sd[i] + r);
-    if (i + 1 < M) e2max = fmaxf(e2max, se[i] * se[i]);
+    if (i + 1 < M) e2max = fmaxf(e2max, se2[i]);
   }
   const float scale = fmaxf(fabsf(glo), fabsf(ghi));
   const float pivmin = FLT_MIN * fmaxf(1.0f, e2max);
   const float tol = 2.0f * FLT_EPSILON * scale + FLT_MIN;
   float lo = glo - tol, hi = ghi + tol;
-  for (int it = 0; it < 100 && hi - lo > tol; ++it) {
-    const float x = 0.5f * (lo + hi);
+  for (int it = 0; it < 64 && hi - lo > tol; ++it) {
+    const float step = (hi - lo) * 0.2f;
+    const float x = lo + step * (float)(sub + 1);
     int cnt = 0;
     float q = sd[0] - x;
     for (int i = 0;; ++i) {
       if (fabsf(q) < pivmin) q = -pivmin;
       cnt += q < 0.0f;
       if (i + 1 == M) break;
-      q = (sd[i + 1] - x) - se[i] * se[i] / q;
+      q = (sd[i + 1] - x) - se2[i] * __builtin_amdgcn_rcpf(q);
     }
-    if (cnt > t)
-      hi = x;
-    else
-      lo = x;
+    const float c = (float)cnt;
+    const float cs[4] = {dpp<0x00>(c), dpp<0x55>(c), dpp<0xAA>(c), dpp<0xFF>(c)};
+    float nlo = lo + step * 4.0f, nhi = hi;  // no count above e: the last fifth
+#pragma unroll
+    for (int k = 3; k >= 0; --k)
+      if (cs[k] > (float)e) {
+        nhi = lo + step * (float)(k + 1);
+        nlo = k == 0 ? lo : lo + step * (float)k;
+      }
+    lo = nlo;
+    hi = nhi;
   }
-  a.eig[(a.bh0 + blockIdx.x) * M + (M - 1 - t)] = 0.5f * (lo + hi);
+  if (sub == 0) a.eig[(a.bh0 + blockIdx.x) * M + (M - 1 - e)] = 0.5f * (lo + hi);
 }
 
 }  // namespace flarepp
