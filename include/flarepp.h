@@ -275,6 +275,44 @@ flarepp_status flarepp_route_noalloc(const flarepp_desc *desc, const void *S, co
 /* Bytes of the built-in scratch of flarepp_route_noalloc. */
 size_t flarepp_noalloc_scratch_bytes(void);
 
+/*
+ * Token shards (context parallelism; French technical summary, "Contributions
+ * Clés": the tokens are split across devices and only the latent outputs and
+ * the softmax statistics are exchanged).  A device holding tokens
+ * [n0, n1) of every (b, h) runs an encode stage over them alone and emits,
+ * per latent row, the shard's combined record (acc = sum of w V, lambda =
+ * sum of w, mu = the shift, in log2 units, with w = 2^(c <q, k> - mu));
+ * records of all shards, merged, give the stage's rows exactly as the
+ * split-N merge does within one device.  The decode needs no exchange: run
+ * flarepp_decode on each shard with the merged Qd and Z.
+ *
+ * Records: float32, [B*H][Mp][nslots][D + 4] with Mp = M rounded up to a
+ * multiple of 16; element d < D of a record is acc_d, element D is lambda,
+ * element D + 1 is mu (D + 2, D + 3 unused).  flarepp_shard_records_size
+ * gives the bytes of a buffer for nslots shards.
+ *
+ * flarepp_encode_shard: desc describes this shard (N = its token count; B, H,
+ * M, D, dtype, scale, seed_head_stride as for the whole problem); K and V
+ * hold its tokens (B x H x N x D, desc dtype).  stage 1: Q = the seeds S (as
+ * in flarepp_seed_encode), giving Qd's records; stage 2: Q = Qd (float32
+ * rows B x H x M x D, the merged stage-1 result), giving Z's records.  The
+ * call writes slot `slot` (0 <= slot < nslots) of every record of `rec` and
+ * nothing else.  Workspace: flarepp_workspace_size with
+ * FLAREPP_OP_SEED_ENCODE (stage 1) or FLAREPP_OP_ENCODE (stage 2) for this
+ * desc.  INVALID_ARG for another stage or slot.
+ *
+ * flarepp_merge_shards: desc describes the whole problem (its N is not
+ * used); out (B x H x M x D float32) receives the merged rows -- Qd after
+ * stage 1, Z after stage 2.  No workspace.  Every slot of rec must have been
+ * written.
+ */
+flarepp_status flarepp_shard_records_size(const flarepp_desc *desc, int32_t nslots, size_t *bytes);
+flarepp_status flarepp_encode_shard(const flarepp_desc *desc, int32_t stage, const void *Q,
+                                    const void *K, const void *V, float *rec, int32_t slot,
+                                    int32_t nslots, void *ws, size_t ws_bytes, void *stream);
+flarepp_status flarepp_merge_shards(const flarepp_desc *desc, const float *rec, int32_t nslots,
+                                    float *out, void *stream);
+
 /* Kernel kinds reported by flarepp_route_profiled. */
 typedef enum flarepp_kernel_kind {
     FLAREPP_KERNEL_PREP = 0,        /* query / value operand preparation */

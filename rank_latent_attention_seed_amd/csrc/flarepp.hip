@@ -67,6 +67,9 @@ struct Plan {
   int Jg, gchunk;
   size_t o_gpart, o_mat;
   int nS;           // seed / fixed-query operand blocks (1 or H)
+  // token-shard encodes: the stage's merge writes the shard's records here
+  float* rec = nullptr;
+  int rec_slot = 0, rec_nslots = 1;
   size_t o_shi, o_slo, o_sqn, o_part, o_knorm, o_qhi, o_qlo, o_qnorm, o_bias, o_zt, o_qf, o_zf, total;
 };
 
@@ -452,6 +455,9 @@ MergeArgs merge_args(const Plan& p, void* ws, int64_t g0) {
   m.M = p.M;
   m.bh0 = g0;
   m.c = p.c;
+  m.rec_out = p.rec;
+  m.rec_slot = p.rec_slot;
+  m.rec_nslots = p.rec_nslots;
   return m;
 }
 
@@ -1353,6 +1359,74 @@ flarepp_status flarepp_route_profiled(const flarepp_desc* desc, const void* S, c
   *n_launches = rec.n;
   if (st == FLAREPP_OK && rec.failed) return FLAREPP_HIP_ERROR;
   return st;
+}
+
+// ---- token shards (context parallelism): one shard's share of an encode
+// stage as records, and the merge of the records of all shards.
+
+flarepp_status flarepp_shard_records_size(const flarepp_desc* desc, int32_t nslots, size_t* bytes) {
+  if (!bytes || nslots < 1) return FLAREPP_INVALID_ARG;
+  FLAREPP_TRY(check_desc(desc));
+  *bytes = (size_t)desc->B * desc->H * (size_t)cdiv(desc->M, 16) * 16 * (size_t)nslots * (desc->D + 4) * 4;
+  return FLAREPP_OK;
+}
+
+flarepp_status flarepp_encode_shard(const flarepp_desc* desc, int32_t stage, const void* Q, const void* K,
+                                    const void* V, float* rec, int32_t slot, int32_t nslots, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  FLAREPP_TRY(check_desc(desc));
+  if ((stage != 1 && stage != 2) || nslots < 1 || slot < 0 || slot >= nslots) return FLAREPP_INVALID_ARG;
+  const Sizes z = sizes(desc);
+  size_t recb = 0;
+  FLAREPP_TRY(flarepp_shard_records_size(desc, nslots, &recb));
+  const void* in[3] = {Q, K, V};
+  const size_t inb[3] = {stage == 1 ? z.s : z.md, z.kv, z.kv};
+  const void* out[1] = {rec};
+  const size_t outb[1] = {recb};
+  const bool req[1] = {true};
+  Plan p;
+  FLAREPP_TRY(prologue(desc, stage == 1 ? FLAREPP_OP_SEED_ENCODE : FLAREPP_OP_ENCODE, in, inb, 3, out, outb, req, 1,
+                       ws, ws_bytes, &p));
+  p.rec = rec;
+  p.rec_slot = slot;
+  p.rec_nslots = nslots;
+  if (stage == 1) return dispatch(p, kSeed, Q, nullptr, nullptr, K, V, nullptr, nullptr, nullptr, ws, stream);
+  return dispatch(p, kEncode, nullptr, static_cast<const float*>(Q), nullptr, K, V, nullptr, nullptr, nullptr, ws,
+                  stream);
+}
+
+flarepp_status flarepp_merge_shards(const flarepp_desc* desc, const float* rec, int32_t nslots, float* out,
+                                    void* stream) {
+  FLAREPP_TRY(check_desc(desc));
+  if (nslots < 1 || !rec || !out || misaligned(rec) || misaligned(out)) return FLAREPP_INVALID_ARG;
+  size_t recb = 0;
+  FLAREPP_TRY(flarepp_shard_records_size(desc, nslots, &recb));
+  const Sizes z = sizes(desc);
+  if (overlap(range(out, z.md), range(rec, recb))) return FLAREPP_ALIASING;
+  Plan p = make_plan(desc, FLAREPP_OP_ROUTE);
+  p.J = nslots;  // one record per shard and row
+  int tpr = 1;
+  while (tpr < p.J && tpr < 64) tpr *= 2;
+  p.tpr = tpr;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Recorder rcd;
+  const int64_t PS = p.D + 4;
+  for (int64_t g0 = 0; g0 < p.BH; g0 += p.G) {
+    const int Gc = (int)std::min<int64_t>(p.G, p.BH - g0);
+    MergeArgs m{};
+    m.part = const_cast<float*>(rec) + g0 * p.Mp * (int64_t)nslots * PS;  // read only: no refit
+    m.J = nslots;
+    m.Mp = p.Mp;
+    m.M = p.M;
+    m.bh0 = g0;
+    m.c = p.c;
+    m.out = out;
+    if (p.D == 16)
+      FLAREPP_TRY(run_merge<16>(p, m, Gc, st, rcd));
+    else
+      FLAREPP_TRY(run_merge<32>(p, m, Gc, st, rcd));
+  }
+  return FLAREPP_OK;
 }
 
 }  // extern "C"

@@ -35,6 +35,12 @@ struct MergeArgs {
   float* bias;         // [G][Mp] bound |c| ||row|| max||K|| for the next encode (+inf if unsafe), or null
   float c;
   float* lse;          // [G][Mp] log-sum-exp of the row's softmax, log2 units (mu + log2 lambda), or null
+  // Record mode (rec_out non-null): instead of the rows, write each row's
+  // combined record -- the unnormalised (acc, lambda, mu) -- to slot rec_slot
+  // of rec_out [BH][Mp][rec_nslots][D + 4] (a token shard's share of the
+  // stage, for a later merge over the shards).
+  float* rec_out;
+  int rec_slot, rec_nslots;
   // The encode whose records are merged, for refit_record (fK null: none is
   // recomputed): its query operand rows (bf16 hi/lo of c * Q, the rows of
   // (b, h) at b*fq_sb + h*fq_sh - fq_off), K, V and token splits.
@@ -162,6 +168,19 @@ __global__ __launch_bounds__(256) void merge_partials(MergeArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) x[4 * d4 + e] = group_sum<T>(num[d4][e]);
 
+  if (a.rec_out) {
+    if (!row_ok) return;
+    float* o = a.rec_out + ((bh * a.Mp + m) * (int64_t)a.rec_nslots + a.rec_slot) * PS;
+    for (int d = q; d < D; d += T) {
+      float v = x[0];
+#pragma unroll
+      for (int e = 1; e < D; ++e) v = (d == e) ? x[e] : v;
+      o[d] = v;
+    }
+    if (q == 0) *reinterpret_cast<f32x4*>(o + D) = f32x4{den, mx, 0.0f, 0.0f};
+    return;
+  }
+
   const bool real = m < a.M;
   const float inv = 1.0f / den;
   float n2 = 0.0f;
@@ -276,6 +295,12 @@ __global__ __launch_bounds__(256) void merge_rows256(MergeArgs a) {
   const bool real = m < a.M;
   const float den = sRed[0][D] + sRed[1][D] + sRed[2][D] + sRed[3][D];
   const int d = lane < D ? lane : 0;
+  if (a.rec_out) {  // record mode (see MergeArgs)
+    float* o = a.rec_out + ((bh * a.Mp + m) * (int64_t)a.rec_nslots + a.rec_slot) * PS;
+    if (lane < D) o[lane] = sRed[0][d] + sRed[1][d] + sRed[2][d] + sRed[3][d];
+    if (lane == 0) *reinterpret_cast<f32x4*>(o + D) = f32x4{den, mx, 0.0f, 0.0f};
+    return;
+  }
   float x = (sRed[0][d] + sRed[1][d] + sRed[2][d] + sRed[3][d]) / den;
   if (!real || lane >= D) x = 0.0f;
   const float nrm = sqrtf(wave_sum(x * x));

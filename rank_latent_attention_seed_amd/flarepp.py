@@ -26,7 +26,8 @@ SYMBOLS = ("flarepp_abi_version", "flarepp_status_string", "flarepp_workspace_si
            "flarepp_seed_encode", "flarepp_encode", "flarepp_decode", "flarepp_route",
            "flarepp_flare", "flarepp_route_backward", "flarepp_spectrum", "flarepp_route_profiled",
            "flarepp_workspace_size_tuned", "flarepp_route_tuned", "flarepp_route_noalloc",
-           "flarepp_noalloc_scratch_bytes")
+           "flarepp_noalloc_scratch_bytes", "flarepp_shard_records_size", "flarepp_encode_shard",
+           "flarepp_merge_shards")
 KERNEL_KINDS = {0: "prep", 1: "seed_encode", 2: "encode", 3: "merge", 4: "decode"}
 
 
@@ -105,6 +106,12 @@ def _lib():
         lib.flarepp_route_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp]
         lib.flarepp_noalloc_scratch_bytes.restype = sz
         lib.flarepp_noalloc_scratch_bytes.argtypes = []
+        lib.flarepp_shard_records_size.restype = ctypes.c_int
+        lib.flarepp_shard_records_size.argtypes = [dp, i32, ctypes.POINTER(sz)]
+        lib.flarepp_encode_shard.restype = ctypes.c_int
+        lib.flarepp_encode_shard.argtypes = [dp, i32, vp, vp, vp, vp, i32, i32, vp, sz, vp]
+        lib.flarepp_merge_shards.restype = ctypes.c_int
+        lib.flarepp_merge_shards.argtypes = [dp, vp, i32, vp, vp]
         if lib.flarepp_abi_version() != ABI_VERSION:
             raise RuntimeError("libflarepp ABI version mismatch")
         _LIB = lib
@@ -161,6 +168,22 @@ def flarepp_route_tuned(desc, tuning, S, K, V, Y, Qd_out, Z_out, ws, ws_bytes, s
 
 def flarepp_route_noalloc(desc, S, K, V, Y, Qd_out, Z_out, stream) -> int:
     return _lib().flarepp_route_noalloc(ctypes.byref(desc), S, K, V, Y, Qd_out, Z_out, stream)
+
+
+def flarepp_shard_records_size(desc, nslots) -> int:
+    n = ctypes.c_size_t(0)
+    _check(_lib().flarepp_shard_records_size(ctypes.byref(desc), int(nslots), ctypes.byref(n)),
+           "flarepp_shard_records_size")
+    return n.value
+
+
+def flarepp_encode_shard(desc, stage, Q, K, V, rec, slot, nslots, ws, ws_bytes, stream) -> int:
+    return _lib().flarepp_encode_shard(ctypes.byref(desc), int(stage), Q, K, V, rec, int(slot), int(nslots), ws,
+                                       ws_bytes, stream)
+
+
+def flarepp_merge_shards(desc, rec, nslots, out, stream) -> int:
+    return _lib().flarepp_merge_shards(ctypes.byref(desc), rec, int(nslots), out, stream)
 
 
 def flarepp_noalloc_scratch_bytes() -> int:
@@ -268,6 +291,46 @@ def _stream(stream):
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def route_sharded(S, K, V, scale, bounds, *, stream=None):
+    """(Y, Qd, Z) of the route computed the context-parallel way over the token
+    shards [bounds[i], bounds[i+1]): per stage every shard emits its records
+    (flarepp_encode_shard), the records of all shards are merged
+    (flarepp_merge_shards), and each shard decodes its own tokens.  Here the
+    shards run one after another on one device, and the record buffer stands
+    in for the exchange between devices."""
+    torch = _torch()
+    for t, n in ((S, "S"), (K, "K"), (V, "V")):
+        _require(t, n)
+    B, H, N, D = K.shape
+    if bounds[0] != 0 or bounds[-1] != N or any(b1 <= b0 for b0, b1 in zip(bounds, bounds[1:])):
+        raise ValueError("bounds must rise strictly from 0 to N")
+    ns = len(bounds) - 1
+    full = desc_for(S, K, scale)
+    M = full.M
+    shards = [(K[:, :, b0:b1].contiguous(), V[:, :, b0:b1].contiguous()) for b0, b1 in zip(bounds, bounds[1:])]
+    descs = [desc_for(S, k, scale) for k, _ in shards]
+    rec = torch.empty(flarepp_shard_records_size(full, ns) // 4, dtype=torch.float32, device=K.device)
+    Qd = torch.empty((B, H, M, D), dtype=torch.float32, device=K.device)
+    Z = torch.empty((B, H, M, D), dtype=torch.float32, device=K.device)
+    st = _stream(stream)
+    for stage, q, out in ((1, S, Qd), (2, Qd, Z)):
+        op = OP_SEED_ENCODE if stage == 1 else OP_ENCODE
+        for i, ((k, v), d) in enumerate(zip(shards, descs)):
+            n = flarepp_workspace_size(d, op)
+            ws = torch.empty(max(n, 1), dtype=torch.uint8, device=K.device)
+            _check(flarepp_encode_shard(d, stage, _ptr(q), _ptr(k), _ptr(v), _ptr(rec), i, ns, _ptr(ws), n, st),
+                   "flarepp_encode_shard")
+        _check(flarepp_merge_shards(full, _ptr(rec), ns, _ptr(out), st), "flarepp_merge_shards")
+    Ys = []
+    for (k, _), d in zip(shards, descs):
+        y = torch.empty(k.shape, dtype=torch.float32, device=K.device)
+        n = flarepp_workspace_size(d, OP_DECODE)
+        ws = torch.empty(max(n, 1), dtype=torch.uint8, device=K.device)
+        _check(flarepp_decode(d, _ptr(Qd), _ptr(Z), _ptr(k), _ptr(y), _ptr(ws), n, st), "flarepp_decode")
+        Ys.append(y)
+    return torch.cat(Ys, dim=2), Qd, Z
 
 
 def route(S, K, V, scale, *, with_intermediates=False, workspace: Workspace | None = None, stream=None,

@@ -141,6 +141,35 @@ def test_backward_validation(dt):
     assert bwd(dS=addr(6)) == ALIASING             # output inside the workspace
 
 
+def test_shard_validation():
+    lib = fp.library()
+    d = desc()
+    n = ctypes.c_size_t(0)
+    assert lib.flarepp_shard_records_size(ctypes.byref(d), 3, ctypes.byref(n)) == OK
+    assert n.value == 2 * 3 * 64 * 3 * (32 + 4) * 4  # B H Mp slots (D + 4) floats
+    assert lib.flarepp_shard_records_size(ctypes.byref(d), 0, ctypes.byref(n)) == INVALID_ARG
+    assert lib.flarepp_shard_records_size(ctypes.byref(desc(M=17)), 1, ctypes.byref(n)) == OK
+    assert n.value == 2 * 3 * 32 * (32 + 4) * 4  # Mp = 32
+    nws = ws_status(d, fp.OP_SEED_ENCODE)[1]
+
+    def shard(stage=1, slot=0, nslots=2, rec=addr(4), nbytes=nws, dd=d):
+        return fp.flarepp_encode_shard(dd, stage, addr(0), addr(1), addr(2), rec, slot, nslots, addr(6), nbytes, None)
+
+    # every case fails validation on the host, before any HIP call
+    assert shard(stage=3) == INVALID_ARG
+    assert shard(slot=2) == INVALID_ARG
+    assert shard(slot=-1) == INVALID_ARG
+    assert shard(nslots=0) == INVALID_ARG
+    assert shard(rec=None) == INVALID_ARG
+    assert shard(rec=addr(4) + 8) == INVALID_ARG    # misaligned
+    assert shard(nbytes=nws - 1) == WS_SMALL
+    assert shard(rec=addr(1) + 256) == ALIASING     # records inside K
+    assert shard(dd=desc(D=24)) == UNSUPPORTED
+    assert fp.flarepp_merge_shards(d, addr(4), 0, addr(5), None) == INVALID_ARG
+    assert fp.flarepp_merge_shards(d, addr(4), 2, None, None) == INVALID_ARG
+    assert fp.flarepp_merge_shards(d, addr(4), 2, addr(4) + 64, None) == ALIASING
+
+
 def test_spectrum_validation():
     for dt in (fp.BF16, fp.F32):
         st, n = ws_status(desc(dtype=dt), fp.OP_SPECTRUM)
