@@ -29,6 +29,9 @@ Rank 0 prints one JSON line:
   backward (bf16 inputs on the matrix cores, and float32 copies on the float32
   path, each with its time over the forward route's) and the mixing-matrix
   spectrum on the same inputs;
+* token_shards = one GPU's share of the route split over --shards token
+  ranges (its shard's encodes and decode plus the merges of all shards'
+  records), against the route time over the shard count;
 * cpu_baseline = the oracle (single-threaded C, fp64) on a bounded sample of
   the same problem, with the host's core count and CPU model.
 
@@ -368,6 +371,67 @@ def spectrum_record(fp, torch, r: Route, steps: int) -> dict:
             "mean_top4_eigenvalues": [round(x, 6) for x in top]}
 
 
+def shard_record(fp, torch, r: Route, shards: int, steps: int, route_ms: float) -> dict:
+    """One GPU's share of the route sharded over `shards` equal token ranges
+    (context parallelism): stage-1 encode of its shard to its record slot,
+    merge of all slots, stage-2 encode, merge, decode of its shard.  The other
+    shards' records are written once before timing and stay in place; the
+    exchange of records between devices is not part of the timed work (its
+    payload per stage is reported).  share_efficiency = (route time / shards)
+    over this time: the fraction of linear speed-up one shard's work allows
+    before any exchange."""
+    p = r.p
+    N = p.N
+    bounds = [N * i // shards for i in range(shards + 1)]
+    K = [r.K[:, :, b0:b1].contiguous() for b0, b1 in zip(bounds, bounds[1:])]
+    V = [r.V[:, :, b0:b1].contiguous() for b0, b1 in zip(bounds, bounds[1:])]
+    descs = [fp.desc_for(r.S, k, p.scale) for k in K]
+    rec_bytes = fp.flarepp_shard_records_size(r.desc, shards)
+    rec = torch.empty(rec_bytes // 4, dtype=torch.float32, device="cuda")
+    Qd = torch.empty((p.B, p.H, p.M, p.D), dtype=torch.float32, device="cuda")
+    Z = torch.empty_like(Qd)
+    Y0 = torch.empty(K[0].shape, dtype=torch.float32, device="cuda")
+    wsn = max(max(fp.flarepp_workspace_size(d, op) for op in (fp.OP_SEED_ENCODE, fp.OP_ENCODE, fp.OP_DECODE))
+              for d in descs)
+    ws = torch.empty(max(wsn, 1), dtype=torch.uint8, device="cuda")
+
+    def ok(st, name):
+        if st != 0:
+            raise fp.FlareppError(st, name)
+
+    def encode(stage, i):
+        q = r.S if stage == 1 else Qd
+        ok(fp.flarepp_encode_shard(descs[i], stage, q.data_ptr(), K[i].data_ptr(), V[i].data_ptr(),
+                                   rec.data_ptr(), i, shards, ws.data_ptr(), wsn, r.stream), "flarepp_encode_shard")
+
+    def merge(out):
+        ok(fp.flarepp_merge_shards(r.desc, rec.data_ptr(), shards, out.data_ptr(), r.stream), "flarepp_merge_shards")
+
+    for stage, out in ((1, Qd), (2, Z)):
+        for i in range(shards):
+            encode(stage, i)
+        merge(out)
+
+    def share_step():
+        encode(1, 0)
+        merge(Qd)
+        encode(2, 0)
+        merge(Z)
+        ok(fp.flarepp_decode(descs[0], Qd.data_ptr(), Z.data_ptr(), K[0].data_ptr(), Y0.data_ptr(),
+                             ws.data_ptr(), wsn, r.stream), "flarepp_decode")
+
+    warm(share_step, torch, 4)
+    sms = statistics.median(time_steps(share_step, torch, r.stream, steps))
+    eff = route_ms / shards / sms
+    log(f"[bench] token shards ({shards}): one shard's share {sms:.3f} ms, route/{shards} = "
+        f"{route_ms / shards:.3f} ms, share efficiency {eff:.3f}; records {rec_bytes / 1e6:.2f} MB per stage")
+    out = {"shards": shards, "tokens_per_shard": bounds[1], "ms_per_step": sms, "steps": steps,
+           "share_efficiency": round(eff, 4), "record_bytes_per_stage": rec_bytes,
+           "exchange": "not timed (one GPU)"}
+    del K, V, rec, ws, Y0
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
     ap.add_argument("--gpus", type=int, default=1)
@@ -385,6 +449,8 @@ def main() -> int:
                     help="timed calls of the float32 backward on the same shapes (0 = skip)")
     ap.add_argument("--spectrum-steps", type=int, default=2,
                     help="timed calls of the mixing-matrix spectrum on the same inputs (0 = skip)")
+    ap.add_argument("--shards", type=int, default=4,
+                    help="token shards for the one-GPU share of a context-parallel route (0 = skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="after the timed runs, copy MIB MiB device-to-device once (a kernel of known "
                          "traffic, for scaling hardware byte counters)")
@@ -392,8 +458,8 @@ def main() -> int:
                     help="tokens of one head for the oracle baseline (0 = skip)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the route's "
-              "multi-GPU token sharding is not built", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the exchange of "
+              "token-shard records between GPUs is not built", file=sys.stderr)
         return 2
     if os.environ.get("WORLD_SIZE", "1") not in ("", "1"):
         print("bench.py runs as a single process on one GPU", file=sys.stderr)
@@ -487,6 +553,7 @@ def main() -> int:
 
     bwd = backward_record(fp, torch, r, args.backward_steps, ms) if args.backward_steps > 0 else None
     spec = spectrum_record(fp, torch, r, args.spectrum_steps) if args.spectrum_steps > 0 else None
+    shard = shard_record(fp, torch, r, args.shards, max(args.steps // 2, 3), ms) if args.shards > 1 else None
 
     if args.calibrate_copy > 0:
         n = args.calibrate_copy << 20
@@ -528,6 +595,7 @@ def main() -> int:
         "flare": flare,
         "backward": bwd,
         "spectrum": spec,
+        "token_shards": shard,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
