@@ -33,8 +33,8 @@
 // registers (common.h).  Latent operands are staged in LDS as rows with
 // XOR-swizzled 16-byte chunks (the route's encode tile layout, slot_off), so
 // both the row operand and the transposed one (ds_read_b64_tr_b16) read
-// without bank conflicts; the K tile of a latent-pass step is transposed
-// into LDS by one wave.
+// without bank conflicts; the latent passes stream their token operands
+// through LDS tiles of the same layout (LatTiles).
 #pragma once
 
 #include "common.h"
@@ -43,8 +43,6 @@
 namespace flarepp {
 
 constexpr int kBwdBf16MaxM = 256;
-// LDS row stride (elements) of a transposed 32-token tile [D][token]
-constexpr int kBwdTT = 32 + 8;
 
 // Latent-side operands of a stage as bf16 from float32 (or bf16) rows.
 // Block k of the source is its rows src + k * src_blk ([M][D]); output
@@ -112,14 +110,6 @@ struct BwdEncArgs {
   int64_t bh0;
   float s;
 };
-
-// the bf16x8 operand of 32 latents (or tokens) kb: k slots 4 g .. 4 g + 3 and
-// 16 + 4 g .. 16 + 4 g + 3 of LDS row `row`
-__device__ __forceinline__ bf16x8 tr_operand(const __bf16* row, int c0, int g) {
-  const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(row + c0 + 4 * g);
-  const bf16x4 x1 = *reinterpret_cast<const bf16x4*>(row + c0 + 16 + 4 * g);
-  return bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-}
 
 // weights of two C tiles (rows 4 g .. 4 g + 3 of tiles 0 and 1) as the k slots
 // of one operand
@@ -340,17 +330,89 @@ __global__ __launch_bounds__(512) void bwd_enc_tok_bf16(BwdEncTokArgs a) {
   }
 }
 
+// ---- token tiles of the latent passes.  A workgroup streams its split's
+// tokens through LDS in tiles of TT = 4096 / D tokens: NOP bf16 operands of
+// 8 KB each ([TT][D] rows with the encode tile's chunk swizzle, so the row
+// operand and the transposing read are both free of bank conflicts) and,
+// with STATS, two float rows of TT (the decode's per-token A_n and
+// <dY_n, Y'_n>).  Three slots: the barrier that opens tile u is taken after
+// every wave has finished tile u - 1, and right after it the loads of tile
+// u + 2 go into the slot tile u - 1 held, so two tiles are in flight while
+// one is read.  The loads go straight to LDS (dma16), each wave waits for its
+// own before the barrier, and no register carries a token operand from one
+// step to the next.  Tiles past the split re-read its last token (the
+// masks give those zero weight), so every wave issues the same loads per
+// tile and the wait counts are constants.
+template <int D, int NOP, bool STATS>
+struct LatTiles {
+  static constexpr int TT = 4096 / D;               // tokens per tile
+  static constexpr int OPE = TT * D;                // bf16 per operand tile (8 KB)
+  static constexpr int SLOT = NOP * OPE + (STATS ? 4 * TT : 0);
+  static constexpr int NSI = STATS ? TT / 128 : 0;  // 1 KB loads of the statistics
+  static constexpr int STEPS = TT / 32;
+};
+
+// Issue wave `wave`'s loads of the tile at token tb into slot `sl`: chunk
+// 64 wave + lane of every operand (lane l of a load fills LDS chunk
+// base + 16 l, so it fetches the (token, chunk) the swizzle places there);
+// waves below NSI also load 1 KB of the [A | D] statistics rows.
+template <int D, int NOP, bool STATS>
+__device__ __forceinline__ void lat_tile_dma(__bf16* sl, const __bf16* const (&src)[NOP], const float* tA,
+                                             const float* tD, int64_t tb, int64_t n1, int wave, int lane) {
+  typedef LatTiles<D, NOP, STATS> T;
+  constexpr int U = D / 8;
+  const int c = wave * 64 + lane;
+  const int t = c / U;
+  const int u = (c % U) ^ chunk_swz<D>(t);
+  const int64_t row = min(tb + t, n1 - 1);
+#pragma unroll
+  for (int o = 0; o < NOP; ++o) dma16(src[o] + row * D + 8 * u, sl + o * T::OPE + wave * 512);
+  if (STATS && wave < T::NSI) {
+    const bool isA = 4 * c < T::TT;
+    const int64_t tok = min(tb + (isA ? 4 * c : 4 * c - T::TT), (n1 - 1) & ~int64_t(3));
+    dma16(reinterpret_cast<const __bf16*>((isA ? tA : tD) + tok), sl + NOP * T::OPE + wave * 512);
+  }
+}
+
+// Wait until this wave's loads of the oldest tile in flight have landed
+// (those of the next tile may still be in flight), then open it to the
+// workgroup.  The lgkm wait makes this wave's reads of the previous tile
+// complete before any wave refills that slot.
+template <int D, int NOP, bool STATS>
+__device__ __forceinline__ void lat_tile_open(int wave) {
+  typedef LatTiles<D, NOP, STATS> T;
+  if (STATS && wave < T::NSI)
+    FLAREPP_WAIT_VM(NOP + 1);
+  else
+    FLAREPP_WAIT_VM(NOP);
+  __builtin_amdgcn_s_waitcnt(kEncWaitLgkm0);
+  ring_barrier();
+}
+
+// Transposed operand of a 32-token step from a tile (lane: row element
+// 16 db + l16, k slots tokens 4 g .. 4 g + 3 and 16 + 4 g .. 16 + 4 g + 3):
+// p = step base + slot_off(4 g + l16 / 4, 16 db + 4 (l16 % 4)).
+template <int D>
+__device__ __forceinline__ bf16x8 tr_at(const __bf16* p) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  const bf16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+  const bf16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 16 * D));
+  return bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+}
+
 // ---- encode-stage latent pass: split partials of dQ_m = s sum_n dL_mn K_n.
 // Per 32-token step: L^T = K (c Q)^T - A (rows tokens, cols latents),
-// dP^T = V dO^T - delta, dL = 2^L dP (zero past the split), dQ^T += K^T dL^T
-// with K^T read from a transposed LDS copy of the step's tile.
+// dP^T = V dO^T - delta, dL = 2^L dP (zero past the split), dQ^T += K^T dL^T,
+// K and V from the LDS tiles (K^T through transposing reads).
 template <int D>
 __global__ __launch_bounds__(512) void bwd_enc_lat_bf16(BwdEncArgs a) {
   constexpr int KL = KOperand<D>::kLen;
   constexpr int DB = D / 16;
   typedef typename KOperand<D>::T kop_t;
-  __shared__ __attribute__((aligned(16))) __bf16 sKt[2][D * kBwdTT];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  typedef LatTiles<D, 2, false> T;
+  __shared__ __attribute__((aligned(16))) __bf16 ring[3 * T::SLOT];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const int j = blockIdx.x;
   const int64_t lbh = blockIdx.y, bh = a.bh0 + lbh;
@@ -381,64 +443,72 @@ __global__ __launch_bounds__(512) void bwd_enc_lat_bf16(BwdEncArgs a) {
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int db = 0; db < DB; ++db) dqt[t][db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // the latent operands must not be counted with the tiles' loads
+  FLAREPP_WAIT_VM(0);
 
-  const __bf16* Kh = a.K + bh * (int64_t)a.N * D;
-  const __bf16* Vh = a.V + bh * (int64_t)a.N * D;
-  // the next step's K and V are loaded while this one computes
-  kop_t kn[2], vn[2];
-  auto load_kv = [&](int64_t tb) {
+  const __bf16* const src[2] = {a.K + bh * (int64_t)a.N * D, a.V + bh * (int64_t)a.N * D};
+  const int ko = slot_off<D>(l16, KL * g);
+  int to[DB];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      kn[hh] = tok_operand<D>(Kh, tb + 16 * hh, n1, l16, g);
-      vn[hh] = tok_operand<D>(Vh, tb + 16 * hh, n1, l16, g);
-    }
-  };
-  if (n0 < n1) load_kv(n0);
-  int buf = 0;
-  for (int64_t tb = n0; tb < n1; tb += 32, buf ^= 1) {
-    kop_t ka[2], va[2];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      ka[hh] = kn[hh];
-      va[hh] = vn[hh];
-    }
-    if (tb + 32 < n1) load_kv(tb + 32);
-    if (w == 0) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int e = 0; e < KL; ++e) sKt[buf][(KL * g + e) * kBwdTT + 16 * hh + l16] = ka[hh][e];
-    }
-    __syncthreads();
-    bf16x8 kt[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) kt[db] = tr_operand(&sKt[buf][(16 * db + l16) * kBwdTT], 0, g);
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      if (!tv[t]) continue;
-      f32x4 dl[2];
+  for (int db = 0; db < DB; ++db) to[db] = slot_off<D>(4 * g + (l16 >> 2), 16 * db + 4 * (l16 & 3));
+
+  const int64_t ntiles = n1 > n0 ? (n1 - n0 + T::TT - 1) / T::TT : 0;
+  if (ntiles > 0) {
+    lat_tile_dma<D, 2, false>(ring, src, nullptr, nullptr, n0, n1, w, lane);
+    lat_tile_dma<D, 2, false>(ring + T::SLOT, src, nullptr, nullptr, n0 + T::TT, n1, w, lane);
+  }
+  int cur = 0;
+  for (int64_t u = 0; u < ntiles; ++u) {
+    lat_tile_open<D, 2, false>(w);
+    const int nxt = cur == 0 ? 2 : cur - 1;
+    lat_tile_dma<D, 2, false>(ring + nxt * T::SLOT, src, nullptr, nullptr, n0 + (u + 2) * T::TT, n1, w, lane);
+    const __bf16* sK = ring + cur * T::SLOT;
+    const __bf16* sV = sK + T::OPE;
+    const int64_t tb0 = n0 + u * T::TT;
+    const int nsteps = (int)min<int64_t>(T::STEPS, (n1 - tb0 + 31) / 32);
+#pragma unroll 1
+    for (int st = 0; st < nsteps; ++st) {
+      const int64_t tb = tb0 + 32 * st;
+      const int so = 32 * st * D;
+      kop_t ka[2], va[2];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        f32x4 L = KOperand<D>::mma(ka[hh], qh[t], splat4(na[t]));
-        L = KOperand<D>::mma(ka[hh], ql[t], L);
-        f32x4 dp = KOperand<D>::mma(va[hh], dov[t], splat4(nd[t]));
-        dp = KOperand<D>::mma(va[hh], dol[t], dp);
-        if (tb + 32 <= n1) {
+        ka[hh] = *reinterpret_cast<const kop_t*>(sK + so + 16 * hh * D + ko);
+        va[hh] = *reinterpret_cast<const kop_t*>(sV + so + 16 * hh * D + ko);
+      }
+      bf16x8 kt[DB];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) dl[hh][r] = fast_exp2(L[r]) * dp[r];
-        } else {  // the split's last, partial step
+      for (int db = 0; db < DB; ++db) kt[db] = tr_at<D>(sK + so + to[db]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const bool live = tb + 16 * hh + 4 * g + r < n1;
-            dl[hh][r] = live ? fast_exp2(L[r]) * dp[r] : 0.0f;
+      for (int t = 0; t < 2; ++t) {
+        if (!tv[t]) continue;
+        f32x4 dl[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          f32x4 L = KOperand<D>::mma(ka[hh], qh[t], splat4(na[t]));
+          L = KOperand<D>::mma(ka[hh], ql[t], L);
+          f32x4 dp = KOperand<D>::mma(va[hh], dov[t], splat4(nd[t]));
+          dp = KOperand<D>::mma(va[hh], dol[t], dp);
+          if (tb + 32 <= n1) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dl[hh][r] = fast_exp2(L[r]) * dp[r];
+          } else {  // the split's last, partial step
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const bool live = tb + 16 * hh + 4 * g + r < n1;
+              dl[hh][r] = live ? fast_exp2(L[r]) * dp[r] : 0.0f;
+            }
           }
         }
-      }
-      const bf16x8 lb = pack_tiles(dl[0], dl[1]);
+        const bf16x8 lb = pack_tiles(dl[0], dl[1]);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) dqt[t][db] = mfma_k32(kt[db], lb, dqt[t][db]);
+        for (int db = 0; db < DB; ++db) dqt[t][db] = mfma_k32(kt[db], lb, dqt[t][db]);
+      }
     }
+    cur = cur == 2 ? 0 : cur + 1;
   }
+  // the trailing tiles' loads must land before the workgroup's LDS is released
+  FLAREPP_WAIT_VM(0);
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int m = 16 * (2 * w + t) + l16;
@@ -691,15 +761,17 @@ __global__ __launch_bounds__(512) void bwd_dec_tok_bf16(BwdDecArgs a) {
 // dQd_m = s sum_n dL_nm K_n, with P_nm = 2^(L - A_n) from the token pass's
 // A_n and dL = P (<dY_n, Z'_m> - <dY_n, Y'_n>).  Per 32-token step: L^T =
 // K (c Qd)^T, dP'^T = dY Z'^T (rows tokens, cols latents); dZ^T += dY^T P^T
-// and dQd^T += K^T dL^T from transposed LDS copies of the step's K and dY.
+// and dQd^T += K^T dL^T; K, dY (hi, lo) and the statistics come from the LDS
+// tiles, K^T and dY^T through transposing reads.
 template <int D>
 __global__ __launch_bounds__(512) void bwd_dec_lat_bf16(BwdDecArgs a) {
   constexpr int KL = KOperand<D>::kLen;
   constexpr int DB = D / 16;
   typedef typename KOperand<D>::T kop_t;
-  __shared__ __attribute__((aligned(16))) __bf16 sKt[2][D * kBwdTT];
-  __shared__ __attribute__((aligned(16))) __bf16 sGt[2][D * kBwdTT];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  typedef LatTiles<D, 3, true> T;
+  __shared__ __attribute__((aligned(16))) __bf16 ring[3 * T::SLOT];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const int j = blockIdx.x;
   const int64_t lbh = blockIdx.y, bh = a.bh0 + lbh;
@@ -725,94 +797,96 @@ __global__ __launch_bounds__(512) void bwd_dec_lat_bf16(BwdDecArgs a) {
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int db = 0; db < DB; ++db) dzt[t][db] = dqt[t][db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // the latent operands must not be counted with the tiles' loads
+  FLAREPP_WAIT_VM(0);
 
-  const __bf16* Kh = a.K + bh * (int64_t)a.N * D;
-  const __bf16* Gh = a.dyh + lbh * (int64_t)a.N * D;
-  const __bf16* Gl = a.dyl + lbh * (int64_t)a.N * D;
-  // per-token statistics of the head: rows of a.tstride floats (a multiple
-  // of 4, so a lane's four tokens are one aligned 16-byte load)
-  const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(a.tA + lbh * a.tstride, (uint32_t)(a.tstride * 4));
-  const __amdgpu_buffer_rsrc_t rD = buffer_rsrc(a.tD + lbh * a.tstride, (uint32_t)(a.tstride * 4));
-  // the next step's K, dY and statistics are loaded while this one computes
-  kop_t kn[2], hn[2], ln[2];
-  f32x4 an[2], dn[2];
-  auto load_step = [&](int64_t tb) {
+  const __bf16* const src[3] = {a.K + bh * (int64_t)a.N * D, a.dyh + lbh * (int64_t)a.N * D,
+                                a.dyl + lbh * (int64_t)a.N * D};
+  const float* tA = a.tA + lbh * a.tstride;
+  const float* tD = a.tD + lbh * a.tstride;
+  const int ko = slot_off<D>(l16, KL * g);
+  int to[DB];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      kn[hh] = tok_operand<D>(Kh, tb + 16 * hh, n1, l16, g);
-      hn[hh] = tok_operand<D>(Gh, tb + 16 * hh, n1, l16, g);
-      ln[hh] = tok_operand<D>(Gl, tb + 16 * hh, n1, l16, g);
-      an[hh] = buffer_load<f32x4>(rA, (int)(tb + 16 * hh + 4 * g) * 4);
-      dn[hh] = buffer_load<f32x4>(rD, (int)(tb + 16 * hh + 4 * g) * 4);
-    }
-  };
-  if (n0 < n1) load_step(n0);
-  int buf = 0;
-  for (int64_t tb = n0; tb < n1; tb += 32, buf ^= 1) {
-    kop_t ka[2], ga[2], gl[2];
-    f32x4 na[2], nd[2];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      ka[hh] = kn[hh];
-      ga[hh] = hn[hh];
-      gl[hh] = ln[hh];
-      if (tb + 32 <= n1) {
-        na[hh] = -an[hh];
-        nd[hh] = -dn[hh];
-      } else {  // the split's last, partial step
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool live = tb + 16 * hh + 4 * g + r < n1;
-          na[hh][r] = live ? -an[hh][r] : -INFINITY;
-          nd[hh][r] = live ? -dn[hh][r] : 0.0f;
-        }
-      }
-    }
-    if (tb + 32 < n1) load_step(tb + 32);
-    if (w == 0) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int e = 0; e < KL; ++e) sKt[buf][(KL * g + e) * kBwdTT + 16 * hh + l16] = ka[hh][e];
-    } else if (w == 1) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int e = 0; e < KL; ++e) sGt[buf][(KL * g + e) * kBwdTT + 16 * hh + l16] = ga[hh][e];
-    }
-    __syncthreads();
-    bf16x8 kt[DB], gt[DB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      kt[db] = tr_operand(&sKt[buf][(16 * db + l16) * kBwdTT], 0, g);
-      gt[db] = tr_operand(&sGt[buf][(16 * db + l16) * kBwdTT], 0, g);
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      if (!tv[t]) continue;
-      f32x4 P[2], dl[2];
+  for (int db = 0; db < DB; ++db) to[db] = slot_off<D>(4 * g + (l16 >> 2), 16 * db + 4 * (l16 & 3));
+
+  const int64_t ntiles = n1 > n0 ? (n1 - n0 + T::TT - 1) / T::TT : 0;
+  if (ntiles > 0) {
+    lat_tile_dma<D, 3, true>(ring, src, tA, tD, n0, n1, w, lane);
+    lat_tile_dma<D, 3, true>(ring + T::SLOT, src, tA, tD, n0 + T::TT, n1, w, lane);
+  }
+  int cur = 0;
+  for (int64_t u = 0; u < ntiles; ++u) {
+    lat_tile_open<D, 3, true>(w);
+    const int nxt = cur == 0 ? 2 : cur - 1;
+    lat_tile_dma<D, 3, true>(ring + nxt * T::SLOT, src, tA, tD, n0 + (u + 2) * T::TT, n1, w, lane);
+    const __bf16* sK = ring + cur * T::SLOT;
+    const __bf16* sGh = sK + T::OPE;
+    const __bf16* sGl = sK + 2 * T::OPE;
+    const float* sA = reinterpret_cast<const float*>(sK + 3 * T::OPE);
+    const float* sD = sA + T::TT;
+    const int64_t tb0 = n0 + u * T::TT;
+    const int nsteps = (int)min<int64_t>(T::STEPS, (n1 - tb0 + 31) / 32);
+#pragma unroll 1
+    for (int st = 0; st < nsteps; ++st) {
+      const int64_t tb = tb0 + 32 * st;
+      const int so = 32 * st * D;
+      kop_t ka[2], ga[2], gl[2];
+      f32x4 na[2], nd[2];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        f32x4 L = KOperand<D>::mma(ka[hh], qh[t], na[hh]);
-        L = KOperand<D>::mma(ka[hh], ql[t], L);
-        f32x4 dp = KOperand<D>::mma(ga[hh], zh[t], nd[hh]);
-        dp = KOperand<D>::mma(ga[hh], zl[t], dp);
-        dp = KOperand<D>::mma(gl[hh], zh[t], dp);
+        ka[hh] = *reinterpret_cast<const kop_t*>(sK + so + 16 * hh * D + ko);
+        ga[hh] = *reinterpret_cast<const kop_t*>(sGh + so + 16 * hh * D + ko);
+        gl[hh] = *reinterpret_cast<const kop_t*>(sGl + so + 16 * hh * D + ko);
+        const f32x4 av = *reinterpret_cast<const f32x4*>(sA + 32 * st + 16 * hh + 4 * g);
+        const f32x4 dv = *reinterpret_cast<const f32x4*>(sD + 32 * st + 16 * hh + 4 * g);
+        if (tb + 32 <= n1) {
+          na[hh] = -av;
+          nd[hh] = -dv;
+        } else {  // the split's last, partial step
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          P[hh][r] = fast_exp2(L[r]);  // 2^-inf = 0 past the split
-          dl[hh][r] = P[hh][r] * dp[r];
+          for (int r = 0; r < 4; ++r) {
+            const bool live = tb + 16 * hh + 4 * g + r < n1;
+            na[hh][r] = live ? -av[r] : -INFINITY;
+            nd[hh][r] = live ? -dv[r] : 0.0f;
+          }
         }
       }
-      const bf16x8 pb = pack_tiles(P[0], P[1]);
-      const bf16x8 lb = pack_tiles(dl[0], dl[1]);
+      bf16x8 kt[DB], gt[DB];
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        dzt[t][db] = mfma_k32(gt[db], pb, dzt[t][db]);
-        dqt[t][db] = mfma_k32(kt[db], lb, dqt[t][db]);
+        kt[db] = tr_at<D>(sK + so + to[db]);
+        gt[db] = tr_at<D>(sGh + so + to[db]);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        if (!tv[t]) continue;
+        f32x4 P[2], dl[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          f32x4 L = KOperand<D>::mma(ka[hh], qh[t], na[hh]);
+          L = KOperand<D>::mma(ka[hh], ql[t], L);
+          f32x4 dp = KOperand<D>::mma(ga[hh], zh[t], nd[hh]);
+          dp = KOperand<D>::mma(ga[hh], zl[t], dp);
+          dp = KOperand<D>::mma(gl[hh], zh[t], dp);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            P[hh][r] = fast_exp2(L[r]);  // 2^-inf = 0 past the split
+            dl[hh][r] = P[hh][r] * dp[r];
+          }
+        }
+        const bf16x8 pb = pack_tiles(P[0], P[1]);
+        const bf16x8 lb = pack_tiles(dl[0], dl[1]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          dzt[t][db] = mfma_k32(gt[db], pb, dzt[t][db]);
+          dqt[t][db] = mfma_k32(kt[db], lb, dqt[t][db]);
+        }
       }
     }
+    cur = cur == 2 ? 0 : cur + 1;
   }
+  // the trailing tiles' loads must land before the workgroup's LDS is released
+  FLAREPP_WAIT_VM(0);
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int m = 16 * (2 * w + t) + l16;
