@@ -64,16 +64,26 @@ struct BwdPrepArgs {
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_bf16(BwdPrepArgs a) {
   __shared__ float smean[D];
+  __shared__ float spart[256 / D][D];
   const int k = blockIdx.x, tid = threadIdx.x;
   auto load = [&](int m, int d) -> float {
     const int64_t i = (int64_t)k * a.src_blk + (int64_t)m * D + d;
     return a.src_bf16 ? (float)static_cast<const __bf16*>(a.src)[i] : static_cast<const float*>(a.src)[i];
   };
   if (a.center) {
+    // column sums: 256 / D threads per column take every (256 / D)-th row,
+    // then one thread per column adds their sums in order
+    constexpr int P = 256 / D;
+    const int d = tid % D, q = tid / D;
+    float s = 0.0f;
+    for (int m = q; m < a.M; m += P) s += load(m, d);
+    spart[q][d] = s;
+    __syncthreads();
     if (tid < D) {
-      float s = 0.0f;
-      for (int m = 0; m < a.M; ++m) s += load(m, tid);
-      smean[tid] = s / (float)a.M;
+      float t = 0.0f;
+#pragma unroll
+      for (int i = 0; i < P; ++i) t += spart[i][tid];
+      smean[tid] = t / (float)a.M;
     }
     __syncthreads();
   }
@@ -183,6 +193,31 @@ __global__ __launch_bounds__(256) void bwd_dy_split(BwdDySplitArgs a) {
   *reinterpret_cast<bf16x4*>(a.lo + i) = bf16x4{l0[0], l0[1], l1[0], l1[1]};
 }
 
+// dS of the seed blocks from per-head totals src ([G][M][D], the launch's
+// heads): out[blk] += sum of src over the heads that use seed block blk
+// (every head when the seeds are shared), in head order.
+struct BwdSeedSumArgs {
+  const float* src;
+  float* out;  // [seed_blocks][M][D]
+  int M, G, H, seed_blocks;
+  int64_t bh0;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_seed_sum(BwdSeedSumArgs a) {
+  const int64_t per = (int64_t)a.M * D;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= a.seed_blocks * per) return;
+  const int blk = (int)(i / per);
+  const int64_t e = i - blk * per;
+  float acc = 0.0f;
+  for (int lbh = 0; lbh < a.G; ++lbh) {
+    if (a.seed_blocks > 1 && (int)((a.bh0 + lbh) % a.H) != blk) continue;
+    acc += a.src[lbh * per + e];
+  }
+  a.out[i] += acc;
+}
+
 // ---- encode-stage token pass, both encode stages at once: dV_n and dK_n
 // of the workgroup's tokens (dK added to the decode's part).  Wave w takes
 // 32-token blocks tb = n0 + 32 w + 256 i; per stage and 32-latent block kb:
@@ -221,7 +256,8 @@ __global__ __launch_bounds__(512) void bwd_enc_tok_bf16(BwdEncTokArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 sDol[2][kBwdBf16MaxM * D];
   __shared__ __attribute__((aligned(16))) float sNA[2][kBwdBf16MaxM];
   __shared__ __attribute__((aligned(16))) float sND[2][kBwdBf16MaxM];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l16 = lane & 15, g = lane >> 4;
   const int64_t lbh = blockIdx.y, bh = a.bh0 + lbh;
   const int b = (int)(bh / a.H), h = (int)(bh - (int64_t)b * a.H);
@@ -559,7 +595,8 @@ __global__ __launch_bounds__(512) void bwd_dec_tok_bf16(BwdDecArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 sQl[kBwdBf16MaxM * D];
   __shared__ __attribute__((aligned(16))) __bf16 sZh[kBwdBf16MaxM * D];
   __shared__ __attribute__((aligned(16))) __bf16 sZl[kBwdBf16MaxM * D];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l16 = lane & 15, g = lane >> 4;
   const int64_t lbh = blockIdx.y, bh = a.bh0 + lbh;
   const int Mt = a.Mt, nkb = Mt / 32;

@@ -1041,7 +1041,14 @@ flarepp_status run_backward_bf16(const Plan& p, const void* S, const void* K, co
     FLAREPP_TRY(reduce(D, 0, dq3, dq, qf, del1, 0));  // dQd = encode + decode parts, delta_1 = <dQd, Qd>
     FLAREPP_TRY(prep(dq, false, MD, Gc, false, 1.0f, dqr, dql, nullptr));
     FLAREPP_TRY(enc_latent(ops[1], del1));
-    FLAREPP_TRY(reduce(D, 0, nullptr, dS, nullptr, nullptr, p.nS));
+    // dS: each head's split partials summed into dq3 (free again), then
+    // the heads summed per seed block
+    FLAREPP_TRY(reduce(D, 0, nullptr, dq3, nullptr, nullptr, 0));
+    {
+      BwdSeedSumArgs ss{dq3, dS, p.M, Gc, p.H, p.nS, g0};
+      bwd_seed_sum<D><<<(unsigned)cdiv((int64_t)p.nS * MD, 256), 256, 0, st>>>(ss);
+      FLAREPP_TRY(launched());
+    }
     ops[0].delta = del2;
     ops[1].delta = del1;
     BwdEncTokArgs t{};
