@@ -51,3 +51,23 @@ def test_no_packed_fp32_valu(device_asm):
     ins = _instructions(device_asm)
     bad = [l for l in ins if re.match(r"v_pk_(add|mul|fma|mov)_f32", l)]
     assert not bad, bad[:5]
+
+
+def test_no_waterfall_loops(device_asm):
+    """A buffer resource built from a value the compiler cannot prove
+    wave-uniform (a wave index taken as threadIdx.x / 64 without
+    readfirstlane, say) is lowered to a loop that peels one distinct value per
+    iteration around every buffer access (readfirstlane, compare, exec mask,
+    s_cbranch_execnz back).  Such loops cost a dozen instructions per access
+    even when the value is uniform; none may appear in the library."""
+    labels = {l[:-1]: i for i, l in enumerate(device_asm) if re.fullmatch(r"\.LBB\w+:", l)}
+    loops = []
+    for i, l in enumerate(device_asm):
+        m = re.fullmatch(r"s_cbranch_execnz (\.LBB\w+)", l)
+        if not m or m.group(1) not in labels or labels[m.group(1)] >= i:
+            continue
+        body = device_asm[labels[m.group(1)]:i]
+        if any(x.startswith("v_readfirstlane_b32") for x in body) and \
+                any(x.startswith(("buffer_load", "buffer_store")) for x in body):
+            loops.append(m.group(1))
+    assert not loops, f"{len(loops)} waterfall loops, e.g. at {loops[:3]}"
