@@ -173,26 +173,6 @@ __device__ __forceinline__ typename KOperand<D>::T tok_operand(const __bf16* bas
   const __amdgpu_buffer_rsrc_t r = buffer_rsrc(base + n * D, (uint32_t)(cnt * D * 2));
   return buffer_load<typename KOperand<D>::T>(r, (l16 * D + KL * g) * 2);
 }
-// dY of the launch's heads as a bf16 hi/lo pair ([G][N][D] each), once per
-// call, for both decode passes.
-struct BwdDySplitArgs {
-  const float* dY;  // the launch's first head
-  __bf16* hi;
-  __bf16* lo;
-  int64_t n;        // elements, a multiple of 4
-};
-
-__global__ __launch_bounds__(256) void bwd_dy_split(BwdDySplitArgs a) {
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (i >= a.n) return;
-  const f32x4 x = *reinterpret_cast<const f32x4*>(a.dY + i);
-  const bf16x2 h0 = pack_bf16(x[0], x[1]), h1 = pack_bf16(x[2], x[3]);
-  const bf16x2 l0 = pack_bf16(x[0] - (float)h0[0], x[1] - (float)h0[1]);
-  const bf16x2 l1 = pack_bf16(x[2] - (float)h1[0], x[3] - (float)h1[1]);
-  *reinterpret_cast<bf16x4*>(a.hi + i) = bf16x4{h0[0], h0[1], h1[0], h1[1]};
-  *reinterpret_cast<bf16x4*>(a.lo + i) = bf16x4{l0[0], l0[1], l1[0], l1[1]};
-}
-
 // dS of the seed blocks from per-head totals src ([G][M][D], the launch's
 // heads): out[blk] += sum of src over the heads that use seed block blk
 // (every head when the seeds are shared), in head order.
@@ -369,33 +349,41 @@ __global__ __launch_bounds__(512) void bwd_enc_tok_bf16(BwdEncTokArgs a) {
 // ---- token tiles of the latent passes.  A workgroup streams its split's
 // tokens through LDS in tiles of TT = 4096 / D tokens: NOP bf16 operands of
 // 8 KB each ([TT][D] rows with the encode tile's chunk swizzle, so the row
-// operand and the transposing read are both free of bank conflicts) and,
-// with STATS, two float rows of TT (the decode's per-token A_n and
+// operand and the transposing read are both free of bank conflicts); NF
+// float32 operands, staged row-major and split by the waves into a bf16 hi
+// and a bf16 lo tile of the same swizzled layout (x = hi + lo to 16 bits);
+// and, with STATS, two float rows of TT (the decode's per-token A_n and
 // <dY_n, Y'_n>).  Three slots: the barrier that opens tile u is taken after
 // every wave has finished tile u - 1, and right after it the loads of tile
 // u + 2 go into the slot tile u - 1 held, so two tiles are in flight while
 // one is read.  The loads go straight to LDS (dma16), each wave waits for its
-// own before the barrier, and no register carries a token operand from one
-// step to the next.  Tiles past the split re-read its last token (the
-// masks give those zero weight), so every wave issues the same loads per
-// tile and the wait counts are constants.
-template <int D, int NOP, bool STATS>
+// own (and splits its own float32 chunks) before the barrier, and no register
+// carries a token operand from one step to the next.  Tiles past the split
+// re-read its last token (the masks give those zero weight), so every wave
+// issues the same loads per tile and the wait counts are constants.
+template <int D, int NOP, int NF, bool STATS>
 struct LatTiles {
   static constexpr int TT = 4096 / D;               // tokens per tile
   static constexpr int OPE = TT * D;                // bf16 per operand tile (8 KB)
-  static constexpr int SLOT = NOP * OPE + (STATS ? 4 * TT : 0);
+  static constexpr int HL = NOP * OPE;              // hi, lo tiles of float operand f at HL + 2 f OPE (+ OPE)
+  static constexpr int F32 = HL + 2 * NF * OPE;     // float32 staging of operand f at F32 + 2 f OPE
+  static constexpr int ST = F32 + 2 * NF * OPE;     // statistics rows
+  static constexpr int SLOT = ST + (STATS ? 4 * TT : 0);
   static constexpr int NSI = STATS ? TT / 128 : 0;  // 1 KB loads of the statistics
   static constexpr int STEPS = TT / 32;
+  static constexpr int NLOAD = NOP + 2 * NF;        // loads per wave and tile (plus the statistics)
 };
 
 // Issue wave `wave`'s loads of the tile at token tb into slot `sl`: chunk
-// 64 wave + lane of every operand (lane l of a load fills LDS chunk
-// base + 16 l, so it fetches the (token, chunk) the swizzle places there);
+// 64 wave + lane of every bf16 operand (lane l of a load fills LDS chunk
+// base + 16 l, so it fetches the (token, chunk) the swizzle places there),
+// chunks 128 wave .. 128 wave + 127 of every float32 operand (row-major);
 // waves below NSI also load 1 KB of the [A | D] statistics rows.
-template <int D, int NOP, bool STATS>
-__device__ __forceinline__ void lat_tile_dma(__bf16* sl, const __bf16* const (&src)[NOP], const float* tA,
-                                             const float* tD, int64_t tb, int64_t n1, int wave, int lane) {
-  typedef LatTiles<D, NOP, STATS> T;
+template <int D, int NOP, int NF, bool STATS>
+__device__ __forceinline__ void lat_tile_dma(__bf16* sl, const __bf16* const* src, const float* const* srcf,
+                                             const float* tA, const float* tD, int64_t tb, int64_t n1, int wave,
+                                             int lane) {
+  typedef LatTiles<D, NOP, NF, STATS> T;
   constexpr int U = D / 8;
   const int c = wave * 64 + lane;
   const int t = c / U;
@@ -403,24 +391,49 @@ __device__ __forceinline__ void lat_tile_dma(__bf16* sl, const __bf16* const (&s
   const int64_t row = min(tb + t, n1 - 1);
 #pragma unroll
   for (int o = 0; o < NOP; ++o) dma16(src[o] + row * D + 8 * u, sl + o * T::OPE + wave * 512);
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int cf = wave * 128 + i * 64 + lane;
+      const int64_t rf = min(tb + cf / (D / 4), n1 - 1);
+      dma16(reinterpret_cast<const __bf16*>(srcf[f] + rf * D + 4 * (cf % (D / 4))),
+            sl + T::F32 + 2 * f * T::OPE + (wave * 128 + i * 64) * 8);
+    }
+  }
   if (STATS && wave < T::NSI) {
     const bool isA = 4 * c < T::TT;
     const int64_t tok = min(tb + (isA ? 4 * c : 4 * c - T::TT), (n1 - 1) & ~int64_t(3));
-    dma16(reinterpret_cast<const __bf16*>((isA ? tA : tD) + tok), sl + NOP * T::OPE + wave * 512);
+    dma16(reinterpret_cast<const __bf16*>((isA ? tA : tD) + tok), sl + T::ST + wave * 512);
   }
 }
 
-// Wait until this wave's loads of the oldest tile in flight have landed
-// (those of the next tile may still be in flight), then open it to the
-// workgroup.  The lgkm wait makes this wave's reads of the previous tile
-// complete before any wave refills that slot.
-template <int D, int NOP, bool STATS>
-__device__ __forceinline__ void lat_tile_open(int wave) {
-  typedef LatTiles<D, NOP, STATS> T;
+// Wait until this wave's loads of the oldest tile in flight (slot `sl`) have
+// landed (those of the next tile may still be in flight), split its float32
+// chunks into the hi/lo tiles, then open the tile to the workgroup.  The lgkm
+// wait makes this wave's LDS writes land, and its reads of the previous tile
+// complete, before the barrier.
+template <int D, int NOP, int NF, bool STATS>
+__device__ __forceinline__ void lat_tile_open(__bf16* sl, int wave, int lane) {
+  typedef LatTiles<D, NOP, NF, STATS> T;
   if (STATS && wave < T::NSI)
-    FLAREPP_WAIT_VM(NOP + 1);
+    FLAREPP_WAIT_VM(T::NLOAD + 1);
   else
-    FLAREPP_WAIT_VM(NOP);
+    FLAREPP_WAIT_VM(T::NLOAD);
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int cf = wave * 128 + i * 64 + lane;
+      const f32x4 x = *reinterpret_cast<const f32x4*>(sl + T::F32 + 2 * f * T::OPE + cf * 8);
+      const bf16x2 h0 = pack_bf16(x[0], x[1]), h1 = pack_bf16(x[2], x[3]);
+      const bf16x2 l0 = pack_bf16(x[0] - (float)h0[0], x[1] - (float)h0[1]);
+      const bf16x2 l1 = pack_bf16(x[2] - (float)h1[0], x[3] - (float)h1[1]);
+      const int o = slot_off<D>(cf / (D / 4), 4 * (cf % (D / 4)));
+      *reinterpret_cast<bf16x4*>(sl + T::HL + 2 * f * T::OPE + o) = bf16x4{h0[0], h0[1], h1[0], h1[1]};
+      *reinterpret_cast<bf16x4*>(sl + T::HL + 2 * f * T::OPE + T::OPE + o) = bf16x4{l0[0], l0[1], l1[0], l1[1]};
+    }
+  }
   __builtin_amdgcn_s_waitcnt(kEncWaitLgkm0);
   ring_barrier();
 }
@@ -445,7 +458,7 @@ __global__ __launch_bounds__(512) void bwd_enc_lat_bf16(BwdEncArgs a) {
   constexpr int KL = KOperand<D>::kLen;
   constexpr int DB = D / 16;
   typedef typename KOperand<D>::T kop_t;
-  typedef LatTiles<D, 2, false> T;
+  typedef LatTiles<D, 2, 0, false> T;
   __shared__ __attribute__((aligned(16))) __bf16 ring[3 * T::SLOT];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -490,14 +503,15 @@ __global__ __launch_bounds__(512) void bwd_enc_lat_bf16(BwdEncArgs a) {
 
   const int64_t ntiles = n1 > n0 ? (n1 - n0 + T::TT - 1) / T::TT : 0;
   if (ntiles > 0) {
-    lat_tile_dma<D, 2, false>(ring, src, nullptr, nullptr, n0, n1, w, lane);
-    lat_tile_dma<D, 2, false>(ring + T::SLOT, src, nullptr, nullptr, n0 + T::TT, n1, w, lane);
+    lat_tile_dma<D, 2, 0, false>(ring, src, nullptr, nullptr, nullptr, n0, n1, w, lane);
+    lat_tile_dma<D, 2, 0, false>(ring + T::SLOT, src, nullptr, nullptr, nullptr, n0 + T::TT, n1, w, lane);
   }
   int cur = 0;
   for (int64_t u = 0; u < ntiles; ++u) {
-    lat_tile_open<D, 2, false>(w);
+    lat_tile_open<D, 2, 0, false>(ring + cur * T::SLOT, w, lane);
     const int nxt = cur == 0 ? 2 : cur - 1;
-    lat_tile_dma<D, 2, false>(ring + nxt * T::SLOT, src, nullptr, nullptr, n0 + (u + 2) * T::TT, n1, w, lane);
+    lat_tile_dma<D, 2, 0, false>(ring + nxt * T::SLOT, src, nullptr, nullptr, nullptr, n0 + (u + 2) * T::TT, n1, w,
+                                 lane);
     const __bf16* sK = ring + cur * T::SLOT;
     const __bf16* sV = sK + T::OPE;
     const int64_t tb0 = n0 + u * T::TT;
@@ -563,8 +577,7 @@ struct BwdDecArgs {
   const __bf16* zh;   // [G][Mp][D] Z' as bf16 hi/lo
   const __bf16* zl;
   const __bf16* K;    // B x H x N x D
-  const __bf16* dyh;  // [G][N][D] dY as bf16 hi
-  const __bf16* dyl;  // [G][N][D] bf16 lo
+  const float* dY;    // [G][N][D] the upstream gradient of the launch's heads
   const float* qnorm; // [G][Mp] ||Qd_m||
   float c;            // s log2 e
   float* dK;          // token pass: written
@@ -617,28 +630,25 @@ __global__ __launch_bounds__(512) void bwd_dec_tok_bf16(BwdDecArgs a) {
 
   const int64_t n0 = (int64_t)blockIdx.x * a.tchunk, n1 = min((int64_t)a.N, n0 + a.tchunk);
   const __bf16* Kh = a.K + bh * (int64_t)a.N * D;
-  const __bf16* Gh = a.dyh + lbh * (int64_t)a.N * D;
-  const __bf16* Gl = a.dyl + lbh * (int64_t)a.N * D;
+  const float* Gf = a.dY + lbh * (int64_t)a.N * D;
   // K and dY of the next 32-token block are loaded while this one computes;
-  // dY both as the lane's operand slots and as the C-tile elements 16 db + 4 g ..
-  kop_t kn[2], hn[2], ln[2];
-  bf16x4 yhn[2][DB], yln[2][DB];
+  // dY (float32) both as the elements of the lane's operand slots (KL g ..)
+  // and as the C-tile elements 16 db + 4 g .. (the same ones when D = 16)
+  constexpr int KQ = KL / 4;
+  kop_t kn[2];
+  f32x4 yn[2][KQ], gyn[2][DB];
   auto load_blk = [&](int64_t tb) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int64_t n = tb + 16 * u;
       kn[u] = tok_operand<D>(Kh, n, n1, l16, g);
-      hn[u] = tok_operand<D>(Gh, n, n1, l16, g);
-      ln[u] = tok_operand<D>(Gl, n, n1, l16, g);
-      if constexpr (D == 32) {
-        const int64_t cnt = n1 > n ? n1 - n : 0;
-        const __amdgpu_buffer_rsrc_t rh = buffer_rsrc(Gh + n * D, (uint32_t)(cnt * D * 2));
-        const __amdgpu_buffer_rsrc_t rl = buffer_rsrc(Gl + n * D, (uint32_t)(cnt * D * 2));
+      const int64_t cnt = n1 > n ? n1 - n : 0;
+      const __amdgpu_buffer_rsrc_t r = buffer_rsrc(Gf + n * D, (uint32_t)(cnt * D * 4));
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          yhn[u][db] = buffer_load<bf16x4>(rh, (l16 * D + 16 * db + 4 * g) * 2);
-          yln[u][db] = buffer_load<bf16x4>(rl, (l16 * D + 16 * db + 4 * g) * 2);
-        }
+      for (int q = 0; q < KQ; ++q) yn[u][q] = buffer_load<f32x4>(r, (l16 * D + KL * g + 4 * q) * 4);
+      if constexpr (D == 32) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) gyn[u][db] = buffer_load<f32x4>(r, (l16 * D + 16 * db + 4 * g) * 4);
       }
     }
   };
@@ -650,20 +660,20 @@ __global__ __launch_bounds__(512) void bwd_dec_tok_bf16(BwdDecArgs a) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       kb_op[u] = kn[u];
-      gb_op[u] = hn[u];
-      gl_op[u] = ln[u];
+      // dY as a bf16 hi/lo operand pair (x = hi + lo to 16 bits)
+#pragma unroll
+      for (int e = 0; e < KL; ++e) {
+        const float x = yn[u][e / 4][e % 4];
+        const __bf16 hi = (__bf16)x;
+        gb_op[u][e] = hi;
+        gl_op[u][e] = (__bf16)(x - (float)hi);
+      }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        bf16x4 yh, yl;
-        if constexpr (D == 32) {
-          yh = yhn[u][db];
-          yl = yln[u][db];
-        } else {
-          yh = hn[u];
-          yl = ln[u];
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) gy[u][db][r] = (float)yh[r] + (float)yl[r];
+        if constexpr (D == 32)
+          gy[u][db] = gyn[u][db];
+        else
+          gy[u][db] = yn[u][0];
       }
       float k2 = 0.0f;
 #pragma unroll
@@ -798,14 +808,14 @@ __global__ __launch_bounds__(512) void bwd_dec_tok_bf16(BwdDecArgs a) {
 // dQd_m = s sum_n dL_nm K_n, with P_nm = 2^(L - A_n) from the token pass's
 // A_n and dL = P (<dY_n, Z'_m> - <dY_n, Y'_n>).  Per 32-token step: L^T =
 // K (c Qd)^T, dP'^T = dY Z'^T (rows tokens, cols latents); dZ^T += dY^T P^T
-// and dQd^T += K^T dL^T; K, dY (hi, lo) and the statistics come from the LDS
-// tiles, K^T and dY^T through transposing reads.
+// and dQd^T += K^T dL^T; K, dY (split into hi and lo in LDS) and the
+// statistics come from the LDS tiles, K^T and dY^T through transposing reads.
 template <int D>
 __global__ __launch_bounds__(512) void bwd_dec_lat_bf16(BwdDecArgs a) {
   constexpr int KL = KOperand<D>::kLen;
   constexpr int DB = D / 16;
   typedef typename KOperand<D>::T kop_t;
-  typedef LatTiles<D, 3, true> T;
+  typedef LatTiles<D, 1, 1, true> T;
   __shared__ __attribute__((aligned(16))) __bf16 ring[3 * T::SLOT];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -837,8 +847,8 @@ __global__ __launch_bounds__(512) void bwd_dec_lat_bf16(BwdDecArgs a) {
   // the latent operands must not be counted with the tiles' loads
   FLAREPP_WAIT_VM(0);
 
-  const __bf16* const src[3] = {a.K + bh * (int64_t)a.N * D, a.dyh + lbh * (int64_t)a.N * D,
-                                a.dyl + lbh * (int64_t)a.N * D};
+  const __bf16* const src[1] = {a.K + bh * (int64_t)a.N * D};
+  const float* const srcf[1] = {a.dY + lbh * (int64_t)a.N * D};
   const float* tA = a.tA + lbh * a.tstride;
   const float* tD = a.tD + lbh * a.tstride;
   const int ko = slot_off<D>(l16, KL * g);
@@ -848,18 +858,18 @@ __global__ __launch_bounds__(512) void bwd_dec_lat_bf16(BwdDecArgs a) {
 
   const int64_t ntiles = n1 > n0 ? (n1 - n0 + T::TT - 1) / T::TT : 0;
   if (ntiles > 0) {
-    lat_tile_dma<D, 3, true>(ring, src, tA, tD, n0, n1, w, lane);
-    lat_tile_dma<D, 3, true>(ring + T::SLOT, src, tA, tD, n0 + T::TT, n1, w, lane);
+    lat_tile_dma<D, 1, 1, true>(ring, src, srcf, tA, tD, n0, n1, w, lane);
+    lat_tile_dma<D, 1, 1, true>(ring + T::SLOT, src, srcf, tA, tD, n0 + T::TT, n1, w, lane);
   }
   int cur = 0;
   for (int64_t u = 0; u < ntiles; ++u) {
-    lat_tile_open<D, 3, true>(w);
+    lat_tile_open<D, 1, 1, true>(ring + cur * T::SLOT, w, lane);
     const int nxt = cur == 0 ? 2 : cur - 1;
-    lat_tile_dma<D, 3, true>(ring + nxt * T::SLOT, src, tA, tD, n0 + (u + 2) * T::TT, n1, w, lane);
+    lat_tile_dma<D, 1, 1, true>(ring + nxt * T::SLOT, src, srcf, tA, tD, n0 + (u + 2) * T::TT, n1, w, lane);
     const __bf16* sK = ring + cur * T::SLOT;
-    const __bf16* sGh = sK + T::OPE;
-    const __bf16* sGl = sK + 2 * T::OPE;
-    const float* sA = reinterpret_cast<const float*>(sK + 3 * T::OPE);
+    const __bf16* sGh = sK + T::HL;
+    const __bf16* sGl = sK + T::HL + T::OPE;
+    const float* sA = reinterpret_cast<const float*>(sK + T::ST);
     const float* sD = sA + T::TT;
     const int64_t tb0 = n0 + u * T::TT;
     const int nsteps = (int)min<int64_t>(T::STEPS, (n1 - tb0 + 31) / 32);

@@ -62,7 +62,7 @@ struct Plan {
   // bf16 backward: latent operands as bf16 (rows [G][Mp][D], transposed [.][D][Mt]),
   // Mt = M rounded up to 32, tokens per token-pass workgroup
   int Mt, tchunk;
-  size_t o_zh, o_zl, o_dzr, o_dzl, o_dqr, o_dql, o_dyh, o_dyl, o_del1;
+  size_t o_zh, o_zl, o_dzr, o_dzl, o_dqr, o_dql, o_del1;
   // spectrum: Gram partials [G][Jg][M][M] over Jg token splits of gchunk, and the reduced [G][M][M]
   int Jg, gchunk;
   size_t o_gpart, o_mat;
@@ -182,7 +182,7 @@ Plan make_plan(const flarepp_desc* d, int op, const flarepp_tuning* t = nullptr)
   p.o_shi = p.o_slo = p.o_sqn = p.o_part = p.o_knorm = p.o_qhi = p.o_qlo = p.o_qnorm = p.o_bias =
       p.o_zt = p.o_qf = p.o_zf = none;
   p.o_lse1 = p.o_lse2 = p.o_tlse = p.o_tdel = p.o_dz = p.o_dq3 = p.o_dq = p.o_del = none;
-  p.o_zh = p.o_zl = p.o_dzr = p.o_dzl = p.o_dqr = p.o_dql = p.o_dyh = p.o_dyl = p.o_del1 = none;
+  p.o_zh = p.o_zl = p.o_dzr = p.o_dzl = p.o_dqr = p.o_dql = p.o_del1 = none;
   p.Mt = (int)cdiv(d->M, 32) * 32;
   {
     // token passes of the bf16 backward: one workgroup per CU over the group
@@ -216,8 +216,6 @@ Plan make_plan(const flarepp_desc* d, int op, const flarepp_tuning* t = nullptr)
     p.o_dzl = take(G_ * opnd);
     p.o_dqr = take(G_ * opnd);
     p.o_dql = take(G_ * opnd);
-    p.o_dyh = take(G_ * (size_t)p.N * D * 2);
-    p.o_dyl = take(G_ * (size_t)p.N * D * 2);
   } else if (bwd) {
     p.o_part = take(G_ * p.J * Mp * std::max<size_t>(D + 4, 2 * D) * 4);
     p.o_qf = take(G_ * p.M * D * 4);
@@ -975,8 +973,7 @@ flarepp_status run_backward_bf16(const Plan& p, const void* S, const void* K, co
       d.zh = zh;
       d.zl = zl;
       d.K = static_cast<const __bf16*>(K);
-      d.dyh = at<__bf16>(ws, p.o_dyh);
-      d.dyl = at<__bf16>(ws, p.o_dyl);
+      d.dY = dY + g0 * (int64_t)p.N * D;
       d.qnorm = at<float>(ws, p.o_qnorm);
       d.c = p.c;
       d.dK = dK;
@@ -994,10 +991,6 @@ flarepp_status run_backward_bf16(const Plan& p, const void* S, const void* K, co
       d.bh0 = g0;
       d.s = p.s;
       d.kscale = kscale;
-      BwdDySplitArgs ys{dY + g0 * (int64_t)p.N * D, at<__bf16>(ws, p.o_dyh), at<__bf16>(ws, p.o_dyl),
-                        (int64_t)Gc * p.N * D};
-      bwd_dy_split<<<(unsigned)cdiv(ys.n / 4, 256), 256, 0, st>>>(ys);
-      FLAREPP_TRY(launched());
       bwd_dec_tok_bf16<D><<<tok_grid, 512, 0, st>>>(d);
       FLAREPP_TRY(launched());
       bwd_dec_lat_bf16<D><<<lat_grid, 512, 0, st>>>(d);
