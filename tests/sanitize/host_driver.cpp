@@ -89,6 +89,15 @@ int main() {
   EXPECT(flarepp_route_backward(&good, addr(0), addr(1), addr(2), faddr(3), faddr(1), faddr(5), faddr(7), addr(6),
                                 size_t(1) << 40, nullptr),
          FLAREPP_ALIASING);  // dS inside K
+  size_t recb = 0;
+  EXPECT(flarepp_shard_records_size(&good, 3, &recb), FLAREPP_OK);
+  EXPECT(flarepp_shard_records_size(&good, 0, &recb), FLAREPP_INVALID_ARG);
+  EXPECT(flarepp_encode_shard(&good, 1, addr(0), addr(1), addr(2), faddr(4), 3, 3, addr(6), size_t(1) << 40, nullptr),
+         FLAREPP_INVALID_ARG);  // slot beyond the slots
+  EXPECT(flarepp_encode_shard(&good, 2, faddr(0), addr(1), addr(2), faddr(1), 0, 2, addr(6), size_t(1) << 40,
+                              nullptr),
+         FLAREPP_ALIASING);  // records inside K
+  EXPECT(flarepp_merge_shards(&good, faddr(4), 2, faddr(4), nullptr), FLAREPP_ALIASING);
   flarepp_desc big = {64, 64, 4096, 256, 32, FLAREPP_BF16, 0.2f, 0};
   EXPECT(flarepp_route_noalloc(&big, addr(0), addr(1), addr(2), faddr(3), nullptr, nullptr, nullptr),
          FLAREPP_SCRATCH_LIMIT);
