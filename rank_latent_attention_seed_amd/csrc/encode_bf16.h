@@ -13,19 +13,23 @@
 // Work decomposition.  A workgroup of NW waves (4 or 8) owns one (b, h,
 // split, latent group); each wave owns MBW 16-latent blocks and all share
 // tiles of TN tokens of K and V.  Tiles travel HBM -> LDS by direct-to-LDS
-// loads (no staging registers) through a ring of four slots, with the loads
-// of the two tiles after the one being consumed in flight; the tile loop is
-// unrolled by four so every slot address is static, and waiting for one
-// tile's loads (s_waitcnt vmcnt) leaves the younger tile's loads running.
-// 16-byte chunks
-// of each token row are XOR-swizzled in LDS (the fetching lane picks the
-// chunk that belongs to its slot) so the matrix-core operand reads are free
-// of bank conflicts (chunk_swz).  Per 32-token step a wave computes S^T = K Q^T tiles
+// loads (no staging registers) through a ring of two slots: the loads of the
+// next tile are issued right after the barrier that opens the current one,
+// so one tile is in flight while one is read (a tile is several microseconds
+// of work, far longer than its loads take); the tile loop is unrolled by two
+// so every slot address is static.  16-byte chunks of each token row are
+// XOR-swizzled in LDS (the fetching lane picks the chunk that belongs to its
+// slot) so the matrix-core operand reads are free of bank conflicts
+// (chunk_swz).  Per 32-token step a wave reads the step's K and V operands
+// and, for each of its latent blocks in turn, computes S^T = K Q^T tiles
 // (rows = tokens, cols = latents), turns them into softmax weights in
 // registers, and accumulates O^T += V^T P^T; V's operand comes from the
-// token-major tile through transposing LDS reads (ds_read_b64_tr_b16).  The
-// work of a step is software-pipelined over the wave's latent blocks so the
-// matrix core and the VALU overlap (see EncodePipe).
+// token-major tile through transposing LDS reads (ds_read_b64_tr_b16).
+// There is no software pipeline across blocks: that keeps a wave within 128
+// registers, so two eight-wave workgroups (64 KB of ring each) share a CU
+// and four waves per SIMD hide each other's matrix-core, exponential and
+// LDS latencies (measured 7% faster than a two-wave-per-SIMD kernel that
+// pipelined the blocks within each wave).
 //
 // Softmax arithmetic.  The query operand arrives pre-multiplied by
 // c = s * log2(e) as a bf16 hi/lo pair (two MFMAs per tile, ~16 mantissa
@@ -37,7 +41,7 @@
 //   * online: initialised from the first step's exact column max and raised
 //     only when some value in a step exceeds mu_m + TAU (exp2(TAU) keeps
 //     every weight and sum finite), at which point acc and lambda are
-//     rescaled.  Both give the same softmax up to rounding (softmax is
+//     rescaled and the step's scores recomputed against the new shift.  Both give the same softmax up to rounding (softmax is
 //     invariant to a common shift).
 // lambda_m sums the same rounded weights that enter the PV product (computed
 // on the matrix core as a row of ones times P^T).  The encodes with a running
@@ -108,12 +112,12 @@ struct Pv<true> {
 };
 
 // ---- tile geometry and the LDS ring.  A slot holds one tile of K or V
-// (TE bf16 = TN tokens x D); the ring has four K slots and four V slots in one
+// (TE bf16 = TN tokens x D); the ring has two K slots and two V slots in one
 // kernel-local LDS array, the V slot of a tile right after its K slot, so
 // that every operand read of a step is a lane base plus an offset that fits
-// the instruction's 16-bit immediate.  Eight-wave workgroups (one per CU) use
-// 16 KB slots (128 KB ring); four-wave workgroups use 8 KB slots so two fit
-// per CU.
+// the instruction's 16-bit immediate.  Eight-wave workgroups use 16 KB slots
+// (a 64 KB ring: two workgroups per CU); four-wave workgroups use 8 KB
+// slots.
 template <int D, int NW>
 struct Ring {
   static constexpr int TE = NW == 8 ? 8192 : 4096;  // elements per slot
@@ -121,6 +125,7 @@ struct Ring {
   static constexpr int SPT = TN / 32;               // 32-token steps per tile
   static constexpr int DI = TE / 8 / 64 / NW;       // 1 KB loads per wave, operand and tile
   static constexpr int kDma = 2 * DI;               // loads per wave and tile
+  static constexpr int SLOTS = 2;
   template <int I>
   __device__ __forceinline__ static __bf16* k(__bf16* ring) {
     return ring + 2 * I * TE;
@@ -143,8 +148,8 @@ template <int D>
 __host__ __device__ __forceinline__ constexpr int chunk_swz(int t) {
   return D == 32 ? ((t >> 1) & 3) : ((t >> 3) & 1);
 }
-// The swizzle of row t equals that of rows t + 16 and t + 32 (EncodePipe's
-// operand offsets rely on it).
+// The swizzle of row t equals that of rows t + 16 and t + 32 (the operand
+// offsets of encode_tiles rely on it).
 template <int D>
 constexpr bool swz_step_invariant() {
   for (int t = 0; t < 64; ++t)
@@ -214,8 +219,9 @@ __device__ __forceinline__ void tile_dma(__bf16* ring, const __bf16* Kp, const _
   }
 }
 
-// Per-wave register state of the encode: query operands, the shift entering
-// each S^T tile as its accumulator input, the softmax statistics, and O^T.
+// Per-wave register state of the encode: query operands, the softmax
+// statistics (the shift -mu enters each S^T tile as its accumulator input),
+// and O^T.
 // acc[DB] is the sum lambda: its tile is ONES^T P^T, whose row 0 carries the
 // column sums of the rounded weights (so lambda sums exactly the weights that
 // enter O^T).
@@ -223,31 +229,9 @@ template <int D, int MBW>
 struct EncodeState {
   typedef typename KOperand<D>::T kop_t;
   kop_t qh[MBW], ql[MBW];
-  f32x4 cb[MBW];
   float mu[MBW];
   float qn2[MBW];  // ||c Q_m||^2 of the lane's latent (from the hi + lo operand)
   f32x4 acc[D / 16 + 1][MBW];
-};
-
-// Software pipeline over (step, latent block) pairs.  While block i's softmax
-// runs on the VALU, the matrix core works on the S^T tiles of the next block
-// and on the O^T update of the previous one; those are independent of block
-// i, so the two units overlap within the wave.
-template <int D, bool F16>
-struct EncodePipe {
-  typedef typename KOperand<D>::T kop_t;
-  typedef typename Pv<F16>::T pv_t;
-  // this lane's operand offsets (elements) within a step of a slot: K row c16
-  // at element KL g, and per 16-column block db the V^T read of row
-  // 4 g + c16 / 4 at element 16 db + 4 (c16 % 4).  The rows 16 further on, and
-  // every later step (32 rows on), add constants: the swizzle of a row depends
-  // on bits of its index that neither changes (chunk_swz), so a step's reads
-  // are these bases plus the step's offset plus immediates.
-  int ko, vo[D / 16];
-  kop_t k0, k1;           // K operands of the current step (two 16-token halves)
-  f32x4 s0, s1;           // S^T tiles of the next (step, block)
-  pv_t p;                 // weights of the previous block, whose O^T update is pending
-  pv_t v[D / 16];         // V^T operands of the previous block's step
 };
 
 // K operands (A of S^T = K Q^T: lane holds token row c16, k-chunk g) of step
@@ -297,8 +281,9 @@ __device__ __forceinline__ void load_vop(const __bf16* sV, int ks, const int (&v
 template <int D, int MBW>
 __device__ __forceinline__ void block_logits(const EncodeState<D, MBW>& st, int i, typename KOperand<D>::T k0,
                                              typename KOperand<D>::T k1, f32x4& s0, f32x4& s1) {
-  s0 = KOperand<D>::mma(k0, st.qh[i], st.cb[i]);
-  s1 = KOperand<D>::mma(k1, st.qh[i], st.cb[i]);
+  const f32x4 cb = f32x4{-st.mu[i], -st.mu[i], -st.mu[i], -st.mu[i]};
+  s0 = KOperand<D>::mma(k0, st.qh[i], cb);
+  s1 = KOperand<D>::mma(k1, st.qh[i], cb);
   s0 = KOperand<D>::mma(k0, st.ql[i], s0);
   s1 = KOperand<D>::mma(k1, st.ql[i], s1);
 }
@@ -329,35 +314,25 @@ __device__ __forceinline__ void block_update(EncodeState<D, MBW>& st, int i, con
   st.acc[D / 16][i] = mfma_k32(ones, p, st.acc[D / 16][i]);
 }
 
-// One 32-token step (step ks of the V slot sV).  sKn / ksn locate the next
-// step's K operands (HAS_NEXT).  Operand loads are placed right after the
-// last use of the registers they replace: the next step's K after the last
-// logits of this step's K, this step's V after the previous block's pending
-// update; the pipeline registers are then overwritten in place instead of
-// copied every step.  ONLINE: running max, starting from the exact column
-// max of the split's first step and raised lazily (only when a value exceeds
-// mu + TAU, so weights and sums stay finite); otherwise the shift is a bound.
-// MASK (the split's ragged last step): tokens at or past n1 weigh zero.
-template <int D, int MBW, bool F16, bool ONLINE, bool MASK, bool HAS_NEXT>
-__device__ __forceinline__ void encode_step(EncodeState<D, MBW>& st, EncodePipe<D, F16>& pp, const __bf16* sV,
-                                            int ks, const __bf16* sKn, int ksn, int sb, int n1, int g, int c16,
+// One 32-token step (step ks of the tile in K slot sK and V slot sV): the
+// step's K and V operands, then each latent block of the wave in turn.
+// ONLINE: running max, starting from the exact column max of the split's
+// first step and raised lazily (only when a score exceeds mu + TAU, so
+// weights and sums stay finite); the raise rescales O^T and lambda and
+// recomputes the block's scores against the new shift (cheaper than keeping
+// them live, and rare).  Otherwise the shift is a bound.  MASK (the split's
+// ragged last step): tokens at or past n1 weigh zero.
+template <int D, int MBW, bool F16, bool ONLINE, bool MASK>
+__device__ __forceinline__ void encode_step(EncodeState<D, MBW>& st, const __bf16* sK, const __bf16* sV, int ks,
+                                            int ko, const int (&vo)[D / 16], int sb, int n1, int g,
                                             typename Pv<F16>::T ones) {
   constexpr int DB = D / 16;
   constexpr float TAU = 8.0f;
-  if (HAS_NEXT && MBW == 1) load_kop<D>(sKn, ksn, pp.ko, pp.k0, pp.k1);
-#pragma unroll
-  for (int i = 0; i < MBW; ++i) {
-    f32x4 s0 = pp.s0, s1 = pp.s1;
-    // matrix core: next block's logits, previous block's update
-    if (i + 1 < MBW) {
-      block_logits<D, MBW>(st, i + 1, pp.k0, pp.k1, pp.s0, pp.s1);
-      if (HAS_NEXT && i + 2 == MBW) load_kop<D>(sKn, ksn, pp.ko, pp.k0, pp.k1);
-    } else if (HAS_NEXT) {
-      block_logits<D, MBW>(st, 0, pp.k0, pp.k1, pp.s0, pp.s1);
-    }
-    block_update<D, MBW, F16>(st, i == 0 ? MBW - 1 : i - 1, pp.v, pp.p, ones);
-    if (i == 0) load_vop<D, F16>(sV, ks, pp.vo, pp.v);
-    // VALU: this block's weights
+  typename KOperand<D>::T k0, k1;
+  load_kop<D>(sK, ks, ko, k0, k1);
+  typename Pv<F16>::T v[DB];
+  load_vop<D, F16>(sV, ks, vo, v);
+  auto mask = [&](f32x4& s0, f32x4& s1) {
     if (MASK) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -365,10 +340,12 @@ __device__ __forceinline__ void encode_step(EncodeState<D, MBW>& st, EncodePipe<
         if (sb + 16 + 4 * g + r >= n1) s1[r] = -INFINITY;
       }
     }
-    typename Pv<F16>::T p = weights<F16>(s0, s1);
-    // keep the weights ahead of the (rare) rescale branch, in the same
-    // scheduling region as the matrix-core work above
-    asm volatile("" : "+v"(p));
+  };
+#pragma unroll
+  for (int i = 0; i < MBW; ++i) {
+    f32x4 s0, s1;
+    block_logits<D, MBW>(st, i, k0, k1, s0, s1);
+    mask(s0, s1);
     if (ONLINE) {
       const float lm = fmaxf(max3(s1[2], s1[3], max3(s0[3], s1[0], max3(s0[0], s0[1], s0[2]))), s1[1]);
       if (__builtin_expect(__builtin_amdgcn_ballot_w64(lm > TAU) != 0, 0)) {
@@ -377,17 +354,15 @@ __device__ __forceinline__ void encode_step(EncodeState<D, MBW>& st, EncodePipe<
         const float al = fast_exp2(-d);
 #pragma unroll
         for (int db = 0; db <= DB; ++db) st.acc[db][i] *= al;
-        s0 -= d;
-        s1 -= d;
-        if (MBW == 1) {  // the pending logits are this block's next step
-          pp.s0 -= d;
-          pp.s1 -= d;
-        }
-        st.cb[i] = f32x4{-st.mu[i], -st.mu[i], -st.mu[i], -st.mu[i]};
-        p = weights<F16>(s0, s1);
+        block_logits<D, MBW>(st, i, k0, k1, s0, s1);
+        mask(s0, s1);
       }
     }
-    pp.p = p;
+    const typename Pv<F16>::T p = weights<F16>(s0, s1);
+    block_update<D, MBW, F16>(st, i, v, p, ones);
+    // keep the next block's work from being hoisted into this one's: the
+    // live ranges would no longer fit four waves per SIMD
+    if (ONLINE) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -420,13 +395,12 @@ __device__ __forceinline__ float own_knorm(const __bf16* ring, int wave, int lan
 // s_waitcnt lgkmcnt(0) (vmcnt and expcnt not waited on).
 constexpr uint32_t kEncWaitLgkm0 = 0xF | (0x7 << 4) | (0x3 << 14);
 
-// Ring protocol.  Tile u+2's loads are issued at the barrier that opens tile
-// u; before it a wave waits for its own loads of tile u (those of tile u+1
-// may still be in flight), so every wave's part of tile u has landed once all
-// have arrived.  The barrier opening tile u is taken at the start of the last
-// step of tile u-1, which still reads tile u-1 and (for the next step's K
-// operands) tile u; the slot refilled there, (u+2) & 3, held tile u-2, which
-// every wave has finished reading.
+// Ring protocol (two slots).  Tile u+1's loads are issued right after the
+// barrier that opens tile u; before that barrier a wave waits for its own
+// loads of tile u (the only ones in flight), so every wave's part of tile u
+// has landed once all have arrived.  The barrier opening tile u is taken
+// after the wave's last step of tile u-1, so the slot refilled right after
+// it, (u+1) & 1, held tile u-1, which every wave has finished reading.
 //
 // Work a wave does on its own chunks of tile u (slot I) once they have
 // landed, published by the barrier that opens the tile:
@@ -461,16 +435,13 @@ template <int D, int NW, int I, bool TNORM, bool F16>
 __device__ __forceinline__ float ring_open(__bf16* ring, float* sKm, const __bf16* Kp, const __bf16* Vp, int u,
                                            int n0, int n1, int wave, int lane) {
   typedef Ring<D, NW> R;
-  constexpr int kWait = R::kDma;
-  FLAREPP_WAIT_VM(kWait);
+  FLAREPP_WAIT_VM(0);
   float* slot = sKm + (u & 1) * NW;
   tile_prep<D, NW, I, TNORM, F16>(ring, sKm, u, wave, lane);
-  if (TNORM || F16) {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(kEncWaitLgkm0);  // this wave's writes are in LDS before the barrier
-  }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kEncWaitLgkm0);  // this wave's LDS accesses are done before the barrier
   ring_barrier();
-  tile_dma<D, NW, (I + 2) & 3>(ring, Kp, Vp, n0 + (u + 2) * Ring<D, NW>::TN, n1, wave, lane);
+  tile_dma<D, NW, I ^ 1>(ring, Kp, Vp, n0 + (u + 1) * R::TN, n1, wave, lane);
   float km2 = 0.0f;
   if (TNORM) {
     km2 = slot[0];
@@ -478,42 +449,6 @@ __device__ __forceinline__ float ring_open(__bf16* ring, float* sKm, const __bf1
     for (int w = 1; w < NW; ++w) km2 = fmaxf(km2, slot[w]);
   }
   return km2;
-}
-
-// Tile t in slot I (already opened): its steps, the last of which opens tile
-// t+1 (if any) and starts that tile's first logits.  CHECK: every step
-// compares its scores with the running max (encode_step's online rule).
-// With TNORM, km2 holds the largest squared key norm of tile t on entry and
-// that of tile t+1 on exit.
-template <int D, int NW, int MBW, bool F16, bool TNORM, bool CHECK, int I>
-__device__ __forceinline__ void encode_tile_steps(EncodeState<D, MBW>& st, EncodePipe<D, F16>& pp, __bf16* ring,
-                                                  float* sKm, const __bf16* Kp, const __bf16* Vp, int t, int n0,
-                                                  int n1, int ntiles, int wave, int lane, bool wave_active, int g,
-                                                  int c16, typename Pv<F16>::T ones, float& km2) {
-  typedef Ring<D, NW> R;
-  constexpr int J1 = (I + 1) & 3;
-  const int tb = n0 + t * R::TN;
-  const int nsteps = min(R::SPT, (n1 - tb + 31) / 32);
-#pragma unroll 1
-  for (int ks = 0; ks + 1 < nsteps; ++ks) {
-    if (wave_active)
-      encode_step<D, MBW, F16, CHECK, false, true>(st, pp, R::template v<I>(ring), ks, R::template k<I>(ring), ks + 1,
-                                              tb + ks * 32, n1, g, c16, ones);
-  }
-  const int ks = nsteps - 1;
-  if (t + 1 < ntiles) {
-    km2 = ring_open<D, NW, J1, TNORM, F16>(ring, sKm, Kp, Vp, t + 1, n0, n1, wave, lane);
-    if (wave_active)
-      encode_step<D, MBW, F16, CHECK, false, true>(st, pp, R::template v<I>(ring), ks, R::template k<J1>(ring), 0,
-                                              tb + ks * 32, n1, g, c16, ones);
-  } else if (wave_active) {
-    if (tb + (ks + 1) * 32 <= n1)
-      encode_step<D, MBW, F16, CHECK, false, false>(st, pp, R::template v<I>(ring), ks, nullptr, 0, tb + ks * 32, n1, g,
-                                               c16, ones);
-    else
-      encode_step<D, MBW, F16, CHECK, true, false>(st, pp, R::template v<I>(ring), ks, nullptr, 0, tb + ks * 32, n1, g,
-                                              c16, ones);
-  }
 }
 
 // Tile rule of the online path.  A score of latent m in a tile is at most
@@ -536,19 +471,35 @@ __device__ __forceinline__ bool tile_needs_check(const EncodeState<D, MBW>& st, 
   return __builtin_amdgcn_ballot_w64(bad) != 0;
 }
 
+// Tile t in slot I: open it (except tile 0, opened before the running max
+// is seeded), then its steps.  With TNORM, km2 is the largest squared key
+// norm of tile t once it is open.
 template <int D, int NW, int MBW, bool F16, bool KNORM, bool ONLINE, bool SKIP, int I>
-__device__ __forceinline__ void encode_tile(EncodeState<D, MBW>& st, EncodePipe<D, F16>& pp, __bf16* ring,
-                                            float* sKm, const __bf16* Kp, const __bf16* Vp, int t, int n0, int n1,
-                                            int ntiles, int wave, int lane, bool wave_active, int g, int c16,
+__device__ __forceinline__ void encode_tile(EncodeState<D, MBW>& st, __bf16* ring, float* sKm, const __bf16* Kp,
+                                            const __bf16* Vp, int t, int n0, int n1, int wave, int lane,
+                                            bool wave_active, int g, int ko, const int (&vo)[D / 16],
                                             typename Pv<F16>::T ones, float& km2, float& kn2) {
+  typedef Ring<D, NW> R;
   constexpr bool TNORM = KNORM || (ONLINE && SKIP);
+  if (t > 0) km2 = ring_open<D, NW, I, TNORM, F16>(ring, sKm, Kp, Vp, t, n0, n1, wave, lane);
   if (KNORM) kn2 = fmaxf(kn2, km2);
-  if (ONLINE && (!SKIP || tile_needs_check<D, MBW>(st, km2)))
-    encode_tile_steps<D, NW, MBW, F16, TNORM, true, I>(st, pp, ring, sKm, Kp, Vp, t, n0, n1, ntiles, wave, lane,
-                                                       wave_active, g, c16, ones, km2);
-  else
-    encode_tile_steps<D, NW, MBW, F16, TNORM, false, I>(st, pp, ring, sKm, Kp, Vp, t, n0, n1, ntiles, wave, lane,
-                                                        wave_active, g, c16, ones, km2);
+  if (!wave_active) return;
+  const int tb = n0 + t * R::TN;
+  const int nsteps = min(R::SPT, (n1 - tb + 31) / 32);
+  const int full = tb + nsteps * 32 <= n1 ? nsteps : nsteps - 1;  // steps with no token past n1
+  const __bf16* sK = R::template k<I>(ring);
+  const __bf16* sV = R::template v<I>(ring);
+  if (ONLINE && (!SKIP || tile_needs_check<D, MBW>(st, km2))) {
+#pragma unroll 1
+    for (int ks = 0; ks < full; ++ks)
+      encode_step<D, MBW, F16, true, false>(st, sK, sV, ks, ko, vo, tb + 32 * ks, n1, g, ones);
+    if (full < nsteps) encode_step<D, MBW, F16, true, true>(st, sK, sV, full, ko, vo, tb + 32 * full, n1, g, ones);
+  } else {
+#pragma unroll 1
+    for (int ks = 0; ks < full; ++ks)
+      encode_step<D, MBW, F16, false, false>(st, sK, sV, ks, ko, vo, tb + 32 * ks, n1, g, ones);
+    if (full < nsteps) encode_step<D, MBW, F16, false, true>(st, sK, sV, full, ko, vo, tb + 32 * full, n1, g, ones);
+  }
 }
 
 // SKIP: the online path applies the tile rule (tile_needs_check); otherwise
@@ -566,53 +517,43 @@ __device__ __forceinline__ void encode_tiles(EncodeState<D, MBW>& st, __bf16* ri
   pv_t ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = c16 == 0 ? 1.0f : 0.0f;
-  EncodePipe<D, F16> pp;
-  pp.ko = slot_off<D>(c16, KOperand<D>::kLen * g);
+  // this lane's operand offsets (elements) within a step of a slot: K row c16
+  // at element KL g, and per 16-column block db the V^T read of row
+  // 4 g + c16 / 4 at element 16 db + 4 (c16 % 4).  The rows 16 further on, and
+  // every later step (32 rows on), add constants: the swizzle of a row depends
+  // on bits of its index that neither changes (chunk_swz).
+  const int ko = slot_off<D>(c16, KOperand<D>::kLen * g);
+  int vo[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) pp.vo[db] = slot_off<D>(4 * g + (c16 >> 2), 16 * db + 4 * (c16 & 3));
-  pp.p = pv_t{};  // no update pending before the first block
-#pragma unroll
-  for (int db = 0; db < DB; ++db) pp.v[db] = pv_t{};
+  for (int db = 0; db < DB; ++db) vo[db] = slot_off<D>(4 * g + (c16 >> 2), 16 * db + 4 * (c16 & 3));
 
   tile_dma<D, NW, 0>(ring, Kp, Vp, n0, n1, wave, lane);
-  tile_dma<D, NW, 1>(ring, Kp, Vp, n0 + R::TN, n1, wave, lane);
   float km2 = ring_open<D, NW, 0, TNORM, F16>(ring, sKm, Kp, Vp, 0, n0, n1, wave, lane);
-  if (wave_active) {
-    load_kop<D>(R::template k<0>(ring), 0, pp.ko, pp.k0, pp.k1);
-    if (ONLINE) {
-      // the running max starts at the exact column max of the first step
-      // (the shift is still zero here)
+  if (wave_active && ONLINE) {
+    // the running max starts at the exact column max of the first step
+    // (the shift is still zero here)
+    typename KOperand<D>::T k0, k1;
+    load_kop<D>(R::template k<0>(ring), 0, ko, k0, k1);
 #pragma unroll
-      for (int i = 0; i < MBW; ++i) {
-        f32x4 s0, s1;
-        block_logits<D, MBW>(st, i, pp.k0, pp.k1, s0, s1);
+    for (int i = 0; i < MBW; ++i) {
+      f32x4 s0, s1;
+      block_logits<D, MBW>(st, i, k0, k1, s0, s1);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (n0 + 4 * g + r >= n1) s0[r] = -INFINITY;
-          if (n0 + 16 + 4 * g + r >= n1) s1[r] = -INFINITY;
-        }
-        const float lm = fmaxf(max3(s1[2], s1[3], max3(s0[3], s1[0], max3(s0[0], s0[1], s0[2]))), s1[1]);
-        st.mu[i] = max_over_rows(lm);
-        st.cb[i] = f32x4{-st.mu[i], -st.mu[i], -st.mu[i], -st.mu[i]};
+      for (int r = 0; r < 4; ++r) {
+        if (n0 + 4 * g + r >= n1) s0[r] = -INFINITY;
+        if (n0 + 16 + 4 * g + r >= n1) s1[r] = -INFINITY;
       }
+      const float lm = fmaxf(max3(s1[2], s1[3], max3(s0[3], s1[0], max3(s0[0], s0[1], s0[2]))), s1[1]);
+      st.mu[i] = max_over_rows(lm);
     }
-    block_logits<D, MBW>(st, 0, pp.k0, pp.k1, pp.s0, pp.s1);
   }
-  for (int t = 0; t < ntiles; t += 4) {
-    encode_tile<D, NW, MBW, F16, KNORM, ONLINE, SKIP, 0>(st, pp, ring, sKm, Kp, Vp, t, n0, n1, ntiles, wave, lane,
-                                              wave_active, g, c16, ones, km2, kn2);
+  for (int t = 0; t < ntiles; t += 2) {
+    encode_tile<D, NW, MBW, F16, KNORM, ONLINE, SKIP, 0>(st, ring, sKm, Kp, Vp, t, n0, n1, wave, lane, wave_active,
+                                                          g, ko, vo, ones, km2, kn2);
     if (t + 1 >= ntiles) break;
-    encode_tile<D, NW, MBW, F16, KNORM, ONLINE, SKIP, 1>(st, pp, ring, sKm, Kp, Vp, t + 1, n0, n1, ntiles, wave, lane,
-                                              wave_active, g, c16, ones, km2, kn2);
-    if (t + 2 >= ntiles) break;
-    encode_tile<D, NW, MBW, F16, KNORM, ONLINE, SKIP, 2>(st, pp, ring, sKm, Kp, Vp, t + 2, n0, n1, ntiles, wave, lane,
-                                              wave_active, g, c16, ones, km2, kn2);
-    if (t + 3 >= ntiles) break;
-    encode_tile<D, NW, MBW, F16, KNORM, ONLINE, SKIP, 3>(st, pp, ring, sKm, Kp, Vp, t + 3, n0, n1, ntiles, wave, lane,
-                                              wave_active, g, c16, ones, km2, kn2);
+    encode_tile<D, NW, MBW, F16, KNORM, ONLINE, SKIP, 1>(st, ring, sKm, Kp, Vp, t + 1, n0, n1, wave, lane,
+                                                          wave_active, g, ko, vo, ones, km2, kn2);
   }
-  // the last block's pending update
-  if (wave_active) block_update<D, MBW, F16>(st, MBW - 1, pp.v, pp.p, ones);
   // the ring's trailing loads must land before the workgroup's LDS is released
   FLAREPP_WAIT_VM(0);
 }
@@ -620,14 +561,15 @@ __device__ __forceinline__ void encode_tiles(EncodeState<D, MBW>& st, __bf16* ri
 // BOUNDED: the shift may come from a.bias (the bound path, with the online
 // path as fallback when a bound is unsafe); otherwise always online.  F16: the
 // P V product in fp16 (online encodes only: the bound shift does not keep the
-// weights inside fp16's range).
+// weights inside fp16's range).  Eight-wave workgroups are compiled for four
+// waves per SIMD (at most 128 VGPRs), so two of them share a CU.
 template <int D, int NW, int MBW, bool KNORM, bool BOUNDED, bool F16>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void encode_split_bf16(EncodeArgs a) {
+__global__ __launch_bounds__(64 * NW, NW == 8 ? 4 : 2) void encode_split_bf16(EncodeArgs a) {
   static_assert(!(F16 && BOUNDED), "fp16 weights need the running max");
   constexpr int DB = D / 16;     // 16-row blocks of O^T
   constexpr int KL = KOperand<D>::kLen;
   typedef typename KOperand<D>::T kop_t;
-  __shared__ __attribute__((aligned(16))) __bf16 ring[8 * Ring<D, NW>::TE];
+  __shared__ __attribute__((aligned(16))) __bf16 ring[2 * Ring<D, NW>::SLOTS * Ring<D, NW>::TE];
   __shared__ float sKm[2 * NW];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -689,10 +631,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void encode_split_bf16(EncodeArgs 
   }
   const bool online = __any(need_online);
 #pragma unroll
-  for (int i = 0; i < MBW; ++i) {
+  for (int i = 0; i < MBW; ++i)
     if (online) st.mu[i] = 0.0f;
-    st.cb[i] = f32x4{-st.mu[i], -st.mu[i], -st.mu[i], -st.mu[i]};
-  }
   float kn2 = 0.0f;
   // the operand loads above must not be counted with the ring's loads
   FLAREPP_WAIT_VM(0);

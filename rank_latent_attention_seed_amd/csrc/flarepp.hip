@@ -125,14 +125,16 @@ Plan make_plan(const flarepp_desc* d, int op, const flarepp_tuning* t = nullptr)
 
   const int nMB = p.Mp / 16;
   // up to 128 latents: four waves; beyond: eight waves of two blocks each
-  // (a wave's registers hold at most two blocks with the pipelined step)
+  // (two blocks per wave keep a wave within the 128 registers of four
+  // waves per SIMD)
   p.nw = nMB <= 8 ? 4 : 8;
   p.mbw = nMB <= 4 ? 1 : 2;
   // splits are whole encode tiles (8192 or 4096 bf16 of K per tile, by wave count)
   const int tile = p.bf16 ? (p.nw == 8 ? 8192 : 4096) / p.D : 64;
-  // encode workgroups per head group: one round over the CUs (eight-wave
-  // workgroups use 128 KB of LDS, one per CU; four-wave ones fit two)
-  const int64_t target = (p.bf16 ? (p.nw == 8 ? 1 : 2) : 4) * int64_t(kComputeUnits);
+  // encode workgroups per head group: one round over the CUs, two
+  // workgroups per CU (eight-wave ones: 64 KB of LDS and at most 128 VGPRs
+  // per wave, four waves per SIMD)
+  const int64_t target = (p.bf16 ? 2 : 4) * int64_t(kComputeUnits);
   int64_t J = std::max<int64_t>(1, cdiv(target, G));
   if (t && t->splits > 0) J = t->splits;
   J = std::min<int64_t>(J, cdiv(d->N, tile));
