@@ -71,3 +71,31 @@ def test_no_waterfall_loops(device_asm):
                 any(x.startswith(("buffer_load", "buffer_store")) for x in body):
             loops.append(m.group(1))
     assert not loops, f"{len(loops)} waterfall loops, e.g. at {loops[:3]}"
+
+
+def test_no_register_spills(device_asm):
+    """No kernel spills registers to scratch.  The split-N encode is compiled
+    for four waves per SIMD (at most 128 VGPRs), the occupancy its speed
+    depends on; a change that no longer fits shows up here as scratch use
+    rather than as a silent slowdown."""
+    kernels = [l.split()[1] for l in device_asm if l.startswith(".amdhsa_kernel ")]
+    sizes = [int(l.split()[1]) for l in device_asm if l.startswith(".amdhsa_private_segment_fixed_size")]
+    assert kernels and len(kernels) == len(sizes)
+    spilled = [k for k, n in zip(kernels, sizes) if n != 0]
+    assert not spilled, f"{len(spilled)} kernels use scratch, e.g. {spilled[:3]}"
+
+
+def test_encode_fits_four_waves_per_simd(device_asm):
+    """The eight-wave encode instantiations stay within 128 VGPRs (two
+    workgroups per CU)."""
+    name = None
+    seen, over = 0, []
+    for l in device_asm:
+        if l.startswith(".amdhsa_kernel "):
+            name = l.split()[1]
+        elif l.startswith(".amdhsa_next_free_vgpr") and name and re.search(r"encode_split_bf16ILi(16|32)ELi8E", name):
+            seen += 1
+            if int(l.split()[1]) > 128:
+                over.append(name)
+    assert seen >= 6, seen
+    assert not over, over[:3]
