@@ -450,11 +450,13 @@ __device__ __forceinline__ bf16x8 tr_at(const __bf16* p) {
 }
 
 // ---- encode-stage latent pass: split partials of dQ_m = s sum_n dL_mn K_n.
+// Compiled for four waves per SIMD (at most 128 VGPRs; 48 KB of LDS), so two
+// workgroups share a CU.
 // Per 32-token step: L^T = K (c Q)^T - A (rows tokens, cols latents),
 // dP^T = V dO^T - delta, dL = 2^L dP (zero past the split), dQ^T += K^T dL^T,
 // K and V from the LDS tiles (K^T through transposing reads).
 template <int D>
-__global__ __launch_bounds__(512) void bwd_enc_lat_bf16(BwdEncArgs a) {
+__global__ __launch_bounds__(512, 4) void bwd_enc_lat_bf16(BwdEncArgs a) {
   constexpr int KL = KOperand<D>::kLen;
   constexpr int DB = D / 16;
   typedef typename KOperand<D>::T kop_t;
