@@ -367,14 +367,18 @@ __device__ __forceinline__ void encode_step(EncodeState<D, MBW>& st, const __bf1
 }
 
 // Largest squared key norm among the tokens of the K tile in slot I whose
-// 16-byte chunks this lane loaded itself (the chunks of one token row are
-// loaded by adjacent lanes), valid as soon as this wave's loads of the tile
-// have landed.
+// 16-byte chunks this wave loaded itself (the U chunks of one token row are
+// loaded by U adjacent lanes, so a quad-permute DPP sum completes each row),
+// valid as soon as this wave's loads of the tile have landed; the same value
+// in every lane.  Squared norms are +0 or more (or NaN, whose bit pattern
+// orders above every finite one and so forces the checked path), so the
+// maximum is taken on the bit patterns as unsigned integers, which folds
+// each DPP move into its max.
 template <int D, int NW, int I>
 __device__ __forceinline__ float own_knorm(const __bf16* ring, int wave, int lane) {
   typedef Ring<D, NW> R;
   constexpr int U = D / 8;
-  float best = 0.0f;
+  uint32_t best = 0;
 #pragma unroll
   for (int i = 0; i < R::DI; ++i) {
     const int blk = wave * R::DI + i;
@@ -385,18 +389,23 @@ __device__ __forceinline__ float own_knorm(const __bf16* ring, int wave, int lan
       const bf16x2 pr = {x[2 * e], x[2 * e + 1]};
       ss = __builtin_amdgcn_fdot2_f32_bf16(pr, pr, ss, false);
     }
-    ss += __shfl_xor(ss, 1);
-    if (U == 4) ss += __shfl_xor(ss, 2);
-    best = fmaxf(best, ss);
+    ss += dpp<0xB1>(ss);              // quad_perm [1,0,3,2]
+    if (U == 4) ss += dpp<0x4E>(ss);  // quad_perm [2,3,0,1]
+    best = max(best, __float_as_uint(ss));
   }
-  return best;
+  best = max(best, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)best, 0x124, 0xF, 0xF, false));  // row_ror:4
+  best = max(best, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)best, 0x128, 0xF, 0xF, false));  // row_ror:8
+  const auto s1 = __builtin_amdgcn_permlane16_swap(best, best, false, false);
+  best = max(s1[0], s1[1]);
+  const auto s2 = __builtin_amdgcn_permlane32_swap(best, best, false, false);
+  return __uint_as_float(max(s2[0], s2[1]));
 }
 
 // s_waitcnt lgkmcnt(0) (vmcnt and expcnt not waited on).
 constexpr uint32_t kEncWaitLgkm0 = 0xF | (0x7 << 4) | (0x3 << 14);
 
 // Ring protocol (two slots).  Tile u+1's loads are issued right after the
-// barrier that opens tile u; before that barrier a wave waits for its own
+// barrier that opens tile u (when the split has a tile u+1); before that barrier a wave waits for its own
 // loads of tile u (the only ones in flight), so every wave's part of tile u
 // has landed once all have arrived.  The barrier opening tile u is taken
 // after the wave's last step of tile u-1, so the slot refilled right after
@@ -426,14 +435,14 @@ __device__ __forceinline__ void tile_prep(__bf16* ring, float* sKm, int u, int w
     }
   }
   if (TNORM) {
-    const float part = wave_max(own_knorm<D, NW, I>(ring, wave, lane));
+    const float part = own_knorm<D, NW, I>(ring, wave, lane);
     if (lane == 0) sKm[(u & 1) * NW + wave] = part;
   }
 }
 
 template <int D, int NW, int I, bool TNORM, bool F16>
 __device__ __forceinline__ float ring_open(__bf16* ring, float* sKm, const __bf16* Kp, const __bf16* Vp, int u,
-                                           int n0, int n1, int wave, int lane) {
+                                           int n0, int n1, bool more, int wave, int lane) {
   typedef Ring<D, NW> R;
   FLAREPP_WAIT_VM(0);
   float* slot = sKm + (u & 1) * NW;
@@ -441,7 +450,7 @@ __device__ __forceinline__ float ring_open(__bf16* ring, float* sKm, const __bf1
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(kEncWaitLgkm0);  // this wave's LDS accesses are done before the barrier
   ring_barrier();
-  tile_dma<D, NW, I ^ 1>(ring, Kp, Vp, n0 + (u + 1) * R::TN, n1, wave, lane);
+  if (more) tile_dma<D, NW, I ^ 1>(ring, Kp, Vp, n0 + (u + 1) * R::TN, n1, wave, lane);
   float km2 = 0.0f;
   if (TNORM) {
     km2 = slot[0];
@@ -476,12 +485,12 @@ __device__ __forceinline__ bool tile_needs_check(const EncodeState<D, MBW>& st, 
 // norm of tile t once it is open.
 template <int D, int NW, int MBW, bool F16, bool KNORM, bool ONLINE, bool SKIP, int I>
 __device__ __forceinline__ void encode_tile(EncodeState<D, MBW>& st, __bf16* ring, float* sKm, const __bf16* Kp,
-                                            const __bf16* Vp, int t, int n0, int n1, int wave, int lane,
+                                            const __bf16* Vp, int t, int ntiles, int n0, int n1, int wave, int lane,
                                             bool wave_active, int g, int ko, const int (&vo)[D / 16],
                                             typename Pv<F16>::T ones, float& km2, float& kn2) {
   typedef Ring<D, NW> R;
   constexpr bool TNORM = KNORM || (ONLINE && SKIP);
-  if (t > 0) km2 = ring_open<D, NW, I, TNORM, F16>(ring, sKm, Kp, Vp, t, n0, n1, wave, lane);
+  if (t > 0) km2 = ring_open<D, NW, I, TNORM, F16>(ring, sKm, Kp, Vp, t, n0, n1, t + 1 < ntiles, wave, lane);
   if (KNORM) kn2 = fmaxf(kn2, km2);
   if (!wave_active) return;
   const int tb = n0 + t * R::TN;
@@ -528,7 +537,7 @@ __device__ __forceinline__ void encode_tiles(EncodeState<D, MBW>& st, __bf16* ri
   for (int db = 0; db < DB; ++db) vo[db] = slot_off<D>(4 * g + (c16 >> 2), 16 * db + 4 * (c16 & 3));
 
   tile_dma<D, NW, 0>(ring, Kp, Vp, n0, n1, wave, lane);
-  float km2 = ring_open<D, NW, 0, TNORM, F16>(ring, sKm, Kp, Vp, 0, n0, n1, wave, lane);
+  float km2 = ring_open<D, NW, 0, TNORM, F16>(ring, sKm, Kp, Vp, 0, n0, n1, ntiles > 1, wave, lane);
   if (wave_active && ONLINE) {
     // the running max starts at the exact column max of the first step
     // (the shift is still zero here)
@@ -548,10 +557,10 @@ __device__ __forceinline__ void encode_tiles(EncodeState<D, MBW>& st, __bf16* ri
     }
   }
   for (int t = 0; t < ntiles; t += 2) {
-    encode_tile<D, NW, MBW, F16, KNORM, ONLINE, SKIP, 0>(st, ring, sKm, Kp, Vp, t, n0, n1, wave, lane, wave_active,
+    encode_tile<D, NW, MBW, F16, KNORM, ONLINE, SKIP, 0>(st, ring, sKm, Kp, Vp, t, ntiles, n0, n1, wave, lane, wave_active,
                                                           g, ko, vo, ones, km2, kn2);
     if (t + 1 >= ntiles) break;
-    encode_tile<D, NW, MBW, F16, KNORM, ONLINE, SKIP, 1>(st, ring, sKm, Kp, Vp, t + 1, n0, n1, wave, lane,
+    encode_tile<D, NW, MBW, F16, KNORM, ONLINE, SKIP, 1>(st, ring, sKm, Kp, Vp, t + 1, ntiles, n0, n1, wave, lane,
                                                           wave_active, g, ko, vo, ones, km2, kn2);
   }
   // the ring's trailing loads must land before the workgroup's LDS is released
