@@ -31,10 +31,15 @@
 // LDS latencies (measured 7% faster than a two-wave-per-SIMD kernel that
 // pipelined the blocks within each wave).
 //
-// Softmax arithmetic.  The query operand arrives pre-multiplied by
-// c = s * log2(e) as a bf16 hi/lo pair (two MFMAs per tile, ~16 mantissa
-// bits), and -mu_m enters as the MFMA accumulator input, so the tile is
-// already t = c <Q_m, K_n> - mu_m and a weight is one exp2.  mu_m is either
+// Softmax arithmetic.  A synthesised query (Qd, float32) arrives
+// pre-multiplied by c = s * log2(e) as a bf16 hi/lo pair (two MFMAs per
+// tile, ~16 mantissa bits), and -mu_m enters as the MFMA accumulator input,
+// so the tile is already t = c <Q_m, K_n> - mu_m.  The seeds are bf16 inputs
+// and therefore an exact operand (EXQ): one MFMA per tile gives <S_m, K_n>
+// to float32 rounding, and one FMA per score applies c and the shift (four
+// matrix-core products per 32-token step of a wave traded for sixteen VALU
+// operations, which measured faster over the whole route).  A weight is one
+// exp2.  mu_m is either
 //   * a bound: |c| ||Q_m|| max_n ||K_n|| (Cauchy-Schwarz), supplied by the
 //     caller when it is known and keeps every exponent within [-100, 0]; no
 //     per-score max is taken; or
@@ -57,9 +62,10 @@ struct EncodeArgs {
   const __bf16* q_lo;  // low part of the same
   int64_t q_sb, q_sh;  // element strides of the operand between batches / heads
   int64_t q_off;       // the operand rows of (b, h) start at b*q_sb + h*q_sh - q_off
-  // Alternatively (q_seed non-null) the unscaled bf16 query rows [.][M][D],
-  // with the same (b, h) addressing; the operands are then formed here as
-  // hi = bf16(qc * row), lo = bf16(qc * row - hi), rows at or past M zero.
+  // Alternatively (q_seed non-null, the kernels compiled with EXQ) the
+  // unscaled bf16 query rows [.][M][D], with the same (b, h) addressing: an
+  // exact operand (rows at or past M zero) whose products are scaled by qc
+  // in float32.
   const __bf16* q_seed;
   float qc;
   int M;
@@ -231,6 +237,7 @@ struct EncodeState {
   kop_t qh[MBW], ql[MBW];
   float mu[MBW];
   float qn2[MBW];  // ||c Q_m||^2 of the lane's latent (from the hi + lo operand)
+  float c;         // exact query operand: the scale applied to its products
   f32x4 acc[D / 16 + 1][MBW];
 };
 
@@ -277,15 +284,28 @@ __device__ __forceinline__ void load_vop(const __bf16* sV, int ks, const int (&v
   }
 }
 
-// S^T tiles of latent block i (shift as accumulator input, query as hi + lo).
-template <int D, int MBW>
+// S^T tiles of latent block i: query as hi + lo with the shift as the
+// accumulator input, or (EXQ) the exact query rows in one product whose
+// float32 result is scaled and shifted, t = c <Q_m, K_n> - mu_m.
+template <int D, int MBW, bool EXQ>
 __device__ __forceinline__ void block_logits(const EncodeState<D, MBW>& st, int i, typename KOperand<D>::T k0,
                                              typename KOperand<D>::T k1, f32x4& s0, f32x4& s1) {
-  const f32x4 cb = f32x4{-st.mu[i], -st.mu[i], -st.mu[i], -st.mu[i]};
-  s0 = KOperand<D>::mma(k0, st.qh[i], cb);
-  s1 = KOperand<D>::mma(k1, st.qh[i], cb);
-  s0 = KOperand<D>::mma(k0, st.ql[i], s0);
-  s1 = KOperand<D>::mma(k1, st.ql[i], s1);
+  if constexpr (EXQ) {
+    const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
+    s0 = KOperand<D>::mma(k0, st.qh[i], z);
+    s1 = KOperand<D>::mma(k1, st.qh[i], z);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      s0[r] = fmaf(s0[r], st.c, -st.mu[i]);
+      s1[r] = fmaf(s1[r], st.c, -st.mu[i]);
+    }
+  } else {
+    const f32x4 cb = f32x4{-st.mu[i], -st.mu[i], -st.mu[i], -st.mu[i]};
+    s0 = KOperand<D>::mma(k0, st.qh[i], cb);
+    s1 = KOperand<D>::mma(k1, st.qh[i], cb);
+    s0 = KOperand<D>::mma(k0, st.ql[i], s0);
+    s1 = KOperand<D>::mma(k1, st.ql[i], s1);
+  }
 }
 
 template <bool F16>
@@ -322,7 +342,7 @@ __device__ __forceinline__ void block_update(EncodeState<D, MBW>& st, int i, con
 // recomputes the block's scores against the new shift (cheaper than keeping
 // them live, and rare).  Otherwise the shift is a bound.  MASK (the split's
 // ragged last step): tokens at or past n1 weigh zero.
-template <int D, int MBW, bool F16, bool ONLINE, bool MASK>
+template <int D, int MBW, bool F16, bool ONLINE, bool MASK, bool EXQ>
 __device__ __forceinline__ void encode_step(EncodeState<D, MBW>& st, const __bf16* sK, const __bf16* sV, int ks,
                                             int ko, const int (&vo)[D / 16], int sb, int n1, int g,
                                             typename Pv<F16>::T ones) {
@@ -344,7 +364,7 @@ __device__ __forceinline__ void encode_step(EncodeState<D, MBW>& st, const __bf1
 #pragma unroll
   for (int i = 0; i < MBW; ++i) {
     f32x4 s0, s1;
-    block_logits<D, MBW>(st, i, k0, k1, s0, s1);
+    block_logits<D, MBW, EXQ>(st, i, k0, k1, s0, s1);
     mask(s0, s1);
     if (ONLINE) {
       const float lm = fmaxf(max3(s1[2], s1[3], max3(s0[3], s1[0], max3(s0[0], s0[1], s0[2]))), s1[1]);
@@ -354,7 +374,7 @@ __device__ __forceinline__ void encode_step(EncodeState<D, MBW>& st, const __bf1
         const float al = fast_exp2(-d);
 #pragma unroll
         for (int db = 0; db <= DB; ++db) st.acc[db][i] *= al;
-        block_logits<D, MBW>(st, i, k0, k1, s0, s1);
+        block_logits<D, MBW, EXQ>(st, i, k0, k1, s0, s1);
         mask(s0, s1);
       }
     }
@@ -483,7 +503,7 @@ __device__ __forceinline__ bool tile_needs_check(const EncodeState<D, MBW>& st, 
 // Tile t in slot I: open it (except tile 0, opened before the running max
 // is seeded), then its steps.  With TNORM, km2 is the largest squared key
 // norm of tile t once it is open.
-template <int D, int NW, int MBW, bool F16, bool KNORM, bool ONLINE, bool SKIP, int I>
+template <int D, int NW, int MBW, bool F16, bool KNORM, bool ONLINE, bool SKIP, bool EXQ, int I>
 __device__ __forceinline__ void encode_tile(EncodeState<D, MBW>& st, __bf16* ring, float* sKm, const __bf16* Kp,
                                             const __bf16* Vp, int t, int ntiles, int n0, int n1, int wave, int lane,
                                             bool wave_active, int g, int ko, const int (&vo)[D / 16],
@@ -501,19 +521,19 @@ __device__ __forceinline__ void encode_tile(EncodeState<D, MBW>& st, __bf16* rin
   if (ONLINE && (!SKIP || tile_needs_check<D, MBW>(st, km2))) {
 #pragma unroll 1
     for (int ks = 0; ks < full; ++ks)
-      encode_step<D, MBW, F16, true, false>(st, sK, sV, ks, ko, vo, tb + 32 * ks, n1, g, ones);
-    if (full < nsteps) encode_step<D, MBW, F16, true, true>(st, sK, sV, full, ko, vo, tb + 32 * full, n1, g, ones);
+      encode_step<D, MBW, F16, true, false, EXQ>(st, sK, sV, ks, ko, vo, tb + 32 * ks, n1, g, ones);
+    if (full < nsteps) encode_step<D, MBW, F16, true, true, EXQ>(st, sK, sV, full, ko, vo, tb + 32 * full, n1, g, ones);
   } else {
 #pragma unroll 1
     for (int ks = 0; ks < full; ++ks)
-      encode_step<D, MBW, F16, false, false>(st, sK, sV, ks, ko, vo, tb + 32 * ks, n1, g, ones);
-    if (full < nsteps) encode_step<D, MBW, F16, false, true>(st, sK, sV, full, ko, vo, tb + 32 * full, n1, g, ones);
+      encode_step<D, MBW, F16, false, false, EXQ>(st, sK, sV, ks, ko, vo, tb + 32 * ks, n1, g, ones);
+    if (full < nsteps) encode_step<D, MBW, F16, false, true, EXQ>(st, sK, sV, full, ko, vo, tb + 32 * full, n1, g, ones);
   }
 }
 
 // SKIP: the online path applies the tile rule (tile_needs_check); otherwise
 // every step of the online path checks.
-template <int D, int NW, int MBW, bool F16, bool KNORM, bool ONLINE, bool SKIP>
+template <int D, int NW, int MBW, bool F16, bool KNORM, bool ONLINE, bool SKIP, bool EXQ>
 __device__ __forceinline__ void encode_tiles(EncodeState<D, MBW>& st, __bf16* ring, float* sKm, const __bf16* Kp,
                                              const __bf16* Vp, int n0, int n1, int wave, int lane,
                                              bool wave_active, int g, int c16, float& kn2) {
@@ -546,7 +566,7 @@ __device__ __forceinline__ void encode_tiles(EncodeState<D, MBW>& st, __bf16* ri
 #pragma unroll
     for (int i = 0; i < MBW; ++i) {
       f32x4 s0, s1;
-      block_logits<D, MBW>(st, i, k0, k1, s0, s1);
+      block_logits<D, MBW, EXQ>(st, i, k0, k1, s0, s1);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if (n0 + 4 * g + r >= n1) s0[r] = -INFINITY;
@@ -557,10 +577,10 @@ __device__ __forceinline__ void encode_tiles(EncodeState<D, MBW>& st, __bf16* ri
     }
   }
   for (int t = 0; t < ntiles; t += 2) {
-    encode_tile<D, NW, MBW, F16, KNORM, ONLINE, SKIP, 0>(st, ring, sKm, Kp, Vp, t, ntiles, n0, n1, wave, lane, wave_active,
+    encode_tile<D, NW, MBW, F16, KNORM, ONLINE, SKIP, EXQ, 0>(st, ring, sKm, Kp, Vp, t, ntiles, n0, n1, wave, lane, wave_active,
                                                           g, ko, vo, ones, km2, kn2);
     if (t + 1 >= ntiles) break;
-    encode_tile<D, NW, MBW, F16, KNORM, ONLINE, SKIP, 1>(st, ring, sKm, Kp, Vp, t + 1, ntiles, n0, n1, wave, lane,
+    encode_tile<D, NW, MBW, F16, KNORM, ONLINE, SKIP, EXQ, 1>(st, ring, sKm, Kp, Vp, t + 1, ntiles, n0, n1, wave, lane,
                                                           wave_active, g, ko, vo, ones, km2, kn2);
   }
   // the ring's trailing loads must land before the workgroup's LDS is released
@@ -572,9 +592,10 @@ __device__ __forceinline__ void encode_tiles(EncodeState<D, MBW>& st, __bf16* ri
 // P V product in fp16 (online encodes only: the bound shift does not keep the
 // weights inside fp16's range).  Eight-wave workgroups are compiled for four
 // waves per SIMD (at most 128 VGPRs), so two of them share a CU.
-template <int D, int NW, int MBW, bool KNORM, bool BOUNDED, bool F16>
+template <int D, int NW, int MBW, bool KNORM, bool BOUNDED, bool F16, bool EXQ>
 __global__ __launch_bounds__(64 * NW, NW == 8 ? 4 : 2) void encode_split_bf16(EncodeArgs a) {
   static_assert(!(F16 && BOUNDED), "fp16 weights need the running max");
+  static_assert(!(EXQ && BOUNDED), "the bound shift comes with the synthesised queries' hi/lo operand");
   constexpr int DB = D / 16;     // 16-row blocks of O^T
   constexpr int KL = KOperand<D>::kLen;
   typedef typename KOperand<D>::T kop_t;
@@ -598,6 +619,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 4 : 2) void encode_split_bf16(En
 
   // ---- query operands (B of S^T = K Q^T: lane holds column m, k = d) and shift
   EncodeState<D, MBW> st;
+  st.c = a.qc;
   bool need_online = !BOUNDED || a.bias == nullptr;
   {
     const int64_t qo = (int64_t)b * a.q_sb + (int64_t)h * a.q_sh - a.q_off;
@@ -606,16 +628,11 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 4 : 2) void encode_split_bf16(En
       const int mblk = mb0 + i;
       if (mblk < nMB) {
         const int m = mblk * 16 + c16;
-        if (a.q_seed) {
+        if constexpr (EXQ) {
           kop_t x = kop_t{};
           if (m < a.M) x = *reinterpret_cast<const kop_t*>(a.q_seed + qo + (int64_t)m * D + KL * g);
-#pragma unroll
-          for (int e = 0; e < KL; ++e) {
-            const float xs = a.qc * (float)x[e];
-            const __bf16 hi = (__bf16)xs;
-            st.qh[i][e] = hi;
-            st.ql[i][e] = (__bf16)(xs - (float)hi);
-          }
+          st.qh[i] = x;
+          st.ql[i] = kop_t{};
         } else {
           st.qh[i] = *reinterpret_cast<const kop_t*>(a.q_hi + qo + (int64_t)m * D + KL * g);
           st.ql[i] = *reinterpret_cast<const kop_t*>(a.q_lo + qo + (int64_t)m * D + KL * g);
@@ -630,7 +647,7 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 4 : 2) void encode_split_bf16(En
       float ss = 0.0f;
 #pragma unroll
       for (int e = 0; e < KL; ++e) {
-        const float x = (float)st.qh[i][e] + (float)st.ql[i][e];
+        const float x = EXQ ? a.qc * (float)st.qh[i][e] : (float)st.qh[i][e] + (float)st.ql[i][e];
         ss = fmaf(x, x, ss);
       }
       st.qn2[i] = sum_over_rows(ss);
@@ -647,10 +664,10 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 4 : 2) void encode_split_bf16(En
   FLAREPP_WAIT_VM(0);
 
   if (!BOUNDED || online)
-    encode_tiles<D, NW, MBW, F16, KNORM, true, !BOUNDED>(st, ring, sKm, Kp, Vp, n0, n1, wave, lane, wave_active, g,
+    encode_tiles<D, NW, MBW, F16, KNORM, true, !BOUNDED, EXQ>(st, ring, sKm, Kp, Vp, n0, n1, wave, lane, wave_active, g,
                                                           c16, kn2);
   else
-    encode_tiles<D, NW, MBW, false, KNORM, false, false>(st, ring, sKm, Kp, Vp, n0, n1, wave, lane, wave_active, g,
+    encode_tiles<D, NW, MBW, false, KNORM, false, false, EXQ>(st, ring, sKm, Kp, Vp, n0, n1, wave, lane, wave_active, g,
                                                           c16, kn2);
 
   // ---- partial records

@@ -337,7 +337,9 @@ flarepp_status run_prep(const Plan& p, const void* src, bool src_bf16, int64_t s
   return launched();
 }
 
-template <int D, bool KNORM, bool BOUNDED>
+// EXQ: the query is the bf16 seeds themselves (a.q_seed set), an exact
+// operand; otherwise the prepared hi/lo operand of c Qd (a.q_hi, a.q_lo).
+template <int D, bool KNORM, bool BOUNDED, bool EXQ>
 flarepp_status run_encode_bf16(const Plan& p, const EncodeArgs& a, int Gc, hipStream_t st, Recorder& rec,
                                int kind) {
   const dim3 grid((unsigned)p.J, (unsigned)Gc, (unsigned)cdiv(p.Mp / 16, p.nw * p.mbw));
@@ -345,11 +347,11 @@ flarepp_status run_encode_bf16(const Plan& p, const EncodeArgs& a, int Gc, hipSt
   // the encodes that take a running max form P V in fp16 (see Pv)
   constexpr bool F16 = !BOUNDED;
   if (p.nw == 8)
-    encode_split_bf16<D, 8, 2, KNORM, BOUNDED, F16><<<grid, dim3(512), 0, st>>>(a);
+    encode_split_bf16<D, 8, 2, KNORM, BOUNDED, F16, EXQ><<<grid, dim3(512), 0, st>>>(a);
   else if (p.mbw == 2)
-    encode_split_bf16<D, 4, 2, KNORM, BOUNDED, F16><<<grid, dim3(256), 0, st>>>(a);
+    encode_split_bf16<D, 4, 2, KNORM, BOUNDED, F16, EXQ><<<grid, dim3(256), 0, st>>>(a);
   else
-    encode_split_bf16<D, 4, 1, KNORM, BOUNDED, F16><<<grid, dim3(256), 0, st>>>(a);
+    encode_split_bf16<D, 4, 1, KNORM, BOUNDED, F16, EXQ><<<grid, dim3(256), 0, st>>>(a);
   rec.after(st);
   return launched();
 }
@@ -550,23 +552,18 @@ flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in
       const bool routed = stage == kRoute || stage == kSpectrum;  // stages 1 and 2 as in the route
       if (stage == kSeed || routed || stage == kFlare) {
         EncodeArgs e = encode_args(p, ws, K, V, g0);
+        // the seeds are the exact query operand, scaled by c in the encode
+        e.q_seed = static_cast<const __bf16*>(S);
+        e.qc = p.c;
+        e.M = p.M;
         e.q_sb = 0;
+        e.q_sh = seed_h;
         e.q_off = 0;
-        if (stage == kFlare) {  // the prepared c S operands
-          e.q_hi = shi;
-          e.q_lo = slo;
-          e.q_sh = p.nS > 1 ? MpD : 0;
-        } else {  // formed from S in the encode
-          e.q_seed = static_cast<const __bf16*>(S);
-          e.qc = p.c;
-          e.M = p.M;
-          e.q_sh = seed_h;
-        }
         e.knorm = at<float>(ws, p.o_knorm);
         if (routed)
-          FLAREPP_TRY((run_encode_bf16<D, true, false>(p, e, Gc, st, rec, FLAREPP_KERNEL_SEED_ENCODE)));
+          FLAREPP_TRY((run_encode_bf16<D, true, false, true>(p, e, Gc, st, rec, FLAREPP_KERNEL_SEED_ENCODE)));
         else
-          FLAREPP_TRY((run_encode_bf16<D, false, false>(p, e, Gc, st, rec, FLAREPP_KERNEL_SEED_ENCODE)));
+          FLAREPP_TRY((run_encode_bf16<D, false, false, true>(p, e, Gc, st, rec, FLAREPP_KERNEL_SEED_ENCODE)));
         MergeArgs m = merge_args(p, ws, g0);
         refit_from(m, e);  // an encode with fp16 weights (see run_encode_bf16)
         if (stage == kFlare) {
@@ -597,9 +594,9 @@ flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in
         e.q_off = g0 * MpD;
         e.bias = routed ? at<float>(ws, p.o_bias) : nullptr;
         if (routed)
-          FLAREPP_TRY((run_encode_bf16<D, false, true>(p, e, Gc, st, rec, FLAREPP_KERNEL_ENCODE)));
+          FLAREPP_TRY((run_encode_bf16<D, false, true, false>(p, e, Gc, st, rec, FLAREPP_KERNEL_ENCODE)));
         else
-          FLAREPP_TRY((run_encode_bf16<D, false, false>(p, e, Gc, st, rec, FLAREPP_KERNEL_ENCODE)));
+          FLAREPP_TRY((run_encode_bf16<D, false, false, false>(p, e, Gc, st, rec, FLAREPP_KERNEL_ENCODE)));
         MergeArgs m = merge_args(p, ws, g0);
         if (!routed) refit_from(m, e);  // the stand-alone encode has fp16 weights, the routed one bf16
         m.out = stage == kSpectrum ? nullptr : Z_out;  // (Z_out carries the spectrum's matrix output)
@@ -924,6 +921,9 @@ flarepp_status run_backward_bf16(const Plan& p, const void* S, const void* K, co
     const int Gc = (int)std::min<int64_t>(p.G, p.BH - g0);
     // ---- forward stages 1 and 2, as in the route
     {
+      // the seed encode takes c S as the same hi/lo operand as the backward
+      // passes of stage 1 below, so that the recomputed forward and the
+      // gradients see the same logits
       EncodeArgs e = encode_args(p, ws, K, V, g0);
       e.q_hi = shi;
       e.q_lo = slo;
@@ -931,7 +931,7 @@ flarepp_status run_backward_bf16(const Plan& p, const void* S, const void* K, co
       e.q_sh = p.nS > 1 ? MpD : 0;
       e.q_off = 0;
       e.knorm = at<float>(ws, p.o_knorm);
-      FLAREPP_TRY((run_encode_bf16<D, true, false>(p, e, Gc, st, rec, FLAREPP_KERNEL_SEED_ENCODE)));
+      FLAREPP_TRY((run_encode_bf16<D, true, false, false>(p, e, Gc, st, rec, FLAREPP_KERNEL_SEED_ENCODE)));
       MergeArgs m = merge_args(p, ws, g0);
       refit_from(m, e);
       m.outl = qf;
@@ -950,7 +950,7 @@ flarepp_status run_backward_bf16(const Plan& p, const void* S, const void* K, co
       e2.q_sh = MpD;
       e2.q_off = g0 * MpD;
       e2.bias = at<float>(ws, p.o_bias);
-      FLAREPP_TRY((run_encode_bf16<D, false, true>(p, e2, Gc, st, rec, FLAREPP_KERNEL_ENCODE)));
+      FLAREPP_TRY((run_encode_bf16<D, false, true, false>(p, e2, Gc, st, rec, FLAREPP_KERNEL_ENCODE)));
       MergeArgs m2 = merge_args(p, ws, g0);
       m2.outl = zf;
       m2.lse = at<float>(ws, p.o_lse2);

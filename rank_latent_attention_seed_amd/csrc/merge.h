@@ -46,7 +46,7 @@ struct MergeArgs {
   // (b, h) at b*fq_sb + h*fq_sh - fq_off), K, V and token splits.
   const __bf16* fq_hi;
   const __bf16* fq_lo;
-  const __bf16* fq_seed;  // or the unscaled rows [.][M][D] the encode formed them from (EncodeArgs::q_seed)
+  const __bf16* fq_seed;  // or the unscaled seed rows [.][M][D] (EncodeArgs::q_seed), scaled by fq_c
   float fq_c;
   int64_t fq_sb, fq_sh, fq_off;
   const __bf16* fK;
@@ -65,17 +65,13 @@ template <int D>
 __device__ __forceinline__ void refit_record(const MergeArgs& a, int64_t bh, int m, int j, float* rec) {
   const int b = (int)(bh / a.H), h = (int)(bh - (int64_t)b * a.H);
   const int64_t qo = (int64_t)b * a.fq_sb + (int64_t)h * a.fq_sh - a.fq_off + (int64_t)m * D;
+  // the encode's query: the exact seed row (zero past M), its products
+  // scaled by c, or the hi + lo operand of c Q
   float q[D];
+  const float qs = a.fq_seed ? a.fq_c : 1.0f;
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    if (a.fq_seed) {  // the encode's own rounding of c * row into hi + lo
-      const float xs = a.fq_c * (float)a.fq_seed[qo + d];
-      const __bf16 hi = (__bf16)xs;
-      q[d] = (float)hi + (float)(__bf16)(xs - (float)hi);
-    } else {
-      q[d] = (float)a.fq_hi[qo + d] + (float)a.fq_lo[qo + d];
-    }
-  }
+  for (int d = 0; d < D; ++d)
+    q[d] = a.fq_seed ? (m < a.M ? (float)a.fq_seed[qo + d] : 0.0f) : (float)a.fq_hi[qo + d] + (float)a.fq_lo[qo + d];
   const int n0 = j * a.chunk, n1 = min(a.N, n0 + a.chunk);
   const __bf16* Kp = a.fK + bh * (int64_t)a.N * D;
   const __bf16* Vp = a.fV + bh * (int64_t)a.N * D;
@@ -83,7 +79,7 @@ __device__ __forceinline__ void refit_record(const MergeArgs& a, int64_t bh, int
     float t = 0.0f;
 #pragma unroll
     for (int d = 0; d < D; ++d) t = fmaf(q[d], (float)Kp[(int64_t)n * D + d], t);
-    return t;
+    return qs * t;
   };
   float mu = -INFINITY;
   for (int n = n0; n < n1; ++n) mu = fmaxf(mu, logit(n));
