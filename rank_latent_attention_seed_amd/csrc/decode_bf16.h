@@ -53,13 +53,66 @@ struct DecodeArgs {
 // the rounding of the hi/lo operand); when 2 mu_g <= kBoundSpan all logits lie
 // in [-2 mu_g, 0] after the shift and no per-token norm is needed.  Needs the
 // split key norms of the head (a.knorm) and the latent norms; +inf otherwise.
-__device__ __forceinline__ float head_shift(const DecodeArgs& a, int64_t lbh, float qmax, int lane) {
+// kmax receives max_n ||K_n|| (+inf without the key norms).
+__device__ __forceinline__ float head_shift(const DecodeArgs& a, int64_t lbh, float qmax, int lane, float& kmax) {
+  kmax = INFINITY;
   if (!a.knorm || !a.qnorm) return INFINITY;
   float k2 = 0.0f;
   for (int j = lane; j < a.Jk; j += 64) k2 = fmaxf(k2, a.knorm[lbh * a.Jk + j]);
-  k2 = wave_max(k2);
-  return fabsf(a.c) * __builtin_sqrtf(k2) * qmax * (1.0f + 1.0f / 4096.0f);
+  kmax = __builtin_sqrtf(wave_max(k2));
+  return fabsf(a.c) * kmax * qmax * (1.0f + 1.0f / 4096.0f);
 }
+
+// Single-product logits.  The keys are exact in fp16 as well as in bf16 when
+// |k| < 2^10 (bf16's 8-bit significand fits fp16's 11 bits; below fp16's
+// normal range a key moves by at most 2^-25).  Rounding c Qd to fp16 moves
+// each product term by at most 2^-11 of itself, so a logit by at most
+// 2^-11 |c| ||Qd_m|| ||K_n|| <= 2^-11 mu_g (Cauchy-Schwarz).  With
+// mu_g <= kF16Logit that is at most 2^-7 in log2 units: a weight changes by at
+// most 0.55%, next to the 0.39% of the bf16 rounding every weight takes before
+// the Z^T P^T product.  Heads within that bound take one fp16 product per
+// logit tile instead of the hi/lo pair (a third fewer matrix-core products
+// per token block); the others keep the pair.
+constexpr float kF16Logit = 16.0f;
+__device__ __forceinline__ bool f16_logits(float mu_g, float kmax, float qmax, float c) {
+  return mu_g <= kF16Logit && kmax <= 1024.0f && fabsf(c) * qmax <= 1024.0f;
+}
+
+template <int D>
+struct KOperand16;
+template <>
+struct KOperand16<32> {
+  typedef f16x8 T;
+  __device__ __forceinline__ static f32x4 mma(T a, T b, f32x4 c) { return mfma_k32(a, b, c); }
+};
+template <>
+struct KOperand16<16> {
+  typedef f16x4 T;
+  __device__ __forceinline__ static f32x4 mma(T a, T b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+  }
+};
+// fp16 operand from a bf16 one (the key rows), and from a bf16 hi/lo pair
+// (c Qd: hi + lo is exact in float32, then rounded to nearest once)
+template <typename H, typename B>
+__device__ __forceinline__ H to_f16(const B x) {
+  H r;
+#pragma unroll
+  for (int e = 0; e < (int)(sizeof(B) / 2); ++e) r[e] = (_Float16)(float)x[e];
+  return r;
+}
+template <typename H, typename B>
+__device__ __forceinline__ H to_f16(const B hi, const B lo) {
+  H r;
+#pragma unroll
+  for (int e = 0; e < (int)(sizeof(B) / 2); ++e) r[e] = (_Float16)((float)hi[e] + (float)lo[e]);
+  return r;
+}
+
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
 
 template <int D, int MB>
 __global__ __launch_bounds__(256, 1) void decode_bf16(DecodeArgs a) {
@@ -106,8 +159,10 @@ __global__ __launch_bounds__(256, 1) void decode_bf16(DecodeArgs a) {
   qmax = wave_max(qmax);
   const bool have_bound = a.qnorm != nullptr;
   const bool ragged_m = a.M < MP;
-  const float mu_g = head_shift(a, lbh, qmax, lane);
+  float kmax;
+  const float mu_g = head_shift(a, lbh, qmax, lane, kmax);
   const bool gshift = 2.0f * mu_g <= kBoundSpan;
+  const bool q16 = f16_logits(mu_g, kmax, qmax, a.c);
 
   // K and Y of this workgroup's tokens as buffer resources: tokens past n1
   // read as zeros and their stores are dropped, so loads need no clamping
@@ -124,10 +179,22 @@ __global__ __launch_bounds__(256, 1) void decode_bf16(DecodeArgs a) {
   // the per-token sum of the same bf16 weights that enter Z^T P^T
   const bf16x8 ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
                        (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
+  // the token loop, compiled once with the hi/lo logits and once with the
+  // fp16 ones (Q16); the head's bound picks one for the whole workgroup
+  auto run = [&](auto q16_tag) {
+  constexpr bool Q16 = decltype(q16_tag)::value;
+  typedef typename KOperand16<D>::T hop_t;
+  hop_t qf[Q16 ? MB : 1];
+  if constexpr (Q16) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) qf[mb] = to_f16<hop_t>(qh[mb], ql[mb]);
+  }
   auto body = [&](const kop_t kb, const int blk) {
 
     float sh = -mu_g;
-    if (!gshift) {
+    hop_t k16;
+    if constexpr (Q16) k16 = to_f16<hop_t>(kb);
+    if (!Q16 && !gshift) {  // (Q16 implies gshift)
       // token norm -> shift
       float ss = 0.0f;
 #pragma unroll
@@ -166,8 +233,12 @@ __global__ __launch_bounds__(256, 1) void decode_bf16(DecodeArgs a) {
       for (int i = 0; i < CH; ++i) {
         const int mb = ch * CH + i;
         if (mb < MB) {
-          L[i] = KOperand<D>::mma(qh[mb], kb, cinit);
-          L[i] = KOperand<D>::mma(ql[mb], kb, L[i]);
+          if constexpr (Q16) {
+            L[i] = KOperand16<D>::mma(qf[mb], k16, cinit);
+          } else {
+            L[i] = KOperand<D>::mma(qh[mb], kb, cinit);
+            L[i] = KOperand<D>::mma(ql[mb], kb, L[i]);
+          }
         } else {
           L[i] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
         }
@@ -220,6 +291,11 @@ __global__ __launch_bounds__(256, 1) void decode_bf16(DecodeArgs a) {
     k1 = kload(blk + 4 * S);
     body(k2, blk + 2 * S);
   }
+  };
+  if (q16)
+    run(Flag<true>{});
+  else
+    run(Flag<false>{});
 }
 
 // Paired decode for many latents.  Holding c * Qd (hi/lo) and Z^T for all M
@@ -242,8 +318,13 @@ __device__ __forceinline__ void pair_barrier() {
 
 // RAGGED: some of this wave's latent rows lie at or past M (M is not a
 // multiple of 16, or the blocks do not split evenly); those get weight zero.
-template <int D, int MBH, bool RAGGED>
-__global__ __launch_bounds__(128, 2) void decode_pair_bf16(DecodeArgs a) {
+//
+// Q16: the kernel serves the heads whose logits take one fp16 product
+// (f16_logits) and returns at once for the others; the route launches both
+// forms back to back.  The fp16 form holds one operand per latent block
+// instead of the hi/lo pair and fits 128 VGPRs: four waves per SIMD.
+template <int D, int MBH, bool RAGGED, bool Q16>
+__global__ __launch_bounds__(128, Q16 ? 4 : 2) void decode_pair_bf16(DecodeArgs a) {
   constexpr int KL = KOperand<D>::kLen;
   constexpr int DB = D / 16;
   constexpr int KBH = (MBH + 1) / 2;  // 32-latent contraction blocks per wave
@@ -261,9 +342,20 @@ __global__ __launch_bounds__(128, 2) void decode_pair_bf16(DecodeArgs a) {
   const int n1 = min(a.N, n0 + a.chunk);
   const int MB = a.Mp >> 4;
   const int mb0 = w2 * MBH;  // this wave's first latent block
+  const int64_t qo = (int64_t)b * a.q_sb + (int64_t)h * a.q_sh - a.q_off;
+
+  float qmax = 0.0f;
+  if (a.qnorm)
+    for (int m = lane; m < a.Mp; m += 64) qmax = fmaxf(qmax, a.qnorm[qo / D + m]);
+  qmax = wave_max(qmax);
+  const bool have_bound = a.qnorm != nullptr;
+  float kmax;
+  const float mu_g = head_shift(a, lbh, qmax, lane, kmax);
+  const bool gshift = 2.0f * mu_g <= kBoundSpan;  // the same in both waves
+  // the same in both waves, so the whole workgroup leaves together
+  if (f16_logits(mu_g, kmax, qmax, a.c) != Q16) return;
 
   // ---- this wave's half of the latent side, in registers
-  const int64_t qo = (int64_t)b * a.q_sb + (int64_t)h * a.q_sh - a.q_off;
   kop_t qh[MBH], ql[MBH];
 #pragma unroll
   for (int i = 0; i < MBH; ++i) {
@@ -290,13 +382,6 @@ __global__ __launch_bounds__(128, 2) void decode_pair_bf16(DecodeArgs a) {
         zop[kb][db] = bf16x8{z0[0], z0[1], z0[2], z0[3], z1[0], z1[1], z1[2], z1[3]};
       }
   }
-  float qmax = 0.0f;
-  if (a.qnorm)
-    for (int m = lane; m < a.Mp; m += 64) qmax = fmaxf(qmax, a.qnorm[qo / D + m]);
-  qmax = wave_max(qmax);
-  const bool have_bound = a.qnorm != nullptr;
-  const float mu_g = head_shift(a, lbh, qmax, lane);
-  const bool gshift = 2.0f * mu_g <= kBoundSpan;  // the same in both waves
   // latent rows of this wave at or past M (the padding of the last block and
   // whole blocks past the end) get weight zero
   const int mvalid = a.M - mb0 * 16;
@@ -320,10 +405,20 @@ __global__ __launch_bounds__(128, 2) void decode_pair_bf16(DecodeArgs a) {
   // the per-token sum of the same bf16 weights that enter Z^T P^T
   const bf16x8 ones = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
                        (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
+  auto run = [&](auto q16_tag) {
+  static_assert(decltype(q16_tag)::value == Q16, "one logit form per kernel");
+  typedef typename KOperand16<D>::T hop_t;
+  hop_t qf[Q16 ? MBH : 1];
+  if constexpr (Q16) {
+#pragma unroll
+    for (int i = 0; i < MBH; ++i) qf[i] = to_f16<hop_t>(qh[i], ql[i]);
+  }
   auto body = [&](const kop_t kb, const int blk, const int buf) {
 
     float sh = -mu_g;
-    if (!gshift) {
+    hop_t k16;
+    if constexpr (Q16) k16 = to_f16<hop_t>(kb);
+    if (!Q16 && !gshift) {  // (Q16 implies gshift)
       // token norm -> shift (identical in both waves)
       float ss = 0.0f;
 #pragma unroll
@@ -367,8 +462,12 @@ __global__ __launch_bounds__(128, 2) void decode_pair_bf16(DecodeArgs a) {
       for (int u = 0; u < 2; ++u) {
         const int i = 2 * kb2 + u;
         if (i < MBH) {
-          L[u] = KOperand<D>::mma(qh[i], kb, cinit);
-          L[u] = KOperand<D>::mma(ql[i], kb, L[u]);
+          if constexpr (Q16) {
+            L[u] = KOperand16<D>::mma(qf[i], k16, cinit);
+          } else {
+            L[u] = KOperand<D>::mma(qh[i], kb, cinit);
+            L[u] = KOperand<D>::mma(ql[i], kb, L[u]);
+          }
           if (RAGGED) {
             if (i == ipart)
               L[u] += padb;
@@ -424,6 +523,8 @@ __global__ __launch_bounds__(128, 2) void decode_pair_bf16(DecodeArgs a) {
     k1 = kload(blk + 4 * S);
     body(k2, blk + 2 * S, par);
   }
+  };
+  run(Flag<Q16>{});
 }
 
 }  // namespace flarepp

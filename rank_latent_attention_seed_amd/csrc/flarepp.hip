@@ -145,14 +145,15 @@ Plan make_plan(const flarepp_desc* d, int op, const flarepp_tuning* t = nullptr)
   while (tpr < p.J && tpr < 64) tpr *= 2;
   p.tpr = tpr;
   // decode: beyond 8 latent blocks two waves share each token block (paired
-  // kernel, four 2-wave workgroups per CU); otherwise one 4-wave workgroup
+  // kernel, eight 2-wave workgroups per CU); otherwise one 4-wave workgroup
   // per CU pair of SIMDs, 64-token rounds
   p.dpair = nMB > 8;
   if (t && t->decode_kernel > 0) p.dpair = nMB > 8 && t->decode_kernel == 1;
   if (p.dpair) {
-    // six 2-wave workgroups per CU: three waves per SIMD at <= 168 VGPRs,
-    // all resident at once (one round)
-    int per_cu = 6;
+    // eight 2-wave workgroups per CU: the fp16-logit form (<= 128 VGPRs)
+    // holds them all at once, four waves per SIMD; the hi/lo form (three
+    // waves per SIMD) takes them in one and a third rounds
+    int per_cu = 8;
     if (t && t->decode_wg_per_cu > 0) per_cu = t->decode_wg_per_cu;
     const int64_t dwg = std::max<int64_t>(1, cdiv(per_cu * int64_t(kComputeUnits), G));
     p.dchunk = (int)std::min<int64_t>(cdiv(cdiv(d->N, dwg), 16) * 16, kMaxDecodeChunk);
@@ -394,27 +395,37 @@ void launch_decode_mb(const DecodeArgs& a, dim3 grid, hipStream_t st) {
   decode_bf16<D, MB><<<grid, dim3(256), 0, st>>>(a);
 }
 
+template <int D, bool Q16>
+void launch_decode_pair(int mbh, bool ragged, const DecodeArgs& a, dim3 grid, hipStream_t st) {
+  if (!ragged) {
+    switch (mbh) {
+      case 5: decode_pair_bf16<D, 5, false, Q16><<<grid, dim3(128), 0, st>>>(a); break;
+      case 6: decode_pair_bf16<D, 6, false, Q16><<<grid, dim3(128), 0, st>>>(a); break;
+      case 7: decode_pair_bf16<D, 7, false, Q16><<<grid, dim3(128), 0, st>>>(a); break;
+      default: decode_pair_bf16<D, 8, false, Q16><<<grid, dim3(128), 0, st>>>(a); break;
+    }
+  } else {
+    switch (mbh) {
+      case 5: decode_pair_bf16<D, 5, true, Q16><<<grid, dim3(128), 0, st>>>(a); break;
+      case 6: decode_pair_bf16<D, 6, true, Q16><<<grid, dim3(128), 0, st>>>(a); break;
+      case 7: decode_pair_bf16<D, 7, true, Q16><<<grid, dim3(128), 0, st>>>(a); break;
+      default: decode_pair_bf16<D, 8, true, Q16><<<grid, dim3(128), 0, st>>>(a); break;
+    }
+  }
+}
+
 template <int D>
 flarepp_status run_decode_bf16(const Plan& p, const DecodeArgs& a, int Gc, hipStream_t st, Recorder& rec) {
   const dim3 grid((unsigned)cdiv(p.N, p.dchunk), (unsigned)Gc);
   rec.before(FLAREPP_KERNEL_DECODE, st);
   if (p.dpair) {
+    // the hi/lo form for heads outside the fp16 bound, then the fp16 form
+    // (only the route passes the key norms that bound; without them every
+    // head takes the hi/lo form)
     const int mbh = (p.Mp / 16 + 1) / 2;
-    if (p.M == 2 * mbh * 16) {
-      switch (mbh) {
-        case 5: decode_pair_bf16<D, 5, false><<<grid, dim3(128), 0, st>>>(a); break;
-        case 6: decode_pair_bf16<D, 6, false><<<grid, dim3(128), 0, st>>>(a); break;
-        case 7: decode_pair_bf16<D, 7, false><<<grid, dim3(128), 0, st>>>(a); break;
-        default: decode_pair_bf16<D, 8, false><<<grid, dim3(128), 0, st>>>(a); break;
-      }
-    } else {
-      switch (mbh) {
-        case 5: decode_pair_bf16<D, 5, true><<<grid, dim3(128), 0, st>>>(a); break;
-        case 6: decode_pair_bf16<D, 6, true><<<grid, dim3(128), 0, st>>>(a); break;
-        case 7: decode_pair_bf16<D, 7, true><<<grid, dim3(128), 0, st>>>(a); break;
-        default: decode_pair_bf16<D, 8, true><<<grid, dim3(128), 0, st>>>(a); break;
-      }
-    }
+    const bool ragged = p.M != 2 * mbh * 16;
+    launch_decode_pair<D, false>(mbh, ragged, a, grid, st);
+    if (a.knorm) launch_decode_pair<D, true>(mbh, ragged, a, grid, st);
     rec.after(st);
     return launched();
   }

@@ -144,6 +144,33 @@ def test_large_logits_ragged_paired_decode(fp):
     run_and_compare(fp, p, label="large logits, ragged paired decode")
 
 
+@pytest.mark.parametrize("M,D", [(256, 32), (200, 32), (96, 32), (240, 16)])
+def test_decode_logit_forms_mixed_heads(fp, M, D):
+    """Heads on both sides of the decode's fp16-logit bound in one call: the
+    head bound mu_g = |c| max||K|| max||Qd|| (c = s log2 e) is <= 16 for the
+    small-key heads (one fp16 product per logit tile) and far above it for the
+    large-key heads (bf16 hi/lo pair).  Key scales are powers of two, exact in
+    bf16.  M = 256 and 200 take the paired decode (both kernel forms run in
+    one route, each serving its heads), M = 96 the single-wave decode."""
+    import oracle
+
+    p = inputs.random_problem(1, 4, 4000, M, D, dtype="bf16", seed=21)
+    K = inputs.bf16_bits_to_f32(p.K)
+    for h, f in enumerate((0.25, 1.0, 4.0, 8.0)):
+        K[0, h] *= f
+    p.K = inputs.f32_to_bf16_bits(K)
+    c = abs(p.scale) * math.log2(math.e)
+    mus = []
+    for h in range(p.H):
+        Qd, _, _ = oracle.route(p.S, p.K[:, h:h + 1], p.V[:, h:h + 1], p.scale)
+        kmax = float(np.sqrt((K[0, h].astype(np.float64) ** 2).sum(-1)).max())
+        qmax = float(np.sqrt((Qd[0, 0] ** 2).sum(-1)).max())
+        mus.append(c * kmax * qmax)
+    print(f"\n  head bounds mu_g = {[round(m, 2) for m in mus]}", flush=True)
+    assert min(mus) < 15 and max(mus) > 17, "the case must cover both logit forms"
+    run_and_compare(fp, p, label=f"mixed logit forms M{M} D{D}")
+
+
 def test_stages_match_oracle(fp):
     import torch
     import oracle
