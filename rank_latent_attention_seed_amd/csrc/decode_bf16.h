@@ -63,52 +63,6 @@ __device__ __forceinline__ float head_shift(const DecodeArgs& a, int64_t lbh, fl
   return fabsf(a.c) * kmax * qmax * (1.0f + 1.0f / 4096.0f);
 }
 
-// Single-product logits.  The keys are exact in fp16 as well as in bf16 when
-// |k| < 2^10 (bf16's 8-bit significand fits fp16's 11 bits; below fp16's
-// normal range a key moves by at most 2^-25).  Rounding c Qd to fp16 moves
-// each product term by at most 2^-11 of itself, so a logit by at most
-// 2^-11 |c| ||Qd_m|| ||K_n|| <= 2^-11 mu_g (Cauchy-Schwarz).  With
-// mu_g <= kF16Logit that is at most 2^-7 in log2 units: a weight changes by at
-// most 0.55%, next to the 0.39% of the bf16 rounding every weight takes before
-// the Z^T P^T product.  Heads within that bound take one fp16 product per
-// logit tile instead of the hi/lo pair (a third fewer matrix-core products
-// per token block); the others keep the pair.
-constexpr float kF16Logit = 16.0f;
-__device__ __forceinline__ bool f16_logits(float mu_g, float kmax, float qmax, float c) {
-  return mu_g <= kF16Logit && kmax <= 1024.0f && fabsf(c) * qmax <= 1024.0f;
-}
-
-template <int D>
-struct KOperand16;
-template <>
-struct KOperand16<32> {
-  typedef f16x8 T;
-  __device__ __forceinline__ static f32x4 mma(T a, T b, f32x4 c) { return mfma_k32(a, b, c); }
-};
-template <>
-struct KOperand16<16> {
-  typedef f16x4 T;
-  __device__ __forceinline__ static f32x4 mma(T a, T b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-  }
-};
-// fp16 operand from a bf16 one (the key rows), and from a bf16 hi/lo pair
-// (c Qd: hi + lo is exact in float32, then rounded to nearest once)
-template <typename H, typename B>
-__device__ __forceinline__ H to_f16(const B x) {
-  H r;
-#pragma unroll
-  for (int e = 0; e < (int)(sizeof(B) / 2); ++e) r[e] = (_Float16)(float)x[e];
-  return r;
-}
-template <typename H, typename B>
-__device__ __forceinline__ H to_f16(const B hi, const B lo) {
-  H r;
-#pragma unroll
-  for (int e = 0; e < (int)(sizeof(B) / 2); ++e) r[e] = (_Float16)((float)hi[e] + (float)lo[e]);
-  return r;
-}
-
 template <bool B>
 struct Flag {
   static constexpr bool value = B;

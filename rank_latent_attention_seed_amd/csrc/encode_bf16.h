@@ -74,6 +74,12 @@ struct EncodeArgs {
   float* part;         // [G][Mp][J][D + 4] partial records (G = heads of this launch)
   float* knorm;        // [G][J] max squared key norm of each split, or null
   const float* bias;   // [G][Mp] mu_m bound (log2 units; +inf = use online), or null
+  // Bounded encodes of the route: the seed encode's split key norms ([G][Jk],
+  // squared) and the latent norms ||Qd_m|| (the operand's block layout over
+  // D), from which the head's logit bound picks the fp16 logit form; or null
+  const float* kin;
+  const float* qnorm;
+  int Jk;
   int H, N, Mp, J, chunk;
   int64_t bh0;         // first (b, h) of this launch: grid.y = lbh indexes (b, h) = bh0 + lbh
 };
@@ -284,13 +290,27 @@ __device__ __forceinline__ void load_vop(const __bf16* sV, int ks, const int (&v
   }
 }
 
+// Form of the query operand (LQ): kHiLo, c Q as a bf16 hi/lo pair; kExact,
+// the exact bf16 query rows (the seeds), whose products are scaled by c in
+// float32; kF16, c Q in fp16 against keys converted to fp16 in the ring
+// (f16_logits).
+constexpr int kHiLo = 0, kExact = 1, kF16 = 2;
+
 // S^T tiles of latent block i: query as hi + lo with the shift as the
-// accumulator input, or (EXQ) the exact query rows in one product whose
-// float32 result is scaled and shifted, t = c <Q_m, K_n> - mu_m.
-template <int D, int MBW, bool EXQ>
+// accumulator input, or (kExact) the exact query rows in one product whose
+// float32 result is scaled and shifted, t = c <Q_m, K_n> - mu_m, or (kF16)
+// one fp16 product with the shift as the accumulator input (qh holds the
+// fp16 bits of c Q, the key slot the fp16 keys).
+template <int D, int MBW, int LQ>
 __device__ __forceinline__ void block_logits(const EncodeState<D, MBW>& st, int i, typename KOperand<D>::T k0,
                                              typename KOperand<D>::T k1, f32x4& s0, f32x4& s1) {
-  if constexpr (EXQ) {
+  if constexpr (LQ == kF16) {
+    typedef typename KOperand16<D>::T hop_t;
+    const f32x4 cb = f32x4{-st.mu[i], -st.mu[i], -st.mu[i], -st.mu[i]};
+    const hop_t q = __builtin_bit_cast(hop_t, st.qh[i]);
+    s0 = KOperand16<D>::mma(__builtin_bit_cast(hop_t, k0), q, cb);
+    s1 = KOperand16<D>::mma(__builtin_bit_cast(hop_t, k1), q, cb);
+  } else if constexpr (LQ == kExact) {
     const f32x4 z = f32x4{0.f, 0.f, 0.f, 0.f};
     s0 = KOperand<D>::mma(k0, st.qh[i], z);
     s1 = KOperand<D>::mma(k1, st.qh[i], z);
@@ -342,7 +362,7 @@ __device__ __forceinline__ void block_update(EncodeState<D, MBW>& st, int i, con
 // recomputes the block's scores against the new shift (cheaper than keeping
 // them live, and rare).  Otherwise the shift is a bound.  MASK (the split's
 // ragged last step): tokens at or past n1 weigh zero.
-template <int D, int MBW, bool F16, bool ONLINE, bool MASK, bool EXQ>
+template <int D, int MBW, bool F16, bool ONLINE, bool MASK, int LQ>
 __device__ __forceinline__ void encode_step(EncodeState<D, MBW>& st, const __bf16* sK, const __bf16* sV, int ks,
                                             int ko, const int (&vo)[D / 16], int sb, int n1, int g,
                                             typename Pv<F16>::T ones) {
@@ -364,7 +384,7 @@ __device__ __forceinline__ void encode_step(EncodeState<D, MBW>& st, const __bf1
 #pragma unroll
   for (int i = 0; i < MBW; ++i) {
     f32x4 s0, s1;
-    block_logits<D, MBW, EXQ>(st, i, k0, k1, s0, s1);
+    block_logits<D, MBW, LQ>(st, i, k0, k1, s0, s1);
     mask(s0, s1);
     if (ONLINE) {
       const float lm = fmaxf(max3(s1[2], s1[3], max3(s0[3], s1[0], max3(s0[0], s0[1], s0[2]))), s1[1]);
@@ -374,7 +394,7 @@ __device__ __forceinline__ void encode_step(EncodeState<D, MBW>& st, const __bf1
         const float al = fast_exp2(-d);
 #pragma unroll
         for (int db = 0; db <= DB; ++db) st.acc[db][i] *= al;
-        block_logits<D, MBW, EXQ>(st, i, k0, k1, s0, s1);
+        block_logits<D, MBW, LQ>(st, i, k0, k1, s0, s1);
         mask(s0, s1);
       }
     }
@@ -439,19 +459,25 @@ constexpr uint32_t kEncWaitLgkm0 = 0xF | (0x7 << 4) | (0x3 << 14);
 //     right after the barrier that opens it, and rewritten (for tile u + 2)
 //     only after the next barrier.
 //   F16: the fp16 conversion of its value chunks, in place.
+//   KF16: the fp16 conversion of its key chunks, in place (after TNORM's
+//     norms, which read the bf16 keys; the two are not combined).
 // It runs in ring_open, after the wave's wait for its loads of tile u.
-template <int D, int NW, int I, bool TNORM, bool F16>
+template <int D, int NW, int I, bool TNORM, bool F16, bool KF16>
 __device__ __forceinline__ void tile_prep(__bf16* ring, float* sKm, int u, int wave, int lane) {
   typedef Ring<D, NW> R;
+  static_assert(!(TNORM && KF16), "key norms read the bf16 keys");
   if (F16) {
 #pragma unroll
     for (int i = 0; i < R::DI; ++i) {
       __bf16* c = R::template v<I>(ring) + (wave * R::DI + i) * 512 + 8 * lane;
-      const bf16x8 x = *reinterpret_cast<const bf16x8*>(c);
-      f16x8 y;
+      *reinterpret_cast<f16x8*>(c) = to_f16<f16x8>(*reinterpret_cast<const bf16x8*>(c));
+    }
+  }
+  if (KF16) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = (_Float16)(float)x[e];
-      *reinterpret_cast<f16x8*>(c) = y;
+    for (int i = 0; i < R::DI; ++i) {
+      __bf16* c = R::template k<I>(ring) + (wave * R::DI + i) * 512 + 8 * lane;
+      *reinterpret_cast<f16x8*>(c) = to_f16<f16x8>(*reinterpret_cast<const bf16x8*>(c));
     }
   }
   if (TNORM) {
@@ -460,13 +486,13 @@ __device__ __forceinline__ void tile_prep(__bf16* ring, float* sKm, int u, int w
   }
 }
 
-template <int D, int NW, int I, bool TNORM, bool F16>
+template <int D, int NW, int I, bool TNORM, bool F16, bool KF16>
 __device__ __forceinline__ float ring_open(__bf16* ring, float* sKm, const __bf16* Kp, const __bf16* Vp, int u,
                                            int n0, int n1, bool more, int wave, int lane) {
   typedef Ring<D, NW> R;
   FLAREPP_WAIT_VM(0);
   float* slot = sKm + (u & 1) * NW;
-  tile_prep<D, NW, I, TNORM, F16>(ring, sKm, u, wave, lane);
+  tile_prep<D, NW, I, TNORM, F16, KF16>(ring, sKm, u, wave, lane);
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(kEncWaitLgkm0);  // this wave's LDS accesses are done before the barrier
   ring_barrier();
@@ -503,14 +529,15 @@ __device__ __forceinline__ bool tile_needs_check(const EncodeState<D, MBW>& st, 
 // Tile t in slot I: open it (except tile 0, opened before the running max
 // is seeded), then its steps.  With TNORM, km2 is the largest squared key
 // norm of tile t once it is open.
-template <int D, int NW, int MBW, bool F16, bool KNORM, bool ONLINE, bool SKIP, bool EXQ, int I>
+template <int D, int NW, int MBW, bool F16, bool KNORM, bool ONLINE, bool SKIP, int LQ, int I>
 __device__ __forceinline__ void encode_tile(EncodeState<D, MBW>& st, __bf16* ring, float* sKm, const __bf16* Kp,
                                             const __bf16* Vp, int t, int ntiles, int n0, int n1, int wave, int lane,
                                             bool wave_active, int g, int ko, const int (&vo)[D / 16],
                                             typename Pv<F16>::T ones, float& km2, float& kn2) {
   typedef Ring<D, NW> R;
   constexpr bool TNORM = KNORM || (ONLINE && SKIP);
-  if (t > 0) km2 = ring_open<D, NW, I, TNORM, F16>(ring, sKm, Kp, Vp, t, n0, n1, t + 1 < ntiles, wave, lane);
+  if (t > 0)
+    km2 = ring_open<D, NW, I, TNORM, F16, LQ == kF16>(ring, sKm, Kp, Vp, t, n0, n1, t + 1 < ntiles, wave, lane);
   if (KNORM) kn2 = fmaxf(kn2, km2);
   if (!wave_active) return;
   const int tb = n0 + t * R::TN;
@@ -521,19 +548,19 @@ __device__ __forceinline__ void encode_tile(EncodeState<D, MBW>& st, __bf16* rin
   if (ONLINE && (!SKIP || tile_needs_check<D, MBW>(st, km2))) {
 #pragma unroll 1
     for (int ks = 0; ks < full; ++ks)
-      encode_step<D, MBW, F16, true, false, EXQ>(st, sK, sV, ks, ko, vo, tb + 32 * ks, n1, g, ones);
-    if (full < nsteps) encode_step<D, MBW, F16, true, true, EXQ>(st, sK, sV, full, ko, vo, tb + 32 * full, n1, g, ones);
+      encode_step<D, MBW, F16, true, false, LQ>(st, sK, sV, ks, ko, vo, tb + 32 * ks, n1, g, ones);
+    if (full < nsteps) encode_step<D, MBW, F16, true, true, LQ>(st, sK, sV, full, ko, vo, tb + 32 * full, n1, g, ones);
   } else {
 #pragma unroll 1
     for (int ks = 0; ks < full; ++ks)
-      encode_step<D, MBW, F16, false, false, EXQ>(st, sK, sV, ks, ko, vo, tb + 32 * ks, n1, g, ones);
-    if (full < nsteps) encode_step<D, MBW, F16, false, true, EXQ>(st, sK, sV, full, ko, vo, tb + 32 * full, n1, g, ones);
+      encode_step<D, MBW, F16, false, false, LQ>(st, sK, sV, ks, ko, vo, tb + 32 * ks, n1, g, ones);
+    if (full < nsteps) encode_step<D, MBW, F16, false, true, LQ>(st, sK, sV, full, ko, vo, tb + 32 * full, n1, g, ones);
   }
 }
 
 // SKIP: the online path applies the tile rule (tile_needs_check); otherwise
 // every step of the online path checks.
-template <int D, int NW, int MBW, bool F16, bool KNORM, bool ONLINE, bool SKIP, bool EXQ>
+template <int D, int NW, int MBW, bool F16, bool KNORM, bool ONLINE, bool SKIP, int LQ>
 __device__ __forceinline__ void encode_tiles(EncodeState<D, MBW>& st, __bf16* ring, float* sKm, const __bf16* Kp,
                                              const __bf16* Vp, int n0, int n1, int wave, int lane,
                                              bool wave_active, int g, int c16, float& kn2) {
@@ -557,7 +584,7 @@ __device__ __forceinline__ void encode_tiles(EncodeState<D, MBW>& st, __bf16* ri
   for (int db = 0; db < DB; ++db) vo[db] = slot_off<D>(4 * g + (c16 >> 2), 16 * db + 4 * (c16 & 3));
 
   tile_dma<D, NW, 0>(ring, Kp, Vp, n0, n1, wave, lane);
-  float km2 = ring_open<D, NW, 0, TNORM, F16>(ring, sKm, Kp, Vp, 0, n0, n1, ntiles > 1, wave, lane);
+  float km2 = ring_open<D, NW, 0, TNORM, F16, LQ == kF16>(ring, sKm, Kp, Vp, 0, n0, n1, ntiles > 1, wave, lane);
   if (wave_active && ONLINE) {
     // the running max starts at the exact column max of the first step
     // (the shift is still zero here)
@@ -566,7 +593,7 @@ __device__ __forceinline__ void encode_tiles(EncodeState<D, MBW>& st, __bf16* ri
 #pragma unroll
     for (int i = 0; i < MBW; ++i) {
       f32x4 s0, s1;
-      block_logits<D, MBW, EXQ>(st, i, k0, k1, s0, s1);
+      block_logits<D, MBW, LQ>(st, i, k0, k1, s0, s1);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if (n0 + 4 * g + r >= n1) s0[r] = -INFINITY;
@@ -577,10 +604,10 @@ __device__ __forceinline__ void encode_tiles(EncodeState<D, MBW>& st, __bf16* ri
     }
   }
   for (int t = 0; t < ntiles; t += 2) {
-    encode_tile<D, NW, MBW, F16, KNORM, ONLINE, SKIP, EXQ, 0>(st, ring, sKm, Kp, Vp, t, ntiles, n0, n1, wave, lane, wave_active,
+    encode_tile<D, NW, MBW, F16, KNORM, ONLINE, SKIP, LQ, 0>(st, ring, sKm, Kp, Vp, t, ntiles, n0, n1, wave, lane, wave_active,
                                                           g, ko, vo, ones, km2, kn2);
     if (t + 1 >= ntiles) break;
-    encode_tile<D, NW, MBW, F16, KNORM, ONLINE, SKIP, EXQ, 1>(st, ring, sKm, Kp, Vp, t + 1, ntiles, n0, n1, wave, lane,
+    encode_tile<D, NW, MBW, F16, KNORM, ONLINE, SKIP, LQ, 1>(st, ring, sKm, Kp, Vp, t + 1, ntiles, n0, n1, wave, lane,
                                                           wave_active, g, ko, vo, ones, km2, kn2);
   }
   // the ring's trailing loads must land before the workgroup's LDS is released
@@ -655,7 +682,24 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 4 : 2) void encode_split_bf16(En
       for (int db = 0; db <= DB; ++db) st.acc[db][i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
-  const bool online = __any(need_online);
+  // The route's bounded encode: the head's logit bound mu_g (the same rule
+  // and inputs as the decode's) picks the fp16 logit form for the whole
+  // workgroup (every wave reads the same norms).  Within it every latent's
+  // bound is at most mu_g <= 16, so no wave needs the online path.
+  bool q16 = false;
+  if constexpr (BOUNDED) {
+    if (a.kin && a.qnorm && a.bias) {
+      float k2 = 0.0f;
+      for (int jj = lane; jj < a.Jk; jj += 64) k2 = fmaxf(k2, a.kin[lbh * a.Jk + jj]);
+      const float kmax = __builtin_sqrtf(wave_max(k2));
+      const int64_t qo = (int64_t)b * a.q_sb + (int64_t)h * a.q_sh - a.q_off;
+      float qmax = 0.0f;
+      for (int m = lane; m < a.Mp; m += 64) qmax = fmaxf(qmax, a.qnorm[qo / D + m]);
+      qmax = wave_max(qmax);
+      q16 = f16_logits(fabsf(a.qc) * kmax * qmax * (1.0f + 1.0f / 4096.0f), kmax, qmax, a.qc);
+    }
+  }
+  const bool online = __any(need_online) && !q16;
 #pragma unroll
   for (int i = 0; i < MBW; ++i)
     if (online) st.mu[i] = 0.0f;
@@ -663,12 +707,23 @@ __global__ __launch_bounds__(64 * NW, NW == 8 ? 4 : 2) void encode_split_bf16(En
   // the operand loads above must not be counted with the ring's loads
   FLAREPP_WAIT_VM(0);
 
-  if (!BOUNDED || online)
-    encode_tiles<D, NW, MBW, F16, KNORM, true, !BOUNDED, EXQ>(st, ring, sKm, Kp, Vp, n0, n1, wave, lane, wave_active, g,
-                                                          c16, kn2);
-  else
-    encode_tiles<D, NW, MBW, false, KNORM, false, false, EXQ>(st, ring, sKm, Kp, Vp, n0, n1, wave, lane, wave_active, g,
-                                                          c16, kn2);
+  constexpr int LQ = EXQ ? kExact : kHiLo;
+  if (!BOUNDED || online) {
+    encode_tiles<D, NW, MBW, F16, KNORM, true, !BOUNDED, LQ>(st, ring, sKm, Kp, Vp, n0, n1, wave, lane, wave_active, g,
+                                                         c16, kn2);
+  } else if constexpr (BOUNDED) {
+    if (q16) {
+      // c Q as fp16 in the hi slot (hi + lo is exact in float32, rounded once)
+#pragma unroll
+      for (int i = 0; i < MBW; ++i)
+        st.qh[i] = __builtin_bit_cast(kop_t, to_f16<typename KOperand16<D>::T>(st.qh[i], st.ql[i]));
+      encode_tiles<D, NW, MBW, false, KNORM, false, false, kF16>(st, ring, sKm, Kp, Vp, n0, n1, wave, lane,
+                                                                wave_active, g, c16, kn2);
+    } else {
+      encode_tiles<D, NW, MBW, false, KNORM, false, false, LQ>(st, ring, sKm, Kp, Vp, n0, n1, wave, lane, wave_active,
+                                                           g, c16, kn2);
+    }
+  }
 
   // ---- partial records
   if (wave_active) {

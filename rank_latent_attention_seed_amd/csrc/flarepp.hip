@@ -604,6 +604,12 @@ flarepp_status run(const Plan& p, Stage stage, const void* S, const float* Qd_in
         e.q_sh = MpD;
         e.q_off = g0 * MpD;
         e.bias = routed ? at<float>(ws, p.o_bias) : nullptr;
+        if (stage == kRoute) {  // the head's logit bound may pick fp16 logits (f16_logits)
+          e.kin = at<float>(ws, p.o_knorm);
+          e.Jk = p.J;
+          e.qnorm = qnorm;
+          e.qc = p.c;
+        }
         if (routed)
           FLAREPP_TRY((run_encode_bf16<D, false, true, false>(p, e, Gc, st, rec, FLAREPP_KERNEL_ENCODE)));
         else
