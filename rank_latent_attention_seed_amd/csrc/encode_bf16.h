@@ -208,6 +208,15 @@ __device__ __forceinline__ void dma16(const __bf16* src, const __bf16* lds_base)
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory");
 }
 
+// The same load from a wave-uniform base (an SGPR pair) plus a 32-bit byte
+// offset per lane: a tile's lane offsets are the same for every tile of a
+// split (only the base moves), so they cost no per-tile address arithmetic.
+__device__ __forceinline__ void dma16s(const __bf16* base, uint32_t off, const __bf16* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(m0) : "memory");
+}
+
 // Issue the direct-to-LDS loads of one tile into slot I: the NW waves split
 // the tile's 16-byte chunks of K and of V (instructions of 1 KB each); lane l
 // of an instruction fills LDS chunk base + 16 l and therefore fetches the
@@ -219,15 +228,21 @@ __device__ __forceinline__ void tile_dma(__bf16* ring, const __bf16* Kp, const _
                                          int wave, int lane) {
   typedef Ring<D, NW> R;
   constexpr int U = D / 8;
+  // the tile's first row as the (uniform) base; rows past the split clamp
+  // to its last row only in a split's last, partial tile
+  const int64_t base = (int64_t)__builtin_amdgcn_readfirstlane(tb) * D;
+  const int last = __builtin_amdgcn_readfirstlane(n1 - 1 - tb);
+  const bool partial = last < R::TN - 1;
 #pragma unroll
   for (int i = 0; i < R::DI; ++i) {
     const int blk = wave * R::DI + i;
     const int s = blk * 64 + lane;
     const int t = s / U;
     const int u = (s % U) ^ chunk_swz<D>(t);
-    const int64_t src = (int64_t)min(tb + t, n1 - 1) * D + 8 * u;
-    dma16(Kp + src, R::template k<I>(ring) + blk * 512);
-    dma16(Vp + src, R::template v<I>(ring) + blk * 512);
+    const int row = partial ? min(t, last) : t;
+    const uint32_t off = (uint32_t)(row * D + 8 * u) * 2u;
+    dma16s(Kp + base, off, R::template k<I>(ring) + blk * 512);
+    dma16s(Vp + base, off, R::template v<I>(ring) + blk * 512);
   }
 }
 
