@@ -124,7 +124,8 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
 
 // Single-product logits.  The keys are exact in fp16 as well as in bf16 when
 // |k| < 2^10 (bf16's 8-bit significand fits fp16's 11 bits; below fp16's
-// normal range a key moves by at most 2^-25).  Rounding c Qd to fp16 moves
+// normal range a key moves by at most 2^-25: these kernels run with 16-bit
+// denormals kept, float_denorm_mode_16_64 = 3, so nothing flushes to zero).  Rounding c Qd to fp16 moves
 // each product term by at most 2^-11 of itself, so a logit by at most
 // 2^-11 |c| ||Qd_m|| ||K_n|| <= 2^-11 mu_g (Cauchy-Schwarz), where
 // mu_g = |c| max_n ||K_n|| max_m ||Qd_m|| is the head's logit bound.  With
