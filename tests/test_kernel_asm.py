@@ -99,3 +99,19 @@ def test_encode_fits_four_waves_per_simd(device_asm):
                 over.append(name)
     assert seen >= 6, seen
     assert not over, over[:3]
+
+
+def test_16bit_denormals_kept(device_asm):
+    # the fp16 logit products take keys and c * Qd down to fp16's subnormal
+    # range; their error bound assumes that nothing there flushes to zero
+    modes = [l.split()[1] for l in device_asm if l.startswith(".amdhsa_float_denorm_mode_16_64")]
+    assert modes, "expected kernel descriptors"
+    assert set(modes) == {"3"}, f"16/64-bit denormal modes {sorted(set(modes))}"
+
+
+def test_fp16_logit_forms_present(device_asm):
+    # the route's stage-2 encode and paired decode carry the single fp16
+    # logit product (v_mfma_f32_16x16x32_f16 on the key operand)
+    assert any(l.startswith("v_mfma_f32_16x16x32_f16") for l in device_asm)
+    names = [l[:-1] for l in device_asm if l.endswith(":") and "decode_pair_bf16" in l and not l.startswith(".")]
+    assert any("Lb1EEEvNS_10DecodeArgsE" in n for n in names), "no fp16-logit paired decode"
