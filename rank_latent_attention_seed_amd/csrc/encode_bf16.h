@@ -231,7 +231,7 @@ __device__ __forceinline__ void tile_dma(__bf16* ring, const __bf16* Kp, const _
   // the tile's first row as the (uniform) base; rows past the split clamp
   // to its last row only in a split's last, partial tile
   const int64_t base = (int64_t)__builtin_amdgcn_readfirstlane(tb) * D;
-  const int last = __builtin_amdgcn_readfirstlane(n1 - 1 - tb);
+  const int last = max(__builtin_amdgcn_readfirstlane(n1 - 1 - tb), 0);  // a tile starts before n1
   const bool partial = last < R::TN - 1;
 #pragma unroll
   for (int i = 0; i < R::DI; ++i) {
