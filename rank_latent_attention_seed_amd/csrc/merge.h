@@ -120,6 +120,47 @@ __device__ __forceinline__ float group_max(float x) {
   return x;
 }
 
+// Sums over the 64 lanes of a wave of 32 values per lane, every lane getting
+// all 32 sums: two halving steps (each lane pair swaps half its values
+// through a permlane swap and keeps the sums of the other half: 16, then 8
+// values left, lane l holding elements 8 (l / 16) .. + 7 summed over the
+// lanes l, l ^ 16, l ^ 32, l ^ 48), an all-reduce of those 8 within each
+// 16-lane row (DPP), and a gather of the four rows' results through the same
+// swaps: about 100 VALU instructions where 32 separate wave sums take ~300.
+__device__ __forceinline__ void wave_sum32(float (&v)[32]) {
+  auto f = [](uint32_t u) { return __uint_as_float(u); };
+  auto u = [](float x) { return __float_as_uint(x); };
+  float h[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {  // lanes < 32 keep element i, lanes >= 32 element i + 16
+    const auto t = __builtin_amdgcn_permlane32_swap(u(v[i]), u(v[i + 16]), false, false);
+    h[i] = f(t[0]) + f(t[1]);
+  }
+  float r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {  // then rows 0 / 2 keep h[i], rows 1 / 3 h[i + 8]
+    const auto t = __builtin_amdgcn_permlane16_swap(u(h[i]), u(h[i + 8]), false, false);
+    r[i] = f(t[0]) + f(t[1]);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {  // row r: element 8 r + i, summed over its 16 lanes
+    r[i] += dpp<0xB1>(r[i]);
+    r[i] += dpp<0x4E>(r[i]);
+    r[i] += dpp<0x124>(r[i]);
+    r[i] += dpp<0x128>(r[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const auto p = __builtin_amdgcn_permlane16_swap(u(r[i]), u(r[i]), false, false);  // rows 2k, 2k + 1
+    const auto a = __builtin_amdgcn_permlane32_swap(p[0], p[0], false, false);        // rows 0, 2
+    const auto b = __builtin_amdgcn_permlane32_swap(p[1], p[1], false, false);        // rows 1, 3
+    v[i] = f(a[0]);
+    v[16 + i] = f(a[1]);
+    v[8 + i] = f(b[0]);
+    v[24 + i] = f(b[1]);
+  }
+}
+
 // One latent row per group of T threads (T = 64 for many splits: one row per
 // wave).  Thread q of a row folds splits q, q + T, ...: a first sweep over
 // the maxima only, then the weighted sums, each unrolled so that its loads are
@@ -135,34 +176,64 @@ __global__ __launch_bounds__(256) void merge_partials(MergeArgs a) {
   const int64_t lbh = blockIdx.y, bh = a.bh0 + lbh;
   const bool row_ok = m < a.Mp;
   float* base = a.part + ((lbh * a.Mp + (row_ok ? m : 0)) * (int64_t)a.J) * PS;
-  if (a.fK && row_ok)
-    for (int jj = q; jj < a.J; jj += T)
-      if (!(base[(int64_t)jj * PS + D] <= 3.0e38f)) refit_record<D>(a, bh, m, jj, base + (int64_t)jj * PS);
+  float mx, den, x[D];
+  if (D == 32 && T == 64 && a.J <= 64) {
+    // one record per lane, read in one pass (a record whose sum is not finite
+    // is recomputed, then read again), weighted, then reduced by wave_sum32
+    const bool has = row_ok && q < a.J;
+    float* rec = base + (int64_t)q * PS;
+    f32x4 rv[D / 4], tail = f32x4{0.f, -INFINITY, 0.f, 0.f};
+#pragma unroll
+    for (int d4 = 0; d4 < D / 4; ++d4) rv[d4] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto load = [&]() {
+#pragma unroll
+      for (int d4 = 0; d4 < D / 4; ++d4) rv[d4] = *reinterpret_cast<const f32x4*>(rec + 4 * d4);
+      tail = *reinterpret_cast<const f32x4*>(rec + D);
+    };
+    if (has) {
+      load();
+      if (a.fK && !(tail[0] <= 3.0e38f)) {
+        refit_record<D>(a, bh, m, q, rec);
+        load();
+      }
+    }
+    mx = wave_max(tail[1]);
+    const float w = has ? fast_exp2(tail[1] - mx) : 0.0f;
+    den = wave_sum(w * tail[0]);
+#pragma unroll
+    for (int d4 = 0; d4 < D / 4; ++d4)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * d4 + e] = w * rv[d4][e];
+    if constexpr (D == 32) wave_sum32(x);
+  } else {
+    if (a.fK && row_ok)
+      for (int jj = q; jj < a.J; jj += T)
+        if (!(base[(int64_t)jj * PS + D] <= 3.0e38f)) refit_record<D>(a, bh, m, jj, base + (int64_t)jj * PS);
 
-  float mx = -INFINITY;
+    mx = -INFINITY;
 #pragma unroll 8
-  for (int jj = q; jj < a.J; jj += T) mx = fmaxf(mx, base[(int64_t)jj * PS + D + 1]);
-  mx = group_max<T>(mx);
+    for (int jj = q; jj < a.J; jj += T) mx = fmaxf(mx, base[(int64_t)jj * PS + D + 1]);
+    mx = group_max<T>(mx);
 
-  float den = 0.0f;
-  f32x4 num[D / 4];
+    den = 0.0f;
+    f32x4 num[D / 4];
 #pragma unroll
-  for (int d4 = 0; d4 < D / 4; ++d4) num[d4] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int d4 = 0; d4 < D / 4; ++d4) num[d4] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
-  for (int jj = q; jj < a.J; jj += T) {
-    const float* rec = base + (int64_t)jj * PS;
-    const f32x4 tail = *reinterpret_cast<const f32x4*>(rec + D);
-    const float w = fast_exp2(tail[1] - mx);
-    den += w * tail[0];
+    for (int jj = q; jj < a.J; jj += T) {
+      const float* rec = base + (int64_t)jj * PS;
+      const f32x4 tl = *reinterpret_cast<const f32x4*>(rec + D);
+      const float w = fast_exp2(tl[1] - mx);
+      den += w * tl[0];
 #pragma unroll
-    for (int d4 = 0; d4 < D / 4; ++d4) num[d4] += w * *reinterpret_cast<const f32x4*>(rec + 4 * d4);
+      for (int d4 = 0; d4 < D / 4; ++d4) num[d4] += w * *reinterpret_cast<const f32x4*>(rec + 4 * d4);
+    }
+    den = group_sum<T>(den);
+#pragma unroll
+    for (int d4 = 0; d4 < D / 4; ++d4)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * d4 + e] = group_sum<T>(num[d4][e]);
   }
-  den = group_sum<T>(den);
-  float x[D];
-#pragma unroll
-  for (int d4 = 0; d4 < D / 4; ++d4)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) x[4 * d4 + e] = group_sum<T>(num[d4][e]);
 
   if (a.rec_out) {
     if (!row_ok) return;
