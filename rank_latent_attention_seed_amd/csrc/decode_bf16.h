@@ -236,7 +236,11 @@ __global__ __launch_bounds__(256, 1) void decode_bf16(DecodeArgs a) {
   // store nothing), so the loop has a single steady state.
   constexpr int S = 64;
   int blk = n0 + wave * 16;
-  kop_t k0 = kload(blk), k1 = kload(blk + S), k2;
+  // k0 is issued before k1 (kept in that order), so that the loop's first
+  // wait for k0 leaves k1 in flight on the entry path as on the back edge
+  kop_t k0 = kload(blk);
+  __builtin_amdgcn_sched_barrier(0);
+  kop_t k1 = kload(blk + S), k2;
   for (; blk < n1; blk += 3 * S) {
     k2 = kload(blk + 2 * S);
     body(k0, blk);
@@ -467,7 +471,11 @@ __global__ __launch_bounds__(128, Q16 ? 4 : 2) void decode_pair_bf16(DecodeArgs 
   // two more for the exchange buffer's parity
   constexpr int S = 16;
   int blk = n0;
-  kop_t k0 = kload(blk), k1 = kload(blk + S), k2;
+  // k0 is issued before k1 (kept in that order), so that the loop's first
+  // wait for k0 leaves k1 in flight on the entry path as on the back edge
+  kop_t k0 = kload(blk);
+  __builtin_amdgcn_sched_barrier(0);
+  kop_t k1 = kload(blk + S), k2;
   for (int it = 0; blk < n1; blk += 3 * S, ++it) {
     const int par = it & 1;  // blocks 3 it .. 3 it + 2 use buffers par, !par, par
     k2 = kload(blk + 2 * S);
