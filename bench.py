@@ -345,6 +345,52 @@ def backward_record(fp, torch, r: Route, steps: int, route_ms: float) -> dict:
                          "unit": "TFLOP/s", "frac": round(btf / peak, 4), "traffic": None},
         }
         del bws, dS, dK, dV
+    # the training step with the forward kept for the backward: flarepp_route_save
+    # (the route with the backward's forward stages, saving Qd, Z and the two
+    # log-sum-exps), then flarepp_route_backward_saved (no recomputed forward)
+    if p.dtype == "bf16" and p.M <= 256:
+        bdesc = fp.desc_for(r.S, r.K, p.scale)
+        bbytes = fp.flarepp_workspace_size(bdesc, fp.OP_ROUTE_BACKWARD)
+        bws = torch.empty(max(bbytes, 1), dtype=torch.uint8, device="cuda")
+        Y = torch.empty(r.K.shape, dtype=torch.float32, device="cuda")
+        Qd = torch.empty((p.B, p.H, p.M, p.D), dtype=torch.float32, device="cuda")
+        Z = torch.empty_like(Qd)
+        lse = torch.empty(fp.saved_lse_count(bdesc), dtype=torch.float32, device="cuda")
+        dS = torch.empty(r.S.shape, dtype=torch.float32, device="cuda")
+        dK = torch.empty(r.K.shape, dtype=torch.float32, device="cuda")
+        dV = torch.empty(r.K.shape, dtype=torch.float32, device="cuda")
+
+        def fstep():
+            st = fp.flarepp_route_save(bdesc, r.S.data_ptr(), r.K.data_ptr(), r.V.data_ptr(), Y.data_ptr(),
+                                       Qd.data_ptr(), Z.data_ptr(), lse.data_ptr(), bws.data_ptr(), bbytes, r.stream)
+            if st != 0:
+                raise fp.FlareppError(st, "flarepp_route_save")
+
+        def gstep():
+            st = fp.flarepp_route_backward_saved(bdesc, r.S.data_ptr(), r.K.data_ptr(), r.V.data_ptr(),
+                                                 Qd.data_ptr(), Z.data_ptr(), lse.data_ptr(), dY.data_ptr(),
+                                                 dS.data_ptr(), dK.data_ptr(), dV.data_ptr(), bws.data_ptr(),
+                                                 bbytes, r.stream)
+            if st != 0:
+                raise fp.FlareppError(st, "flarepp_route_backward_saved")
+
+        fstep()
+        gstep()
+        torch.cuda.synchronize()
+        fms = statistics.median(time_steps(fstep, torch, r.stream, steps))
+        gms = statistics.median(time_steps(gstep, torch, r.stream, steps))
+        gtf = flops / (gms * 1e-3) / 1e12
+        log(f"[bench] saved forward {fms:.2f} ms + backward (bf16, saved) {gms:.2f} ms = {fms + gms:.2f} ms "
+            f"per training step (route + recomputing backward: {route_ms + out['bf16']['ms_per_step']:.2f} ms); "
+            f"backward {gms / route_ms:.2f} x the forward route")
+        out["bf16_saved"] = {
+            "ops": "flarepp_route_save + flarepp_route_backward_saved",
+            "route_save_ms": fms, "backward_ms": gms, "training_step_ms": fms + gms,
+            "over_forward_route": round(gms / route_ms, 3),
+            "roofline": {"bound": "mfma", "achieved": round(gtf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(gtf / BF16_PEAK_TFLOPS, 4), "traffic": None},
+        }
+        del bws, Y, Qd, Z, lse, dS, dK, dV
     return out
 
 

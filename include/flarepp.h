@@ -189,6 +189,35 @@ flarepp_status flarepp_route_backward(const flarepp_desc *desc, const void *S, c
                                       float *dV, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * The training step without the recomputed forward: flarepp_route_save runs
+ * the route with the backward's own forward stages 1 and 2 (c S and c Qd as
+ * bf16 hi/lo operands, the logits the backward's passes take) and keeps
+ * what the backward needs; flarepp_route_backward_saved takes those instead
+ * of recomputing them.  The pair gives the gradients of
+ * flarepp_route_backward up to the rounding of the latent norms (the saved
+ * path recomputes ||Qd_m|| from the float32 Qd), and the forward's Y of
+ * flarepp_route up to its query operands (hi/lo seeds here, exact seeds
+ * there).  Chain rule and the pages' per-step cost: as flarepp_route_backward.
+ *   Y, Qd_out, Z_out (outputs of flarepp_route_save): as flarepp_route's,
+ *     all required.
+ *   lse_out / lse: the log-sum-exp (log2 units) of the two encodes' softmax
+ *     rows, float32 [2][B x H][Mp] with Mp = 16 * ceil(M / 16) (rows M ..
+ *     Mp - 1 are written and read back as they are), 2 * B * H * Mp floats.
+ * bf16 only (FLAREPP_F32: FLAREPP_UNSUPPORTED), M <= 256.  Workspace (both
+ * calls): flarepp_workspace_size with FLAREPP_OP_ROUTE_BACKWARD; the saved
+ * buffers are the caller's and pass nothing through the workspace.  Outputs
+ * must not overlap the inputs, each other or the workspace.
+ */
+flarepp_status flarepp_route_save(const flarepp_desc *desc, const void *S, const void *K,
+                                  const void *V, float *Y, float *Qd_out, float *Z_out,
+                                  float *lse_out, void *ws, size_t ws_bytes, void *stream);
+flarepp_status flarepp_route_backward_saved(const flarepp_desc *desc, const void *S,
+                                            const void *K, const void *V, const float *Qd,
+                                            const float *Z, const float *lse, const float *dY,
+                                            float *dS, float *dK, float *dV, void *ws,
+                                            size_t ws_bytes, void *stream);
+
+/*
  * Spectrum of each head's mixing matrix W = W_dec W_enc (N x N, rank <= M):
  * its nonzero eigenvalues are those of the M x M product W_enc W_dec, where
  * W_enc = softmax over tokens of s Qd K^T (the encode weights) and W_dec =

@@ -219,6 +219,7 @@ Plan make_plan(const flarepp_desc* d, int op, const flarepp_tuning* t = nullptr)
     p.o_dzl = take(G_ * opnd);
     p.o_dqr = take(G_ * opnd);
     p.o_dql = take(G_ * opnd);
+    p.o_zt = take(G_ * opnd);  // the decode of flarepp_route_save
   } else if (bwd) {
     p.o_part = take(G_ * p.J * Mp * std::max<size_t>(D + 4, 2 * D) * 4);
     p.o_qf = take(G_ * p.M * D * 4);
@@ -896,14 +897,71 @@ flarepp_status run_backward(const Plan& p, const float* S, const float* K, const
   return FLAREPP_OK;
 }
 
+// The forward stages 1 and 2 of the backward (and of flarepp_route_save) for
+// one launch group: the seed encode with c S as the bf16 hi/lo operand that
+// the backward's stage-1 passes also take, merge (Qd to qd_out, staged c Qd
+// hi/lo operands, norms, bounds, stage 1's log-sum-exp), the encode with the
+// hi/lo query (the backward's stage-2 logits), merge (Z to z_out, its
+// log-sum-exp, and Z^T for a decode when zt is set).
+template <int D>
+flarepp_status forward_for_backward(const Plan& p, const void* K, const void* V, void* ws, int64_t g0, int Gc,
+                                    float* qd_out, float* qd_stage, float* z_out, float* z_stage, float* lse1,
+                                    float* lse2, __bf16* zt, hipStream_t st, Recorder& rec) {
+  const int64_t MpD = (int64_t)p.Mp * D;
+  EncodeArgs e = encode_args(p, ws, K, V, g0);
+  e.q_hi = at<__bf16>(ws, p.o_shi);
+  e.q_lo = at<__bf16>(ws, p.o_slo);
+  e.q_sb = 0;
+  e.q_sh = p.nS > 1 ? MpD : 0;
+  e.q_off = 0;
+  e.knorm = at<float>(ws, p.o_knorm);
+  FLAREPP_TRY((run_encode_bf16<D, true, false, false>(p, e, Gc, st, rec, FLAREPP_KERNEL_SEED_ENCODE)));
+  MergeArgs m = merge_args(p, ws, g0);
+  refit_from(m, e);
+  m.out = qd_out;
+  m.outl = qd_stage;
+  m.op_hi = at<__bf16>(ws, p.o_qhi);
+  m.op_lo = at<__bf16>(ws, p.o_qlo);
+  m.qnorm = at<float>(ws, p.o_qnorm);
+  m.knorm = e.knorm;
+  m.Jk = p.J;
+  m.bias = at<float>(ws, p.o_bias);
+  m.lse = lse1;
+  FLAREPP_TRY(run_merge<D>(p, m, Gc, st, rec));
+  EncodeArgs e2 = encode_args(p, ws, K, V, g0);
+  e2.q_hi = m.op_hi;
+  e2.q_lo = m.op_lo;
+  e2.q_sb = (int64_t)p.H * MpD;
+  e2.q_sh = MpD;
+  e2.q_off = g0 * MpD;
+  e2.bias = m.bias;
+  FLAREPP_TRY((run_encode_bf16<D, false, true, false>(p, e2, Gc, st, rec, FLAREPP_KERNEL_ENCODE)));
+  MergeArgs m2 = merge_args(p, ws, g0);
+  m2.out = z_out;
+  m2.outl = z_stage;
+  m2.lse = lse2;
+  m2.op_zt = zt;
+  return run_merge<D>(p, m2, Gc, st, rec);
+}
+
 // Backward of the route (bf16 inputs, matrix cores): the forward's stages 1
-// and 2 as the route runs them, keeping Qd, Z and the log-sum-exp of both
-// encodes; then per stage in reverse order the token pass (dK, dV), the
-// latent pass (split partials) and their reduction, with the latent
-// operands of each stage converted to bf16 rows and transposes first.
+// and 2 (forward_for_backward), keeping Qd, Z and the log-sum-exp of both
+// encodes, or those of a saved forward; then per stage in reverse order the
+// token pass (dK, dV), the latent pass (split partials) and their
+// reduction, with the latent operands of each stage converted to bf16 rows
+// and transposes first.
+// saved (flarepp_route_backward_saved): Qd, Z and both log-sum-exps from
+// flarepp_route_save instead of recomputing stages 1 and 2; null otherwise.
+struct SavedForward {
+  const float* Qd;   // [BH][M][D]
+  const float* Z;    // [BH][M][D]
+  const float* lse;  // [2][BH][Mp]
+};
+
 template <int D>
 flarepp_status run_backward_bf16(const Plan& p, const void* S, const void* K, const void* V, const float* dY,
-                                 float* dS, float* dK, float* dV, void* ws, hipStream_t st) {
+                                 float* dS, float* dK, float* dV, void* ws, hipStream_t st,
+                                 const SavedForward* saved = nullptr) {
   Recorder rec;
   const int64_t MD = (int64_t)p.M * D, MpD = (int64_t)p.Mp * D;
   const int64_t seed_h = p.nS > 1 ? MD : 0;
@@ -913,8 +971,6 @@ flarepp_status run_backward_bf16(const Plan& p, const void* S, const void* K, co
   __bf16* slo = at<__bf16>(ws, p.o_slo);
   __bf16* qhi = at<__bf16>(ws, p.o_qhi);
   __bf16* qlo = at<__bf16>(ws, p.o_qlo);
-  float* qf = at<float>(ws, p.o_qf);
-  float* zf = at<float>(ws, p.o_zf);
   float* part = at<float>(ws, p.o_part);
   float* dz = at<float>(ws, p.o_dz);
   float* dq3 = at<float>(ws, p.o_dq3);
@@ -936,42 +992,26 @@ flarepp_status run_backward_bf16(const Plan& p, const void* S, const void* K, co
   FLAREPP_TRY(run_prep<D>(p, S, true, 0, seed_h, p.nS, shi, slo, nullptr, nullptr, p.c, st, rec));
   for (int64_t g0 = 0; g0 < p.BH; g0 += p.G) {
     const int Gc = (int)std::min<int64_t>(p.G, p.BH - g0);
-    // ---- forward stages 1 and 2, as in the route
-    {
-      // the seed encode takes c S as the same hi/lo operand as the backward
-      // passes of stage 1 below, so that the recomputed forward and the
-      // gradients see the same logits
-      EncodeArgs e = encode_args(p, ws, K, V, g0);
-      e.q_hi = shi;
-      e.q_lo = slo;
-      e.q_sb = 0;
-      e.q_sh = p.nS > 1 ? MpD : 0;
-      e.q_off = 0;
-      e.knorm = at<float>(ws, p.o_knorm);
-      FLAREPP_TRY((run_encode_bf16<D, true, false, false>(p, e, Gc, st, rec, FLAREPP_KERNEL_SEED_ENCODE)));
-      MergeArgs m = merge_args(p, ws, g0);
-      refit_from(m, e);
-      m.outl = qf;
-      m.op_hi = qhi;
-      m.op_lo = qlo;
-      m.qnorm = at<float>(ws, p.o_qnorm);
-      m.knorm = e.knorm;
-      m.Jk = p.J;
-      m.bias = at<float>(ws, p.o_bias);
-      m.lse = at<float>(ws, p.o_lse1);
-      FLAREPP_TRY(run_merge<D>(p, m, Gc, st, rec));
-      EncodeArgs e2 = encode_args(p, ws, K, V, g0);
-      e2.q_hi = qhi;
-      e2.q_lo = qlo;
-      e2.q_sb = (int64_t)p.H * MpD;
-      e2.q_sh = MpD;
-      e2.q_off = g0 * MpD;
-      e2.bias = at<float>(ws, p.o_bias);
-      FLAREPP_TRY((run_encode_bf16<D, false, true, false>(p, e2, Gc, st, rec, FLAREPP_KERNEL_ENCODE)));
-      MergeArgs m2 = merge_args(p, ws, g0);
-      m2.outl = zf;
-      m2.lse = at<float>(ws, p.o_lse2);
-      FLAREPP_TRY(run_merge<D>(p, m2, Gc, st, rec));
+    // ---- forward stages 1 and 2 (recomputed, or from the saved forward)
+    const float* qf;
+    const float* zf;
+    float* lse1;
+    float* lse2;
+    if (saved) {
+      qf = saved->Qd + g0 * MD;
+      zf = saved->Z + g0 * MD;
+      lse1 = const_cast<float*>(saved->lse) + g0 * p.Mp;
+      lse2 = const_cast<float*>(saved->lse) + (p.BH + g0) * p.Mp;
+      FLAREPP_TRY(run_prep<D>(p, saved->Qd, false, g0 * MD, MD, Gc, qhi, qlo, nullptr, at<float>(ws, p.o_qnorm), p.c,
+                              st, rec));
+    } else {
+      float* qs = at<float>(ws, p.o_qf);
+      float* zs = at<float>(ws, p.o_zf);
+      lse1 = at<float>(ws, p.o_lse1);
+      lse2 = at<float>(ws, p.o_lse2);
+      FLAREPP_TRY(forward_for_backward<D>(p, K, V, ws, g0, Gc, nullptr, qs, nullptr, zs, lse1, lse2, nullptr, st, rec));
+      qf = qs;
+      zf = zs;
     }
     auto reduce = [&](int R, int field0, const float* add_to, float* out, const float* dot_with, float* delta,
                       int seed_blocks) {
@@ -1019,8 +1059,8 @@ flarepp_status run_backward_bf16(const Plan& p, const void* S, const void* K, co
     }
     // ---- stages 2 and 1: latent passes, then one token pass for both
     BwdStageOps ops[2];
-    ops[0] = BwdStageOps{qhi, qlo, (int64_t)p.H * MpD, MpD, g0 * MpD, dzr, dzl, at<float>(ws, p.o_lse2), nullptr};
-    ops[1] = BwdStageOps{shi, slo, 0, p.nS > 1 ? MpD : 0, 0, dqr, dql, at<float>(ws, p.o_lse1), nullptr};
+    ops[0] = BwdStageOps{qhi, qlo, (int64_t)p.H * MpD, MpD, g0 * MpD, dzr, dzl, lse2, nullptr};
+    ops[1] = BwdStageOps{shi, slo, 0, p.nS > 1 ? MpD : 0, 0, dqr, dql, lse1, nullptr};
     auto enc_latent = [&](const BwdStageOps& o, const float* delta) {
       BwdEncArgs e{};
       e.qhi = o.qhi;
@@ -1084,6 +1124,47 @@ flarepp_status run_backward_bf16(const Plan& p, const void* S, const void* K, co
   return FLAREPP_OK;
 }
 
+// The route with the forward of the backward (flarepp_route_save): stages 1
+// and 2 as forward_for_backward runs them (c S and c Qd as bf16 hi/lo
+// operands, the logits the backward's passes take), Qd, Z and both
+// log-sum-exps written for flarepp_route_backward_saved, then the route's
+// decode.
+template <int D>
+flarepp_status run_route_save(const Plan& p, const void* S, const void* K, const void* V, float* Y, float* Qd_out,
+                              float* Z_out, float* lse_out, void* ws, hipStream_t st) {
+  Recorder rec;
+  const int64_t MD = (int64_t)p.M * D, MpD = (int64_t)p.Mp * D;
+  FLAREPP_TRY(run_prep<D>(p, S, true, 0, p.nS > 1 ? MD : 0, p.nS, at<__bf16>(ws, p.o_shi), at<__bf16>(ws, p.o_slo),
+                          nullptr, nullptr, p.c, st, rec));
+  for (int64_t g0 = 0; g0 < p.BH; g0 += p.G) {
+    const int Gc = (int)std::min<int64_t>(p.G, p.BH - g0);
+    __bf16* zt = at<__bf16>(ws, p.o_zt);
+    FLAREPP_TRY(forward_for_backward<D>(p, K, V, ws, g0, Gc, Qd_out, nullptr, Z_out, nullptr, lse_out + g0 * p.Mp,
+                                        lse_out + (p.BH + g0) * p.Mp, zt, st, rec));
+    DecodeArgs d{};
+    d.q_hi = at<__bf16>(ws, p.o_qhi);
+    d.q_lo = at<__bf16>(ws, p.o_qlo);
+    d.q_sb = (int64_t)p.H * MpD;
+    d.q_sh = MpD;
+    d.q_off = g0 * MpD;
+    d.qnorm = at<float>(ws, p.o_qnorm);
+    d.knorm = at<float>(ws, p.o_knorm);
+    d.Jk = p.J;
+    d.zt = zt;
+    d.K = static_cast<const __bf16*>(K);
+    d.Y = Y;
+    d.H = p.H;
+    d.N = p.N;
+    d.M = p.M;
+    d.Mp = p.Mp;
+    d.chunk = p.dchunk;
+    d.bh0 = g0;
+    d.c = p.c;
+    FLAREPP_TRY(run_decode_bf16<D>(p, d, Gc, st, rec));
+  }
+  return FLAREPP_OK;
+}
+
 flarepp_status dispatch(const Plan& p, Stage stage, const void* S, const float* Qd_in, const float* Z_in,
                         const void* K, const void* V, float* Y, float* Qd_out, float* Z_out, void* ws,
                         void* stream, Recorder* recorder = nullptr) {
@@ -1114,9 +1195,10 @@ flarepp_status prologue(const flarepp_desc* d, int op, const void* const* in, co
     if (!ws || misaligned(ws)) return FLAREPP_INVALID_ARG;
     if (ws_bytes < plan->total) return FLAREPP_WORKSPACE_TOO_SMALL;
   }
-  Range ins[6], outs[4];
-  const void* inp[6];
-  const void* outp[4];
+  Range ins[10], outs[6];
+  const void* inp[10];
+  const void* outp[6];
+  if (nin > 9 || nout > 6) return FLAREPP_INVALID_ARG;
   int ni = 0;
   for (int i = 0; i < nin; ++i) {
     ins[ni] = range(in[i], in_bytes[i]);
@@ -1354,6 +1436,49 @@ flarepp_status flarepp_route_backward(const flarepp_desc* desc, const void* S, c
               *Vf = static_cast<const float*>(V);
   if (p.D == 16) return run_backward<16>(p, Sf, Kf, Vf, dY, dS, dK, dV, ws, st);
   return run_backward<32>(p, Sf, Kf, Vf, dY, dS, dK, dV, ws, st);
+}
+
+// Bytes of the saved log-sum-exps: [2][B H][Mp] float32.
+static size_t saved_lse_bytes(const flarepp_desc* d) {
+  return (size_t)2 * d->B * d->H * (size_t)(cdiv(d->M, 16) * 16) * 4;
+}
+
+flarepp_status flarepp_route_save(const flarepp_desc* desc, const void* S, const void* K, const void* V, float* Y,
+                                  float* Qd_out, float* Z_out, float* lse_out, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  FLAREPP_TRY(check_desc(desc));
+  if (desc->dtype != FLAREPP_BF16 || desc->M > kBwdBf16MaxM) return FLAREPP_UNSUPPORTED;
+  const Sizes z = sizes(desc);
+  const void* in[3] = {S, K, V};
+  const size_t inb[3] = {z.s, z.kv, z.kv};
+  const void* out[4] = {Y, Qd_out, Z_out, lse_out};
+  const size_t outb[4] = {z.y, z.md, z.md, saved_lse_bytes(desc)};
+  const bool req[4] = {true, true, true, true};
+  Plan p;
+  FLAREPP_TRY(prologue(desc, FLAREPP_OP_ROUTE_BACKWARD, in, inb, 3, out, outb, req, 4, ws, ws_bytes, &p));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (p.D == 16) return run_route_save<16>(p, S, K, V, Y, Qd_out, Z_out, lse_out, ws, st);
+  return run_route_save<32>(p, S, K, V, Y, Qd_out, Z_out, lse_out, ws, st);
+}
+
+flarepp_status flarepp_route_backward_saved(const flarepp_desc* desc, const void* S, const void* K, const void* V,
+                                            const float* Qd, const float* Z, const float* lse, const float* dY,
+                                            float* dS, float* dK, float* dV, void* ws, size_t ws_bytes,
+                                            void* stream) {
+  FLAREPP_TRY(check_desc(desc));
+  if (desc->dtype != FLAREPP_BF16 || desc->M > kBwdBf16MaxM) return FLAREPP_UNSUPPORTED;
+  const Sizes z = sizes(desc);
+  const void* in[7] = {S, K, V, Qd, Z, lse, dY};
+  const size_t inb[7] = {z.s, z.kv, z.kv, z.md, z.md, saved_lse_bytes(desc), z.y};
+  const void* out[3] = {dS, dK, dV};
+  const size_t outb[3] = {z.s, z.kv, z.kv};
+  const bool req[3] = {true, true, true};
+  Plan p;
+  FLAREPP_TRY(prologue(desc, FLAREPP_OP_ROUTE_BACKWARD, in, inb, 7, out, outb, req, 3, ws, ws_bytes, &p));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const SavedForward saved{Qd, Z, lse};
+  if (p.D == 16) return run_backward_bf16<16>(p, S, K, V, dY, dS, dK, dV, ws, st, &saved);
+  return run_backward_bf16<32>(p, S, K, V, dY, dS, dK, dV, ws, st, &saved);
 }
 
 flarepp_status flarepp_route_profiled(const flarepp_desc* desc, const void* S, const void* K, const void* V,

@@ -27,7 +27,7 @@ SYMBOLS = ("flarepp_abi_version", "flarepp_status_string", "flarepp_workspace_si
            "flarepp_flare", "flarepp_route_backward", "flarepp_spectrum", "flarepp_route_profiled",
            "flarepp_workspace_size_tuned", "flarepp_route_tuned", "flarepp_route_noalloc",
            "flarepp_noalloc_scratch_bytes", "flarepp_shard_records_size", "flarepp_encode_shard",
-           "flarepp_merge_shards")
+           "flarepp_merge_shards", "flarepp_route_save", "flarepp_route_backward_saved")
 KERNEL_KINDS = {0: "prep", 1: "seed_encode", 2: "encode", 3: "merge", 4: "decode"}
 
 
@@ -91,6 +91,10 @@ def _lib():
         lib.flarepp_flare.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.flarepp_route_backward.restype = ctypes.c_int
         lib.flarepp_route_backward.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.flarepp_route_save.restype = ctypes.c_int
+        lib.flarepp_route_save.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.flarepp_route_backward_saved.restype = ctypes.c_int
+        lib.flarepp_route_backward_saved.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.flarepp_spectrum.restype = ctypes.c_int
         lib.flarepp_spectrum.argtypes = [dp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.flarepp_route_profiled.restype = ctypes.c_int
@@ -221,6 +225,21 @@ def flarepp_spectrum(desc, S, K, V, eig, sym_out, ws, ws_bytes, stream) -> int:
 def flarepp_route_backward(desc, S, K, V, dY, dS, dK, dV, ws, ws_bytes, stream) -> int:
     return _lib().flarepp_route_backward(ctypes.byref(desc), S, K, V, dY, dS, dK, dV, ws, ws_bytes,
                                          stream)
+
+
+def flarepp_route_save(desc, S, K, V, Y, Qd_out, Z_out, lse_out, ws, ws_bytes, stream) -> int:
+    return _lib().flarepp_route_save(ctypes.byref(desc), S, K, V, Y, Qd_out, Z_out, lse_out, ws, ws_bytes,
+                                     stream)
+
+
+def flarepp_route_backward_saved(desc, S, K, V, Qd, Z, lse, dY, dS, dK, dV, ws, ws_bytes, stream) -> int:
+    return _lib().flarepp_route_backward_saved(ctypes.byref(desc), S, K, V, Qd, Z, lse, dY, dS, dK, dV, ws,
+                                               ws_bytes, stream)
+
+
+def saved_lse_count(desc: FlareppDesc) -> int:
+    """Floats of the saved log-sum-exp buffer: [2][B H][16 ceil(M / 16)]."""
+    return 2 * desc.B * desc.H * (-(-desc.M // 16) * 16)
 
 
 def flarepp_route_profiled(desc, S, K, V, Y, Qd_out, Z_out, ws, ws_bytes, stream, events, kinds,
@@ -376,6 +395,43 @@ def route_backward(S, K, V, scale, dY, *, workspace: Workspace | None = None, st
     buf, nbytes = ws.get(flarepp_workspace_size(desc, OP_ROUTE_BACKWARD))
     _check(flarepp_route_backward(desc, _ptr(S), _ptr(K), _ptr(V), _ptr(dY), _ptr(dS), _ptr(dK),
                                   _ptr(dV), _ptr(buf), nbytes, _stream(stream)), "flarepp_route_backward")
+    return dS, dK, dV
+
+
+def route_save(S, K, V, scale, *, workspace: Workspace | None = None, stream=None):
+    """(Y, saved): the route with the backward's forward stages, and what
+    route_backward_saved needs (Qd, Z, the encodes' log-sum-exps); bf16 only."""
+    torch = _torch()
+    for t, n in ((S, "S"), (K, "K"), (V, "V")):
+        _require(t, n)
+    desc = desc_for(S, K, scale)
+    B, H, N, D = K.shape
+    Y = torch.empty((B, H, N, D), dtype=torch.float32, device=K.device)
+    Qd = torch.empty((B, H, desc.M, D), dtype=torch.float32, device=K.device)
+    Z = torch.empty_like(Qd)
+    lse = torch.empty(saved_lse_count(desc), dtype=torch.float32, device=K.device)
+    ws = workspace or Workspace(K.device)
+    buf, nbytes = ws.get(flarepp_workspace_size(desc, OP_ROUTE_BACKWARD))
+    _check(flarepp_route_save(desc, _ptr(S), _ptr(K), _ptr(V), _ptr(Y), _ptr(Qd), _ptr(Z), _ptr(lse),
+                              _ptr(buf), nbytes, _stream(stream)), "flarepp_route_save")
+    return Y, (Qd, Z, lse)
+
+
+def route_backward_saved(S, K, V, scale, saved, dY, *, workspace: Workspace | None = None, stream=None):
+    """(dS, dK, dV) as route_backward, from route_save's saved forward."""
+    torch = _torch()
+    Qd, Z, lse = saved
+    for t, n in ((S, "S"), (K, "K"), (V, "V"), (dY, "dY"), (Qd, "Qd"), (Z, "Z"), (lse, "lse")):
+        _require(t, n)
+    desc = desc_for(S, K, scale)
+    dS = torch.empty_like(S, dtype=torch.float32)
+    dK = torch.empty(K.shape, dtype=torch.float32, device=K.device)
+    dV = torch.empty(K.shape, dtype=torch.float32, device=K.device)
+    ws = workspace or Workspace(K.device)
+    buf, nbytes = ws.get(flarepp_workspace_size(desc, OP_ROUTE_BACKWARD))
+    _check(flarepp_route_backward_saved(desc, _ptr(S), _ptr(K), _ptr(V), _ptr(Qd), _ptr(Z), _ptr(lse), _ptr(dY),
+                                        _ptr(dS), _ptr(dK), _ptr(dV), _ptr(buf), nbytes, _stream(stream)),
+           "flarepp_route_backward_saved")
     return dS, dK, dV
 
 

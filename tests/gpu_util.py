@@ -150,3 +150,32 @@ def compare_route(p, Y, Qd, Z, heads=None, ref=None):
     out["Y"] = assert_close("Y", np.stack([Y[b, h] for b, h in heads]), np.stack([r[2] for r in ref]), p.dtype)
     assert np.isfinite(Y).all()
     return ref, out
+
+
+def saved_backward_poisoned(fp, S, K, V, scale, dY):
+    """flarepp_route_save, then flarepp_route_backward_saved on its saved
+    forward, every output and both workspaces NaN-poisoned before the calls:
+    (Y, Qd, Z, lse) and (dS, dK, dV)."""
+    import torch
+
+    desc = fp.desc_for(S, K, scale)
+    B, H, N, D = K.shape
+    M = desc.M
+    n = fp.flarepp_workspace_size(desc, fp.OP_ROUTE_BACKWARD)
+    Y = poisoned((B, H, N, D))
+    Qd, Z = poisoned((B, H, M, D)), poisoned((B, H, M, D))
+    lse = poisoned((fp.saved_lse_count(desc),))
+    ws = poisoned((max(n, 1),), torch.uint8)
+    st = fp.flarepp_route_save(desc, S.data_ptr(), K.data_ptr(), V.data_ptr(), Y.data_ptr(), Qd.data_ptr(),
+                               Z.data_ptr(), lse.data_ptr(), ws.data_ptr(), n, fp._stream(None))
+    if st != 0:
+        raise fp.FlareppError(st, "flarepp_route_save")
+    dS = poisoned(tuple(S.shape))
+    dK, dV = poisoned(tuple(K.shape)), poisoned(tuple(K.shape))
+    ws2 = poisoned((max(n, 1),), torch.uint8)
+    st = fp.flarepp_route_backward_saved(desc, S.data_ptr(), K.data_ptr(), V.data_ptr(), Qd.data_ptr(),
+                                         Z.data_ptr(), lse.data_ptr(), dY.data_ptr(), dS.data_ptr(),
+                                         dK.data_ptr(), dV.data_ptr(), ws2.data_ptr(), n, fp._stream(None))
+    if st != 0:
+        raise fp.FlareppError(st, "flarepp_route_backward_saved")
+    return (Y, Qd, Z, lse), (dS, dK, dV)

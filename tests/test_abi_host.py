@@ -141,6 +141,35 @@ def test_backward_validation(dt):
     assert bwd(dS=addr(6)) == ALIASING             # output inside the workspace
 
 
+def test_saved_forward_validation():
+    d = desc()
+    n = ws_status(d, fp.OP_ROUTE_BACKWARD)[1]
+    assert fp.saved_lse_count(d) == 2 * 2 * 3 * 64
+    assert fp.saved_lse_count(desc(M=17)) == 2 * 2 * 3 * 32
+
+    def save(dd=d, Y=addr(3), Qd=addr(4), Z=addr(5), lse=addr(7), ws=addr(6), nbytes=n):
+        return fp.flarepp_route_save(dd, addr(0), addr(1), addr(2), Y, Qd, Z, lse, ws, nbytes, None)
+
+    def bwd(dd=d, Qd=addr(3), Z=addr(4), lse=addr(5), dS=addr(7), dK=addr(8), dV=addr(9), ws=addr(6), nbytes=n):
+        return fp.flarepp_route_backward_saved(dd, addr(0), addr(1), addr(2), Qd, Z, lse, addr(10), dS, dK, dV, ws,
+                                               nbytes, None)
+
+    # every case fails validation on the host, before any HIP call
+    for call in (save, bwd):
+        assert call(dd=desc(dtype=fp.F32)) == UNSUPPORTED
+        assert call(dd=desc(M=257)) == UNSUPPORTED
+        assert call(nbytes=n - 1) == WS_SMALL
+    assert save(lse=None) == INVALID_ARG
+    assert save(Qd=None) == INVALID_ARG
+    assert save(Z=addr(5) + 4) == INVALID_ARG           # misaligned
+    assert save(lse=addr(2) + 256) == ALIASING          # output inside V
+    assert save(Z=addr(4) + 64) == ALIASING             # two outputs overlap
+    assert bwd(lse=None) == INVALID_ARG
+    assert bwd(dK=addr(3) + 128) == ALIASING            # output inside the saved Qd
+    assert bwd(dS=addr(5) + 16) == ALIASING             # output inside the saved log-sum-exps
+    assert bwd(dV=addr(6)) == ALIASING                  # output inside the workspace
+
+
 def test_shard_validation():
     lib = fp.library()
     d = desc()

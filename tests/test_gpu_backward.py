@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 from rank_latent_attention_seed_amd import inputs
-from gpu_util import backward_poisoned, to_device
+from gpu_util import assert_close, backward_poisoned, oracle_heads, saved_backward_poisoned, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -144,3 +144,52 @@ def test_backward_bf16_deterministic(fp):
     for x, y in zip(a, b):
         assert torch.isfinite(x).all(), "non-finite gradient"
         assert torch.equal(x, y), "two identical calls differ"
+
+
+SAVED_CASES = [
+    # B, H, N, M, D, scale, per-head seeds
+    (1, 2, 300, 20, 16, 0.25, False),
+    (1, 3, 777, 33, 32, 0.4, True),
+    (1, 1, 5000, 256, 32, 1 / np.sqrt(32), False),
+    (2, 2, 129, 100, 16, 1.0, False),
+    (1, 2, 900, 48, 32, -1.0, False),
+    (1, 2, 3000, 128, 32, 1.0, False),
+]
+
+
+@pytest.mark.parametrize("B,H,N,M,D,scale,per_head", SAVED_CASES)
+def test_saved_forward_and_backward(fp, B, H, N, M, D, scale, per_head):
+    """flarepp_route_save's outputs against the oracle's forward, and
+    flarepp_route_backward_saved's gradients against the oracle's backward
+    and against flarepp_route_backward on the same inputs (which recomputes
+    the same forward stages: they differ only by the rounding of the latent
+    norms that each path forms), all buffers NaN-poisoned."""
+    import oracle
+    import torch
+
+    p = inputs.random_problem(B, H, N, M, D, dtype="bf16", scale=scale, seed=N + M + 7, per_head_seeds=per_head)
+    print(f"\n  case saved forward/backward: B{B} H{H} N{N} M{M} D{D} s={scale:g}", flush=True)
+    rng = np.random.default_rng(N + 9)
+    dY = rng.standard_normal((B, H, N, D)).astype(np.float32)
+    S, K, V, G = to_device(p.S), to_device(p.K), to_device(p.V), to_device(dY)
+    (Y, Qd, Z, lse), (dS, dK, dV) = saved_backward_poisoned(fp, S, K, V, p.scale, G)
+    rS, rK, rV = backward_poisoned(fp, S, K, V, p.scale, G)
+    torch.cuda.synchronize()
+    assert torch.isfinite(lse).all(), "log-sum-exp rows left unwritten"
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    ref = oracle_heads(p.S, p.K, p.V, p.scale, heads)
+    for name, got, k in (("Qd", Qd, 0), ("Z", Z, 1), ("Y", Y, 2)):
+        g = got.cpu().numpy()
+        assert_close(name, np.stack([g[b, h] for b, h in heads]), np.stack([r[k] for r in ref]), "bf16")
+    oS, oK, oV = oracle.route_backward(p.S, p.K, p.V, p.scale, dY.astype(np.float64))
+    joint = max(float(np.abs(r).max()) for r in (oS, oK, oV))
+    for name, got, rec, ref in (("dS", dS, rS, oS), ("dK", dK, rK, oK), ("dV", dV, rV, oV)):
+        g, r = got.cpu().numpy().astype(np.float64), rec.cpu().numpy().astype(np.float64)
+        own = float(np.abs(ref).max())
+        scale_ = own if own > 0.0 else joint
+        err = float(np.abs(g - ref).max())
+        diff = float(np.abs(g - r).max())
+        print(f"    {name}: vs oracle {err / scale_:.3e} normwise, vs recomputing backward {diff / scale_:.3e}",
+              flush=True)
+        assert err <= BWD_NORMWISE["bf16"] * scale_, f"{name}: {err:.3e} vs oracle"
+        assert diff <= 1e-3 * scale_, f"{name}: saved and recomputing backward differ by {diff:.3e}"
