@@ -89,6 +89,19 @@ int main() {
   EXPECT(flarepp_route_backward(&good, addr(0), addr(1), addr(2), faddr(3), faddr(1), faddr(5), faddr(7), addr(6),
                                 size_t(1) << 40, nullptr),
          FLAREPP_ALIASING);  // dS inside K
+  // the saved-forward pair: seven inputs plus the workspace in one aliasing check
+  EXPECT(flarepp_route_save(&good, addr(0), addr(1), addr(2), faddr(3), faddr(4), faddr(5), faddr(1), addr(6),
+                            size_t(1) << 40, nullptr),
+         FLAREPP_ALIASING);  // the log-sum-exps inside K
+  EXPECT(flarepp_route_save(&good, addr(0), addr(1), addr(2), faddr(3), faddr(4), faddr(5), nullptr, addr(6),
+                            size_t(1) << 40, nullptr),
+         FLAREPP_INVALID_ARG);
+  EXPECT(flarepp_route_backward_saved(&good, addr(0), addr(1), addr(2), faddr(3), faddr(4), faddr(5), faddr(8),
+                                      faddr(9), faddr(10), faddr(4), addr(6), size_t(1) << 40, nullptr),
+         FLAREPP_ALIASING);  // dV inside the saved Z
+  EXPECT(flarepp_route_backward_saved(&good, addr(0), addr(1), addr(2), faddr(3), faddr(4), faddr(5), faddr(8),
+                                      faddr(9), faddr(10), faddr(11), addr(6), 0, nullptr),
+         FLAREPP_WORKSPACE_TOO_SMALL);
   size_t recb = 0;
   EXPECT(flarepp_shard_records_size(&good, 3, &recb), FLAREPP_OK);
   EXPECT(flarepp_shard_records_size(&good, 0, &recb), FLAREPP_INVALID_ARG);
