@@ -169,7 +169,9 @@ flarepp_status flarepp_flare(const flarepp_desc *desc, const void *Q, const void
  *     dS  (shape of S: M x D, or H x M x D with per-head seeds; a seed block
  *          shared by several (b, h) receives the sum of their gradients),
  *     dK, dV  (B x H x N x D),
- * all fp32.  The forward is recomputed inside the call.  It is the chain
+ * all fp32.  The forward is recomputed inside the call (flarepp_route_save
+ * and flarepp_route_backward_saved below split a training step so that it
+ * is not).  It is the chain
  * rule through the three SDPA stages in reverse -- decode (queries K, keys
  * Qd, values Z), encode (queries Qd), seed encode (queries S) -- with Qd's
  * gradient collecting its two uses (encode query, decode key); for one SDPA
