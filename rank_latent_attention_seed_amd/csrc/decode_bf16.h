@@ -6,8 +6,9 @@
 //
 // Work decomposition.  A 256-thread workgroup owns one (b, h) and a chunk of
 // tokens.  Every wave keeps the whole latent side in registers for its
-// lifetime (c * Qd as a bf16 hi/lo pair and Z^T, as matrix-core operands:
-// ~200 VGPRs at M = 256, D = 32, one wave per SIMD), and streams 16-token
+// lifetime (c * Qd as a bf16 hi/lo pair, or for heads within the fp16 logit
+// bound as one fp16 operand against keys converted to fp16 after each load
+// (f16_logits, common.h), and Z^T, as matrix-core operands), and streams 16-token
 // blocks of K straight from global memory (each lane 16 contiguous bytes of
 // one token row), two blocks ahead of the one it consumes.
 // Per block a wave computes L^T = Qd K^T (rows = latents, cols = tokens) for

@@ -34,7 +34,10 @@
 // Softmax arithmetic.  A synthesised query (Qd, float32) arrives
 // pre-multiplied by c = s * log2(e) as a bf16 hi/lo pair (two MFMAs per
 // tile, ~16 mantissa bits), and -mu_m enters as the MFMA accumulator input,
-// so the tile is already t = c <Q_m, K_n> - mu_m.  The seeds are bf16 inputs
+// so the tile is already t = c <Q_m, K_n> - mu_m; in the route's bounded
+// encode, heads within the fp16 logit bound (f16_logits, common.h) take c Q
+// as one fp16 operand against keys converted to fp16 in the ring instead
+// (one product per tile).  The seeds are bf16 inputs
 // and therefore an exact operand (EXQ): one MFMA per tile gives <S_m, K_n>
 // to float32 rounding, and one FMA per score applies c and the shift (four
 // matrix-core products per 32-token step of a wave traded for sixteen VALU
