@@ -249,6 +249,18 @@ def test_deterministic_and_split_invariant(fp):
         assert torch.equal(x, y), "head grouping changed results"
 
 
+@pytest.mark.parametrize("splits,M,D", [(33, 256, 32), (64, 128, 32), (48, 96, 16), (64, 200, 32)])
+def test_merge_one_record_per_lane(fp, splits, M, D):
+    """Split counts of 33 to 64: the merge reads one record per lane and
+    reduces all of a row's values together (D = 32), lanes past the last
+    split contributing nothing; D = 16 takes the per-value reductions.  The
+    route against the oracle on NaN-poisoned buffers, at 2000 tokens per
+    split."""
+    p = inputs.random_problem(1, 2, 2000 * splits, M, D, dtype="bf16", seed=splits + M)
+    run_and_compare(fp, p, label=f"{splits} splits M{M} D{D}", tuning=fp.make_tuning(splits=splits),
+                    heads=[(0, 1)])
+
+
 @pytest.mark.parametrize("M", [256, 64])
 def test_writes_stay_inside_outputs(fp, M):
     """Y, Qd and Z are written exactly: sentinel-filled space after each stays
