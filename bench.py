@@ -260,6 +260,46 @@ def route_rates(p, ms: float, elem: int) -> dict:
     }
 
 
+def graph_record(fp, torch, r: Route, steps: int) -> dict:
+    """The route captured once in a HIP graph (through torch.cuda.CUDAGraph; the
+    library launches its kernels on the stream it is given, allocates nothing
+    and records no memset) and replayed: median time per replay, and every
+    checked replay bitwise equal to the eager route."""
+    Y0 = r.Y.clone()
+    r.step()
+    torch.cuda.synchronize()
+    ref = r.Y.clone()
+
+    def launch():
+        st = fp.flarepp_route(r.desc, *r.ptrs, None, None, r.ws.data_ptr(), r.nbytes,
+                              ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise fp.FlareppError(st, "flarepp_route (capture)")
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        launch()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launch()
+    torch.cuda.synchronize()
+    match = True
+    for i in range(4):  # replays with eager work and synchronisations between them
+        r.Y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        match = match and bool(torch.equal(r.Y, ref))
+        r.step()
+        torch.cuda.synchronize()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ms = time_steps(g.replay, torch, stream, steps)
+    r.Y.copy_(Y0)
+    del g
+    return {"ms_per_step_graph": statistics.median(ms), "replays_match_eager": match}
+
+
 def config_record(fp, torch, inputs, name: str, steps: int, warmup: int) -> dict:
     t0 = time.perf_counter()
     p = inputs.make_problem(name)
@@ -271,6 +311,7 @@ def config_record(fp, torch, inputs, name: str, steps: int, warmup: int) -> dict
            "steps": steps, "ms_per_step": med, "ms_per_step_mean": sum(ms) / len(ms)}
     rec.update(route_rates(p, med, r.elem))
     rec["kernels_avg_us"] = {k: round(v["avg_us"], 2) for k, v in r.kernel_stats(10).items()}
+    rec.update(graph_record(fp, torch, r, steps))
     kv_bytes = 2 * p.B * p.H * p.N * p.D * r.elem
     if kv_bytes < (256 << 20) and name != "tiny":
         fl = time_flushed(r.step, torch, r.stream, 20)
@@ -280,7 +321,8 @@ def config_record(fp, torch, inputs, name: str, steps: int, warmup: int) -> dict
         f"(mean {1e3 * rec['ms_per_step_mean']:.1f}), {rec['token_heads_per_s'] / 1e9:.3f} G token*heads/s, "
         f"{100 * rec['frac_of_compute_peak']:.1f}% of compute peak, {100 * rec['frac_of_hbm_peak']:.1f}% of HBM"
         + (f"; cache flushed {1e3 * rec['ms_per_step_cache_flushed']:.1f} us" if "ms_per_step_cache_flushed" in rec
-           else "") + f" ({time.perf_counter() - t0:.1f} s)")
+           else "") + f"; graph replay {1e3 * rec['ms_per_step_graph']:.1f} us"
+        + ("" if rec["replays_match_eager"] else " (REPLAYS DIFFER)") + f" ({time.perf_counter() - t0:.1f} s)")
     del r
     torch.cuda.empty_cache()
     return rec
